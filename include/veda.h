@@ -1,0 +1,199 @@
+/*
+ * veda.h -- C ABI of the tile-sparse self-attention hot path (libveda.so).
+ *
+ * The method: "Veda: Scalable Video Diffusion via Distilled Sparse Attention"
+ * (technical summary on gist.science; zh/fr/es editions share the section
+ * numbers cited here as "Veda §x") and the aikraft.ru news item on Veda
+ * ("Veda news").  For one attention layer of a video DiT whose tokens form a
+ * T x H x W latent grid, the path is:
+ *
+ *   veda_tile_permute(FWD)    tokens -> per-head tiles       (Veda §2.2)
+ *   veda_tripool_score        TripPool + per-head projection
+ *                             + tile-pair scores             (Veda §2.1)
+ *   veda_select_tiles         row-wise top-k -> CSR          (Veda lay summary, §5)
+ *   veda_sparse_attn_fwd      tile-skipping attention        (Veda §2.3)
+ *   veda_tile_permute(INV)    tiles -> tokens
+ *   veda_oracle_maxpool_map   two-pass max-pooled attention
+ *                             map (distillation target)      (Veda §2.1, §2.3)
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *    memory; the library never allocates, frees or retains a pointer.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Device calls are
+ *    enqueued on it asynchronously; the library never synchronises, except
+ *    when the environment variable VEDA_DEBUG_SYNC=1 is set (then every call
+ *    synchronises and reports kernel failures, and veda_sparse_attn_fwd
+ *    validates the CSR on the host first).
+ *  - Every argument is validated on the host before anything is enqueued.  An
+ *    invalid argument returns a negative veda_status and enqueues nothing.
+ *  - Calls keep no state between them and may be made from several threads.
+ *  - bf16 is the IEEE-754 binary32 high half (bfloat16); f32 is binary32.
+ *
+ * Token and tile order (the pages leave these open; the readings taken):
+ *  - token n of a [N][heads][d] tensor sits at grid point (t, h, w) with
+ *    n = (t*H + h)*W + w;
+ *  - head `hd` with tile shape (pt, ph, pw), pt*ph*pw = tile_size = S, has
+ *    nT*nH*nW tiles, nT = ceil(T/pt) etc.: every grid dimension is padded up
+ *    to whole tiles and the slots outside the grid are padding;
+ *  - tile j = (it*nH + ih)*nW + iw, slot u = (dt*ph + dh)*pw + dw holds the
+ *    token (it*pt + dt, ih*ph + dh, iw*pw + dw) when it lies in the grid;
+ *  - "tile order" tensors are [sum_h n_tiles[h]*S][d]: head hd occupies rows
+ *    tile_off[hd]*S .. tile_off[hd+1]*S - 1, tile j of that head the S rows
+ *    from (tile_off[hd] + j)*S.  Padding rows hold zeros.
+ *  - "tile-transposed" tensors hold each tile as a [d][S] block instead of
+ *    [S][d] (same per-tile offsets); the attention kernel takes V this way.
+ */
+#ifndef VEDA_H
+#define VEDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VEDA_MAX_HEADS 64
+
+typedef enum veda_status {
+  VEDA_OK = 0,
+  VEDA_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad enum, bad layout    */
+  VEDA_ERR_UNSUPPORTED = -2, /* valid but outside the built set (see each call) */
+  VEDA_ERR_LAUNCH = -3,      /* the HIP runtime refused or failed a launch      */
+  VEDA_ERR_BAD_CSR = -4      /* debug validation found an invalid CSR           */
+} veda_status;
+
+typedef enum veda_dtype { VEDA_BF16 = 0, VEDA_F32 = 1 } veda_dtype;
+
+typedef enum veda_dir {
+  VEDA_FWD = 0,   /* token order -> tile order                    */
+  VEDA_INV = 1,   /* tile order -> token order (real slots only)  */
+  VEDA_FWD_T = 2  /* token order -> tile-transposed order         */
+} veda_dir;
+
+/* Geometry of one attention layer.  The caller fills the inputs and calls
+ * veda_layout_init, which checks them and fills the derived fields. */
+typedef struct veda_layout {
+  /* inputs */
+  int32_t T, H, W;                           /* latent grid: frames, height, width */
+  int32_t num_heads;                         /* 1 .. VEDA_MAX_HEADS                 */
+  int32_t head_dim;                          /* d                                   */
+  int32_t tile_size;                         /* S = pt*ph*pw for every head         */
+  int32_t tile_shape[VEDA_MAX_HEADS][3];     /* per head (pt, ph, pw)               */
+  /* derived by veda_layout_init */
+  int32_t tile_grid[VEDA_MAX_HEADS][3];      /* per head (nT, nH, nW)               */
+  int32_t n_tiles[VEDA_MAX_HEADS];           /* per head nT*nH*nW                   */
+  int32_t max_tiles;                         /* max over heads of n_tiles           */
+  int32_t reserved0;
+  int64_t tile_off[VEDA_MAX_HEADS + 1];      /* prefix sum of n_tiles               */
+  int64_t score_off[VEDA_MAX_HEADS + 1];     /* prefix sum of n_tiles^2             */
+} veda_layout;
+
+/* Host only.  Veda §2.2: each head has its own tile shape (pt, ph, pw) whose
+ * volume is the hardware tile.  Checks T, H, W >= 1, 1 <= num_heads <=
+ * VEDA_MAX_HEADS, head_dim >= 1, tile_size >= 1, every shape positive with
+ * pt*ph*pw == tile_size, and that every offset fits int32 row/column indices
+ * of the CSR; fills the derived fields.  VEDA_ERR_INVALID_ARG otherwise. */
+int veda_layout_init(veda_layout* L);
+
+/* Host only.  Key tiles kept per query tile at `sparsity_pct` percent tile
+ * sparsity (Veda: 95 % sparsity keeps about 5 % of the tiles):
+ * k = max(1, ceil(n_tiles * (100 - sparsity_pct) / 100)) in integer
+ * arithmetic.  Needs n_tiles >= 1 and 0 <= sparsity_pct <= 100 and a non-null
+ * (host) k_out; VEDA_ERR_INVALID_ARG otherwise. */
+int veda_keep_count(int32_t n_tiles, int32_t sparsity_pct, int32_t* k_out);
+
+/* Veda §2.2 (head-aware tiling); Veda news (head-conditioned tile geometry).
+ * FWD:   x [N][num_heads][d] (token order)  -> y tile order   [tile_off*S][d]
+ * FWD_T: x [N][num_heads][d]                -> y tile-transposed order
+ * INV:   x tile order                       -> y [N][num_heads][d]
+ * FWD/FWD_T write zeros to padding slots; INV reads only real slots and
+ * writes every element of y.  Pure data movement: bit-exact.
+ * dtype VEDA_BF16 or VEDA_F32 (element size 2 or 4 bytes).  Supported:
+ * head_dim*element_size a multiple of 16 bytes and pointers 16-byte aligned
+ * (VEDA_ERR_UNSUPPORTED otherwise).  x and y must not overlap. */
+int veda_tile_permute(const veda_layout* L, int32_t dtype, int32_t dir,
+                      const void* x, void* y, void* stream);
+
+/* Veda §2.1 (distilled tile scoring): TripPool descriptor per tile, per-head
+ * projection, tile-pair scores.  Per head hd and tile j, over the tile's real
+ * slots and per channel:
+ *   desc[side][tile_off[hd]+j] = [mean | max | min]               (3d floats)
+ *   phi[side][tile_off[hd]+j]  = W_side[hd] desc + b_side[hd]     (d_e floats)
+ *   scores[score_off[hd] + i*n_tiles[hd] + j] = <phi[0][..i], phi[1][..j]>
+ * side 0 uses q_perm/w_q/b_q, side 1 k_perm/w_k/b_k.
+ *  q_perm, k_perm  tile order, dtype `dtype` (VEDA_BF16 or VEDA_F32)
+ *  w_q, w_k        f32 [num_heads][d_e][3*head_dim] (may be the same pointer)
+ *  b_q, b_k        f32 [num_heads][d_e], or NULL for no bias
+ *  desc            f32 [2][tile_off[num_heads]][3*head_dim]  (output)
+ *  phi             f32 [2][tile_off[num_heads]][d_e]         (output)
+ *  scores          f32 [score_off[num_heads]]                (output)
+ * Arithmetic in f32.  Supported: head_dim in {64, 128}, 1 <= d_e <= 256,
+ * 16-byte aligned q_perm/k_perm. */
+int veda_tripool_score(const veda_layout* L, int32_t dtype, const void* q_perm,
+                       const void* k_perm, const float* w_q, const float* w_k,
+                       const float* b_q, const float* b_k, int32_t d_e,
+                       float* desc, float* phi, float* scores, void* stream);
+
+/* Tile selection (Veda lay summary and §5; Veda news: 95 % sparsity): per
+ * query tile row, keep the k_per_head[hd] largest scores; equal scores prefer
+ * the lower tile index, -0.0 equals +0.0, NaN ranks below every number.
+ *  scores      f32 as written by veda_tripool_score
+ *  k_per_head  (host) int32 [num_heads], 1 <= k <= n_tiles[hd]
+ *  row_ptr     int32 [tile_off[num_heads] + 1] (output): head-major rows,
+ *              row_ptr[tile_off[hd] + i] = sum_{h<hd} n_h*k_h + i*k_hd
+ *  col_idx     int32 [row_ptr[last]] (output): head-local tile indices,
+ *              ascending within each row
+ * Bit-exact and deterministic.  Supported: max_tiles <= 8192. */
+int veda_select_tiles(const veda_layout* L, const float* scores,
+                      const int32_t* k_per_head, int32_t* row_ptr,
+                      int32_t* col_idx, void* stream);
+
+/* Tile-skipping attention forward (Veda §2.3).  For every query tile of every
+ * head, softmax(sm_scale * Q K^T) V over the real key slots of the key tiles
+ * its CSR row lists (any other tile is never read), computed with online
+ * softmax, bf16 matrix-core products and f32 accumulation.
+ *  q_perm, k_perm  bf16, tile order
+ *  vt_perm         bf16, tile-transposed order (veda_tile_permute FWD_T)
+ *  row_ptr,col_idx CSR as written by veda_select_tiles (any valid CSR:
+ *                  row_ptr non-decreasing, entries in [0, n_tiles[hd]))
+ *  o_perm          bf16, tile order (output); padding query rows unspecified
+ *  lse             f32 [tile_off[num_heads]*S] natural-log log-sum-exp per
+ *                  query slot, or NULL (output)
+ * A query row whose CSR row is empty gets O = 0 and lse = -inf.  Entries of
+ * col_idx outside [0, n_tiles[hd]) are skipped.  Supported: (head_dim,
+ * tile_size) in {(64,64), (128,128)}, 16-byte aligned tensors. */
+int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k_perm,
+                         const void* vt_perm, const int32_t* row_ptr,
+                         const int32_t* col_idx, float sm_scale, void* o_perm,
+                         float* lse, void* stream);
+
+/* Max-pooled attention map, the distillation target (Veda §2.1 target
+ * construction; Veda §2.3: two passes over a random subset of query tiles).
+ * For subset entry s, q_tiles[s] = global tile index g (tile_off[hd] <= g <
+ * tile_off[hd+1]); pass 1 gives each real query row r of the tile
+ *   lse_r = log sum_c exp(sm_scale q_r.k_c)    over every real key of head hd;
+ * pass 2 gives, for every key tile j of the head,
+ *   map[s][j] = max over real r in the tile, real c in tile j of
+ *               exp(sm_scale q_r.k_c - lse_r)
+ * and map[s][j] = 0 for n_tiles[hd] <= j < max_tiles.
+ *  q_perm, k_perm  bf16, tile order
+ *  q_tiles         int32 [n_sub] global query-tile indices; an entry outside
+ *                  [0, tile_off[num_heads]) gets a map row of zeros
+ *  lse             f32 [n_sub*S] (output); padding query rows unspecified
+ *  map             f32 [n_sub][max_tiles] (output)
+ * Supported: (head_dim, tile_size) in {(64,64), (128,128)}. */
+int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void* k_perm,
+                            float sm_scale, const int32_t* q_tiles, int32_t n_sub,
+                            float* lse, float* map, void* stream);
+
+/* Static text for a veda_status value. */
+const char* veda_status_string(int status);
+
+/* sizeof(veda_layout) as compiled into the library, so that bindings can
+ * check their copy of the struct. */
+int64_t veda_layout_sizeof(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VEDA_H */

@@ -1,0 +1,102 @@
+"""Shared helpers of the GPU parity tests: upload a seeded workload, run the
+library's stages through the Python binding, bring results back, and build
+the oracle's per-head inputs from the same host arrays."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import workloads
+from workloads import bf16_to_f64
+
+
+def need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a visible MI355X (torch.cuda.is_available() is False)")
+    return torch
+
+
+def to_dev_bf16(bits: np.ndarray):
+    torch = need_gpu()
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_dev_f32(a: np.ndarray):
+    torch = need_gpu()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def bf16_bits(t) -> np.ndarray:
+    torch = need_gpu()
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_f64(t) -> np.ndarray:
+    return bf16_to_f64(bf16_bits(t))
+
+
+def host(t) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+class Run:
+    """A workload on the GPU plus its oracle-side view."""
+
+    def __init__(self, name: str, seed: int = 0, sparsity: int = None, T: int = None,
+                 k_per_head=None):
+        torch = need_gpu()
+        import tile_sparse_attention_head_amd as V
+        self.V = V
+        self.wl = workloads.make(name, seed, T=T)
+        cfg = self.wl.config
+        self.cfg = cfg
+        self.T, self.H, self.W = self.wl.T, cfg.H, cfg.W
+        self.sparsity = cfg.sparsities[0] if sparsity is None else sparsity
+        self.layer = V.TileSparseAttention(self.T, self.H, self.W, cfg.head_dim, cfg.tile_size,
+                                           self.wl.tile_shapes, sparsity_pct=self.sparsity,
+                                           k_per_head=k_per_head)
+        self.L = self.layer.L
+        self.q = to_dev_bf16(self.wl.q)
+        self.k = to_dev_bf16(self.wl.k)
+        self.v = to_dev_bf16(self.wl.v)
+        self.w = to_dev_f32(self.wl.w)
+        self.sm_scale = cfg.sm_scale
+        self.S = cfg.tile_size
+        self.d = cfg.head_dim
+        self.heads = cfg.heads
+        self.tilings = [oracle.HeadTiling(self.T, self.H, self.W, s) for s in self.wl.tile_shapes]
+
+    def forward(self):
+        out = self.layer.forward(self.q, self.k, self.v, self.w, self.w, self.sm_scale)
+        self.V.lib()
+        need_gpu().cuda.synchronize()
+        return out
+
+    # oracle-side per-head inputs (fp64, tile order)
+    def head_tokens(self, h):
+        return (bf16_to_f64(self.wl.q[:, h, :]), bf16_to_f64(self.wl.k[:, h, :]),
+                bf16_to_f64(self.wl.v[:, h, :]))
+
+    def head_perm(self, h):
+        ht = self.tilings[h]
+        q, k, v = self.head_tokens(h)
+        g = lambda a: oracle.gather(a, self.T, self.H, self.W, ht.shape)
+        return g(q), g(k), g(v)
+
+    def rows(self, h):
+        """Slice of tile-order rows of head h."""
+        a = int(self.L.tile_off[h]) * self.S
+        return slice(a, a + self.L.n(h) * self.S)
+
+    def csr_head(self, h):
+        rp = host(self.layer.row_ptr).astype(np.int64)
+        ci = host(self.layer.col_idx).astype(np.int64)
+        a, b = int(self.L.tile_off[h]), int(self.L.tile_off[h + 1])
+        loc = rp[a:b + 1] - rp[a]
+        return loc, ci[rp[a]:rp[b]]
+
+    def scores_head(self, h):
+        s = host(self.layer.scores)
+        a, n = int(self.L.score_off[h]), self.L.n(h)
+        return s[a:a + n * n].reshape(n, n)

@@ -1,0 +1,164 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/veda.h declares, derive
+the same tile geometry and keep counts as the oracle, and reject bad
+arguments before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import tile_sparse_attention_head_amd as V
+from tile_sparse_attention_head_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "veda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(V.LIB_PATH):
+        pytest.fail("libveda.so is not built (python -m tile_sparse_attention_head_amd.build)")
+    return V.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(veda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_layout_struct_size_matches(lib):
+    assert lib.veda_layout_sizeof() == ctypes.sizeof(_lib.veda_layout)
+
+
+@pytest.mark.parametrize("T,H,W,shapes", [
+    (21, 30, 52, [(4, 4, 8)] * 12),
+    (61, 45, 80, [(1, 8, 16), (2, 8, 8), (4, 4, 8), (8, 4, 4)]),
+    (5, 9, 20, [(8, 4, 4), (1, 8, 16), (2, 8, 8)]),
+    (4, 8, 8, [(4, 4, 4)]),
+])
+def test_layout_matches_oracle(lib, T, H, W, shapes):
+    S = int(np.prod(shapes[0]))
+    L = V.veda_layout_init(T, H, W, 128, S, shapes)
+    off = 0
+    soff = 0
+    for h, s in enumerate(shapes):
+        g = oracle.tile_grid(T, H, W, s)
+        n = g[0] * g[1] * g[2]
+        assert tuple(L.tile_grid[h]) == g and L.n(h) == n
+        assert L.tile_off[h] == off and L.score_off[h] == soff
+        off += n
+        soff += n * n
+    assert L.total_tiles == off and L.total_scores == soff
+    assert L.max_tiles == max(L.n(h) for h in range(len(shapes)))
+
+
+@pytest.mark.parametrize("n", [1, 4, 7, 336, 630, 720, 1830, 1920, 8191])
+@pytest.mark.parametrize("s", [0, 1, 50, 90, 95, 99, 100])
+def test_keep_count_matches_oracle(lib, n, s):
+    assert V.veda_keep_count(n, s) == oracle.keep_count(n, s)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_layout_rejections(lib):
+    bad = [
+        dict(T=0), dict(H=-1), dict(head_dim=0), dict(tile_size=0),
+    ]
+    for b in bad:
+        L = _lib.veda_layout()
+        L.T, L.H, L.W, L.num_heads, L.head_dim, L.tile_size = 4, 8, 8, 1, 64, 64
+        L.tile_shape[0][0], L.tile_shape[0][1], L.tile_shape[0][2] = 4, 4, 4
+        for k, v in b.items():
+            setattr(L, k, v)
+        assert lib.veda_layout_init(ctypes.byref(L)) == -1
+    L = _lib.veda_layout()
+    L.T, L.H, L.W, L.num_heads, L.head_dim, L.tile_size = 4, 8, 8, 1, 64, 64
+    L.tile_shape[0][0], L.tile_shape[0][1], L.tile_shape[0][2] = 4, 4, 8     # 128 != 64
+    assert lib.veda_layout_init(ctypes.byref(L)) == -1
+    L.num_heads = 65
+    assert lib.veda_layout_init(ctypes.byref(L)) == -1
+    assert lib.veda_layout_init(None) == -1
+    with pytest.raises(V.VedaError):
+        V.veda_layout_init(4, 8, 8, 64, 64, [(4, 4, 0)])
+
+
+def test_keep_count_rejections(lib):
+    k = ctypes.c_int32(0)
+    assert lib.veda_keep_count(0, 50, ctypes.byref(k)) == -1
+    assert lib.veda_keep_count(4, 101, ctypes.byref(k)) == -1
+    assert lib.veda_keep_count(4, -1, ctypes.byref(k)) == -1
+    assert lib.veda_keep_count(4, 50, None) == -1
+
+
+def _layout():
+    return V.veda_layout_init(5, 9, 20, 128, 128, [(8, 4, 4), (1, 8, 16)])
+
+
+def test_device_calls_reject_before_launch(lib):
+    L = _layout()
+    Lp = ctypes.byref(L)
+    fake = 1 << 20          # aligned, never dereferenced: calls must fail validation first
+    # tampered layout
+    L2 = _layout()
+    L2.tile_off[1] += 1
+    assert lib.veda_tile_permute(ctypes.byref(L2), 0, 0, fake, fake * 4, None) == -1
+    # permute: nulls, bad enums, misalignment, overlap
+    assert lib.veda_tile_permute(Lp, 0, 0, None, fake, None) == -1
+    assert lib.veda_tile_permute(Lp, 7, 0, fake, fake * 4, None) == -1
+    assert lib.veda_tile_permute(Lp, 0, 9, fake, fake * 4, None) == -1
+    assert lib.veda_tile_permute(Lp, 0, 0, fake + 2, fake * 4, None) == -2
+    assert lib.veda_tile_permute(Lp, 0, 0, fake, fake + 4096, None) == -1      # overlap
+    # tripool: null weights, bad d_e
+    assert lib.veda_tripool_score(Lp, 0, fake, fake, None, fake, None, None, 128, fake, fake, fake, None) == -1
+    assert lib.veda_tripool_score(Lp, 0, fake, fake, fake, fake, None, None, 0, fake, fake, fake, None) == -1
+    assert lib.veda_tripool_score(Lp, 0, fake, fake, fake, fake, None, None, 999, fake, fake, fake, None) == -2
+    # select: k out of range
+    kh = (ctypes.c_int32 * 2)(0, 3)
+    assert lib.veda_select_tiles(Lp, fake, kh, fake, fake, None) == -1
+    kh = (ctypes.c_int32 * 2)(3, L.n(1) + 1)
+    assert lib.veda_select_tiles(Lp, fake, kh, fake, fake, None) == -1
+    # attention: nulls, NaN scale, unsupported shape
+    assert lib.veda_sparse_attn_fwd(Lp, fake, fake, None, fake, fake, 0.1, fake, None, None) == -1
+    assert lib.veda_sparse_attn_fwd(Lp, fake, fake, fake, fake, fake, float("nan"), fake, None, None) == -1
+    L3 = V.veda_layout_init(5, 9, 20, 96, 128, [(8, 4, 4)])
+    assert lib.veda_sparse_attn_fwd(ctypes.byref(L3), fake, fake, fake, fake, fake, 0.1, fake, None, None) == -2
+    # map: negative count, nulls
+    assert lib.veda_oracle_maxpool_map(Lp, fake, fake, 0.1, fake, -1, fake, fake, None) == -1
+    assert lib.veda_oracle_maxpool_map(Lp, None, fake, 0.1, fake, 3, fake, fake, None) == -1
+    assert lib.veda_oracle_maxpool_map(Lp, fake, fake, float("inf"), fake, 3, fake, fake, None) == -1
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4):
+        assert V.status_string(s).startswith("VEDA_")
+    assert "unknown" in V.status_string(12345)
+
+
+def test_product_path_does_not_touch_the_oracle(repo_root):
+    pkg = os.path.join(repo_root, "tile_sparse_attention_head_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
+                assert "oracle/" not in src, f
+    for dirpath, _, files in os.walk(os.path.join(repo_root, "oracle")):
+        for f in files:
+            if f.endswith(".py"):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "tile_sparse_attention_head_amd" not in src, f
+                assert not re.search(r"^\s*(import|from)\s+workloads\b", src, re.M), f

@@ -1,0 +1,429 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle on the same
+seeded inputs.
+
+Bars: bit-exact for the permutation, the TripPool max/min and the CSR;
+mean |d| <= 1e-4 for the TripPool mean and |d| <= 1e-4 max(1, max|S|) for the
+f32 tile scores; attention outputs (bf16) max-abs <= 2e-2 and mean-abs <=
+2e-3, log-sum-exp |d| <= 1e-4; the max-pooled map relative 1e-3 with an
+absolute floor of 1e-7.  The oracle always gets the GPU's own inputs to the
+stage under test (e.g. the GPU's f32 score matrix for top-k, the GPU's CSR
+for attention), so each stage is judged on its own.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_common import Run, bf16_bits, bf16_f64, host, need_gpu, to_dev_bf16, to_dev_f32
+from workloads import bf16_round, bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+ATT_MAX, ATT_MEAN, LSE_TOL = 2e-2, 2e-3, 1e-4
+SMALL = ["tiny", "ragged-small", "ragged-d64"]
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------- permutation
+@pytest.mark.parametrize("name", SMALL + ["wan1.3b-480p-81f"])
+def test_permute_bit_exact(name):
+    _say(f"permute {name}")
+    r = Run(name)
+    V, L = r.V, r.L
+    torch = need_gpu()
+    r.layer.permute_inputs(r.q, r.k, r.v)
+    out = torch.empty_like(r.q)
+    r.layer.o_perm.copy_(r.layer.q_perm)
+    r.layer.unpermute(out)
+    torch.cuda.synchronize()
+    qp = bf16_bits(r.layer.q_perm).reshape(-1, r.d)
+    vt = bf16_bits(r.layer.vt_perm)
+    for h in range(r.heads):
+        ht = r.tilings[h]
+        ref = np.zeros((ht.n * r.S, r.d), dtype=np.uint16)
+        ref[ht.valid] = r.wl.q[ht.perm[ht.valid], h, :]
+        assert np.array_equal(qp[r.rows(h)], ref), h
+        vref = np.zeros((ht.n * r.S, r.d), dtype=np.uint16)
+        vref[ht.valid] = r.wl.v[ht.perm[ht.valid], h, :]
+        vt_h = vt[r.rows(h).start * r.d:r.rows(h).stop * r.d].reshape(ht.n, r.d, r.S)
+        assert np.array_equal(vt_h, vref.reshape(ht.n, r.S, r.d).transpose(0, 2, 1)), h
+    assert np.array_equal(bf16_bits(out), r.wl.q)      # INV(FWD(q)) == q
+
+
+def test_permute_f32_and_inverse_of_arbitrary_tiles():
+    _say("permute f32")
+    torch = need_gpu()
+    r = Run("tiny")
+    V, L = r.V, r.L
+    x = to_dev_f32(r.wl.q32)
+    y = torch.empty(V.tiles_numel(L), dtype=torch.float32, device="cuda")
+    V.veda_tile_permute(L, x, y, V.VEDA_FWD)
+    yt = torch.empty_like(y)
+    V.veda_tile_permute(L, x, yt, V.VEDA_FWD_T)
+    rnd = np.random.default_rng(0).standard_normal(V.tiles_numel(L)).astype(np.float32)
+    z = torch.empty_like(x)
+    V.veda_tile_permute(L, to_dev_f32(rnd), z, V.VEDA_INV)
+    torch.cuda.synchronize()
+    ht = r.tilings[0]
+    ref = oracle.gather(r.wl.q32[:, 0, :].astype(np.float64), r.T, r.H, r.W, ht.shape)
+    assert np.array_equal(host(y).reshape(-1, r.d), ref.astype(np.float32))
+    assert np.array_equal(host(yt).reshape(ht.n, r.d, r.S),
+                          ref.astype(np.float32).reshape(ht.n, r.S, r.d).transpose(0, 2, 1))
+    sref = oracle.scatter(rnd.reshape(-1, r.d).astype(np.float64), r.T, r.H, r.W, ht.shape)
+    assert np.array_equal(host(z).reshape(-1, r.d), sref.astype(np.float32))
+
+
+# -------------------------------------------------------------- estimator
+def _check_estimator(r, dtype="bf16"):
+    torch = need_gpu()
+    V, L = r.V, r.L
+    d, S = r.d, r.S
+    if dtype == "f32":
+        x = to_dev_f32(r.wl.q32)
+        kk = to_dev_f32(r.wl.k32)
+        qp = torch.empty(V.tiles_numel(L), dtype=torch.float32, device="cuda")
+        kp = torch.empty_like(qp)
+        V.veda_tile_permute(L, x, qp, V.VEDA_FWD)
+        V.veda_tile_permute(L, kk, kp, V.VEDA_FWD)
+        V.veda_tripool_score(L, qp, kp, r.w, r.w, r.layer.desc, r.layer.phi, r.layer.scores)
+    else:
+        r.layer.permute_inputs(r.q, r.k, r.v)
+        r.layer.score(r.w, r.w)
+    torch.cuda.synchronize()
+    tot = L.total_tiles
+    desc = host(r.layer.desc).reshape(2, tot, 3 * d)
+    phi = host(r.layer.phi).reshape(2, tot, -1)
+    for h in range(r.heads):
+        ht = r.tilings[h]
+        if dtype == "f32":
+            qt = r.wl.q32[:, h, :].astype(np.float64)
+            kt = r.wl.k32[:, h, :].astype(np.float64)
+        else:
+            qt, kt, _ = r.head_tokens(h)
+        a, b = int(L.tile_off[h]), int(L.tile_off[h + 1])
+        w = r.wl.w[h].astype(np.float64)
+        for side, xt in ((0, qt), (1, kt)):
+            ref = oracle.tripool(oracle.gather(xt, r.T, r.H, r.W, ht.shape), ht.valid, S)
+            got = desc[side, a:b]
+            assert np.array_equal(got[:, d:], ref[:, d:].astype(np.float32)), (h, side)   # max, min exact
+            assert np.abs(got[:, :d] - ref[:, :d]).mean() <= 1e-4
+            assert np.abs(got[:, :d] - ref[:, :d]).max() <= 1e-4
+            pref = oracle.project(got.astype(np.float64), w)     # stage on its own: GPU desc in
+            np.testing.assert_allclose(phi[side, a:b], pref, rtol=0, atol=1e-4 * max(1.0, np.abs(pref).max()))
+        sref = oracle.tile_scores(phi[0, a:b].astype(np.float64), phi[1, a:b].astype(np.float64))
+        sg = r.scores_head(h)
+        assert np.abs(sg - sref).max() <= 1e-4 * max(1.0, np.abs(sref).max()), h
+        # end to end (fp64 all the way from the inputs)
+        fq = oracle.project(oracle.tripool(oracle.gather(qt, r.T, r.H, r.W, ht.shape), ht.valid, S), w)
+        fk = oracle.project(oracle.tripool(oracle.gather(kt, r.T, r.H, r.W, ht.shape), ht.valid, S), w)
+        full = oracle.tile_scores(fq, fk)
+        assert np.abs(sg - full).max() <= 1e-4 * max(1.0, np.abs(full).max()), h
+
+
+@pytest.mark.parametrize("name", SMALL + ["wan1.3b-480p-81f"])
+def test_tripool_score(name):
+    _say(f"tripool {name}")
+    _check_estimator(Run(name))
+
+
+def test_tripool_score_f32_inputs():
+    _say("tripool f32")
+    _check_estimator(Run("tiny"), dtype="f32")
+
+
+def test_tripool_bias_and_two_projections():
+    _say("tripool bias")
+    torch = need_gpu()
+    r = Run("ragged-small")
+    V, L = r.V, r.L
+    rng = np.random.default_rng(5)
+    wk = (rng.standard_normal(r.wl.w.shape) * 0.02).astype(np.float32)
+    bq = rng.standard_normal((r.heads, r.d)).astype(np.float32)
+    bk = rng.standard_normal((r.heads, r.d)).astype(np.float32)
+    r.layer.permute_inputs(r.q, r.k, r.v)
+    V.veda_tripool_score(L, r.layer.q_perm, r.layer.k_perm, r.w, to_dev_f32(wk), r.layer.desc,
+                         r.layer.phi, r.layer.scores, to_dev_f32(bq), to_dev_f32(bk))
+    torch.cuda.synchronize()
+    for h in range(r.heads):
+        ht = r.tilings[h]
+        qt, kt, _ = r.head_tokens(h)
+        fq = oracle.project(oracle.tripool(oracle.gather(qt, r.T, r.H, r.W, ht.shape), ht.valid, r.S),
+                            r.wl.w[h], bq[h])
+        fk = oracle.project(oracle.tripool(oracle.gather(kt, r.T, r.H, r.W, ht.shape), ht.valid, r.S),
+                            wk[h], bk[h])
+        full = oracle.tile_scores(fq, fk)
+        assert np.abs(r.scores_head(h) - full).max() <= 1e-4 * max(1.0, np.abs(full).max())
+
+
+# -------------------------------------------------------------- selection
+@pytest.mark.parametrize("name", SMALL + ["wan1.3b-480p-81f"])
+def test_select_bit_exact_on_gpu_scores(name):
+    _say(f"select {name}")
+    torch = need_gpu()
+    r = Run(name)
+    r.layer.permute_inputs(r.q, r.k, r.v)
+    r.layer.score(r.w, r.w)
+    r.layer.select()
+    torch.cuda.synchronize()
+    rp_all = host(r.layer.row_ptr)
+    off = 0
+    for h in range(r.heads):
+        k = r.layer.k_per_head[h]
+        rp, ci = r.csr_head(h)
+        ref_rp, ref_ci = oracle.select_topk(r.scores_head(h), k)
+        assert rp_all[int(r.L.tile_off[h])] == off
+        assert np.array_equal(rp, ref_rp) and np.array_equal(ci, ref_ci), h
+        off += r.L.n(h) * k
+    assert rp_all[-1] == off
+
+
+def _near_tie_ok(s64, k, gpu_cols, tol):
+    """GPU row (from f32 scores) vs the fp64 oracle row: equal sets, except
+    swaps between tiles whose fp64 scores lie within tol of the k-th."""
+    ref = set(oracle.select_topk(s64[None, :], k)[1].tolist())
+    got = set(gpu_cols.tolist())
+    if ref == got:
+        return 0
+    kth = np.sort(s64)[::-1][k - 1]
+    for j in ref ^ got:
+        assert abs(s64[j] - kth) <= tol, (j, s64[j], kth)
+    return len(ref - got)
+
+
+@pytest.mark.parametrize("name", ["ragged-small", "wan1.3b-480p-81f"])
+def test_selection_end_to_end_near_ties(name):
+    _say(f"selection e2e {name}")
+    torch = need_gpu()
+    r = Run(name)
+    r.layer.permute_inputs(r.q, r.k, r.v)
+    r.layer.score(r.w, r.w)
+    r.layer.select()
+    torch.cuda.synchronize()
+    swaps = 0
+    for h in range(r.heads):
+        ht = r.tilings[h]
+        qt, kt, _ = r.head_tokens(h)
+        w = r.wl.w[h]
+        fq = oracle.project(oracle.tripool(oracle.gather(qt, r.T, r.H, r.W, ht.shape), ht.valid, r.S), w)
+        fk = oracle.project(oracle.tripool(oracle.gather(kt, r.T, r.H, r.W, ht.shape), ht.valid, r.S), w)
+        s64 = oracle.tile_scores(fq, fk)
+        tol = 2e-4 * max(1.0, np.abs(s64).max())
+        rp, ci = r.csr_head(h)
+        k = r.layer.k_per_head[h]
+        for i in range(ht.n):
+            swaps += _near_tie_ok(s64[i], k, ci[rp[i]:rp[i + 1]], tol)
+    _say(f"  near-tie swaps: {swaps}")
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_select_random_scores_with_ties_nan_and_signed_zero(ties):
+    _say(f"select random ties={ties}")
+    torch = need_gpu()
+    import tile_sparse_attention_head_amd as V
+    from workloads import random_scores
+    shapes = [(1, 8, 16), (4, 4, 8), (2, 8, 8)]
+    L = V.veda_layout_init(9, 17, 40, 128, 128, shapes)
+    ks = [1, V.veda_keep_count(L.n(1), 50), L.n(2)]
+    mats = []
+    for h in range(3):
+        s = random_scores(L.n(h), L.n(h), seed=100 + h, ties=ties)
+        if ties:
+            s[::3, ::5] = np.nan
+        mats.append(s)
+    flat = np.concatenate([m.ravel() for m in mats])
+    rp = torch.empty(L.total_tiles + 1, dtype=torch.int32, device="cuda")
+    ci = torch.empty(V.csr_nnz(L, ks), dtype=torch.int32, device="cuda")
+    V.veda_select_tiles(L, to_dev_f32(flat), ks, rp, ci)
+    torch.cuda.synchronize()
+    rp, ci = host(rp), host(ci)
+    for h in range(3):
+        a, b = int(L.tile_off[h]), int(L.tile_off[h + 1])
+        ref_rp, ref_ci = oracle.select_topk(mats[h], ks[h])
+        assert np.array_equal(rp[a:b + 1] - rp[a], ref_rp)
+        assert np.array_equal(ci[rp[a]:rp[b]], ref_ci)
+
+
+# -------------------------------------------------------------- attention
+def _check_attention(r, q_tiles_per_head=None):
+    """GPU attention vs oracle on the GPU's own CSR."""
+    L = r.L
+    o = bf16_f64(r.layer.o_perm).reshape(-1, r.d)
+    lse = host(r.layer.lse)
+    worst, means = 0.0, []
+    for h in range(r.heads):
+        ht = r.tilings[h]
+        qp, kp, vp = r.head_perm(h)
+        rp, ci = r.csr_head(h)
+        tiles = None if q_tiles_per_head is None else q_tiles_per_head[h]
+        ro, rl = oracle.sparse_attention(qp, kp, vp, ht.valid, r.S, rp, ci, r.sm_scale, q_tiles=tiles)
+        sel = ~np.isnan(rl)
+        go = o[r.rows(h)][sel]
+        err = np.abs(go - ro[sel])
+        worst = max(worst, err.max())
+        means.append(err.mean())
+        assert err.max() <= ATT_MAX, (h, err.max())
+        assert err.mean() <= ATT_MEAN, (h, err.mean())
+        assert np.abs(lse[r.rows(h)][sel] - rl[sel]).max() <= LSE_TOL, h
+    return worst, float(np.mean(means))
+
+
+@pytest.mark.parametrize("name,sparsity", [("tiny", 50), ("tiny", 0), ("ragged-small", 75),
+                                           ("ragged-small", 0), ("ragged-d64", 60), ("ragged-d64", 0)])
+def test_sparse_attention_small(name, sparsity):
+    _say(f"attention {name} s={sparsity}")
+    r = Run(name, sparsity=sparsity)
+    r.forward()
+    worst, mean = _check_attention(r)
+    _say(f"  max-abs {worst:.3e} mean-abs {mean:.3e}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged-small", "ragged-d64"])
+def test_zero_sparsity_is_dense_attention_in_token_order(name):
+    _say(f"dense {name}")
+    r = Run(name, sparsity=0)
+    out = r.forward()
+    o = bf16_f64(out)
+    for h in range(r.heads):
+        q, k, v = r.head_tokens(h)
+        od, _ = oracle.dense_attention(q, k, v, r.sm_scale)
+        err = np.abs(o[:, h, :] - od)
+        assert err.max() <= ATT_MAX and err.mean() <= ATT_MEAN, h
+
+
+def test_attention_bench_config_sampled():
+    """Wan-1.3B-like layer (12 heads, 21x30x52, 90 %) in the benchmark's
+    launch configuration: every head, a seeded sample of query tiles."""
+    _say("attention wan1.3b 90% sampled")
+    r = Run("wan1.3b-480p-81f", sparsity=90)
+    r.forward()
+    rng = np.random.default_rng(3)
+    sample = [np.sort(rng.choice(r.L.n(h), size=6, replace=False)) for h in range(r.heads)]
+    for h in range(r.heads):
+        sample[h][0] = r.L.n(h) - 1          # always include a boundary tile
+    worst, mean = _check_attention(r, sample)
+    _say(f"  max-abs {worst:.3e} mean-abs {mean:.3e}")
+
+
+def test_attention_properties_full_size():
+    """At full size: V = 1 gives O = 1 on every real row; outputs finite."""
+    _say("attention properties")
+    torch = need_gpu()
+    r = Run("wan1.3b-480p-81f", sparsity=95)
+    r.layer.permute_inputs(r.q, r.k, r.v)
+    r.layer.score(r.w, r.w)
+    r.layer.select()
+    ones = torch.ones_like(r.v)
+    r.V.veda_tile_permute(r.L, ones, r.layer.vt_perm, r.V.VEDA_FWD_T)
+    r.layer.attend(r.sm_scale)
+    torch.cuda.synchronize()
+    o = bf16_f64(r.layer.o_perm).reshape(-1, r.d)
+    for h in range(r.heads):
+        ht = r.tilings[h]
+        assert np.all(np.abs(o[r.rows(h)][ht.valid] - 1.0) <= 1e-2)
+
+
+def test_attention_edge_csr():
+    """Hand-made CSR: an empty row (O = 0, lse = -inf), out-of-range entries
+    (skipped), a repeated tile, a single kept tile."""
+    _say("attention edge csr")
+    torch = need_gpu()
+    r = Run("tiny")
+    V, L = r.V, r.L
+    r.layer.permute_inputs(r.q, r.k, r.v)
+    rows = [[], [3, -1, 7, 0], [2, 2], [1]]
+    rp = np.cumsum([0] + [len(x) for x in rows]).astype(np.int32)
+    ci = np.array(sum(rows, []), dtype=np.int32)
+    V.veda_sparse_attn_fwd(L, r.layer.q_perm, r.layer.k_perm, r.layer.vt_perm,
+                           torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(), r.sm_scale,
+                           r.layer.o_perm, r.layer.lse)
+    torch.cuda.synchronize()
+    o = bf16_f64(r.layer.o_perm).reshape(-1, r.d)
+    lse = host(r.layer.lse)
+    S = r.S
+    assert np.all(o[:S] == 0) and np.all(np.isneginf(lse[:S]))
+    qp, kp, vp = r.head_perm(0)
+    clean = [[3, 0], [2, 2], [1]]
+    crp = np.cumsum([0, 0] + [len(x) for x in clean])
+    cci = np.array(sum(clean, []))
+    ro, rl = oracle.sparse_attention(qp, kp, vp, r.tilings[0].valid, S, crp, cci, r.sm_scale,
+                                     q_tiles=[1, 2, 3])
+    sel = ~np.isnan(rl)
+    assert np.abs(o[sel] - ro[sel]).max() <= ATT_MAX
+    assert np.abs(lse[sel] - rl[sel]).max() <= LSE_TOL
+
+
+def test_deterministic():
+    _say("determinism")
+    torch = need_gpu()
+    r = Run("ragged-small")
+    a = bf16_bits(r.forward()).copy()
+    rp, ci = host(r.layer.row_ptr).copy(), host(r.layer.col_idx).copy()
+    s = host(r.layer.scores).copy()
+    b = bf16_bits(r.forward())
+    assert np.array_equal(a, b)
+    assert np.array_equal(rp, host(r.layer.row_ptr)) and np.array_equal(ci, host(r.layer.col_idx))
+    assert np.array_equal(s, host(r.layer.scores))
+
+
+# ------------------------------------------------------------ max-pooled map
+def _check_map(r, subset):
+    torch = need_gpu()
+    L = r.L
+    flat = np.concatenate([int(L.tile_off[h]) + s for h, s in enumerate(subset)]).astype(np.int32)
+    q_tiles = torch.from_numpy(flat).cuda()
+    lse, mp = r.layer.maxpool_map(q_tiles, r.sm_scale)
+    torch.cuda.synchronize()
+    lse = host(lse).reshape(-1, r.S)
+    mp = host(mp).reshape(-1, L.max_tiles)
+    row = 0
+    for h, s in enumerate(subset):
+        ht = r.tilings[h]
+        qp, kp, _ = r.head_perm(h)
+        rl, rm = oracle.maxpool_map(qp, kp, ht.valid, r.S, s, r.sm_scale)
+        got = mp[row:row + len(s)]
+        assert np.all(got[:, ht.n:] == 0)
+        g = got[:, :ht.n]
+        assert np.all(np.abs(g - rm) <= np.maximum(1e-3 * rm, 1e-7)), h
+        gl = lse[row:row + len(s)].ravel()
+        sel = ~np.isnan(rl)
+        assert np.abs(gl[sel] - rl[sel]).max() <= LSE_TOL, h
+        row += len(s)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_maxpool_map_small(name):
+    _say(f"map {name}")
+    import workloads
+    r = Run(name)
+    r.layer.permute_inputs(r.q, r.k, r.v)
+    subset = workloads.draw_subset(r.wl, [r.L.n(h) for h in range(r.heads)])
+    _check_map(r, subset)
+
+
+def test_maxpool_map_bench_config_subset():
+    _say("map wan1.3b 10%")
+    import workloads
+    r = Run("wan1.3b-480p-81f")
+    r.layer.permute_inputs(r.q, r.k, r.v)
+    subset = workloads.draw_subset(r.wl, [r.L.n(h) for h in range(r.heads)])
+    subset = [s[:4] for s in subset]           # oracle cost: 4 query tiles per head
+    _check_map(r, subset)
+
+
+def test_maxpool_map_edges():
+    _say("map edges")
+    torch = need_gpu()
+    r = Run("ragged-small")
+    r.layer.permute_inputs(r.q, r.k, r.v)
+    L = r.L
+    # out-of-range entries give zero rows; n_sub = 0 is a no-op
+    qt = torch.tensor([-1, L.total_tiles, int(L.tile_off[1])], dtype=torch.int32, device="cuda")
+    lse, mp = r.layer.maxpool_map(qt, r.sm_scale)
+    torch.cuda.synchronize()
+    mp = host(mp).reshape(3, L.max_tiles)
+    assert np.all(mp[:2] == 0) and np.all(mp[2, :L.n(1)] > 0)
+    empty = torch.empty(0, dtype=torch.int32, device="cuda")
+    r.layer.maxpool_map(empty, r.sm_scale)
+    torch.cuda.synchronize()

@@ -1,0 +1,263 @@
+"""ctypes binding of libveda.so.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Each function here has the name of the C entry point it calls
+(declared in include/veda.h) and takes torch tensors for device buffers; the
+tensors are checked for device, dtype, contiguity and size so that a call
+can never hand the kernels a buffer smaller than the layout needs, then
+their data pointers and the current HIP stream are passed on.  A non-zero
+status raises VedaError.  The library must have been built
+(``python -m tile_sparse_attention_head_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+MAX_HEADS = 64
+VEDA_BF16, VEDA_F32 = 0, 1
+VEDA_FWD, VEDA_INV, VEDA_FWD_T = 0, 1, 2
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libveda.so")
+
+c_i32, c_i64, c_f32, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+
+
+class VedaError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {status_string(status)} ({status})")
+
+
+class veda_layout(ctypes.Structure):
+    _fields_ = [
+        ("T", c_i32), ("H", c_i32), ("W", c_i32),
+        ("num_heads", c_i32), ("head_dim", c_i32), ("tile_size", c_i32),
+        ("tile_shape", (c_i32 * 3) * MAX_HEADS),
+        ("tile_grid", (c_i32 * 3) * MAX_HEADS),
+        ("n_tiles", c_i32 * MAX_HEADS),
+        ("max_tiles", c_i32), ("reserved0", c_i32),
+        ("tile_off", c_i64 * (MAX_HEADS + 1)),
+        ("score_off", c_i64 * (MAX_HEADS + 1)),
+    ]
+
+    # convenience views
+    @property
+    def heads(self) -> int:
+        return self.num_heads
+
+    @property
+    def total_tiles(self) -> int:
+        return int(self.tile_off[self.num_heads])
+
+    @property
+    def total_scores(self) -> int:
+        return int(self.score_off[self.num_heads])
+
+    @property
+    def tokens(self) -> int:
+        return self.T * self.H * self.W
+
+    def n(self, h: int) -> int:
+        return int(self.n_tiles[h])
+
+    def shapes(self):
+        return [tuple(self.tile_shape[h]) for h in range(self.num_heads)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libveda.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m tile_sparse_attention_head_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(veda_layout)
+    sig = {
+        "veda_layout_init": (c_i32, [P]),
+        "veda_keep_count": (c_i32, [c_i32, c_i32, ctypes.POINTER(c_i32)]),
+        "veda_tile_permute": (c_i32, [P, c_i32, c_i32, c_vp, c_vp, c_vp]),
+        "veda_tripool_score": (c_i32, [P, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                       c_vp, c_vp, c_vp, c_vp]),
+        "veda_select_tiles": (c_i32, [P, c_vp, ctypes.POINTER(c_i32), c_vp, c_vp, c_vp]),
+        "veda_sparse_attn_fwd": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_vp, c_vp,
+                                         c_vp]),
+        "veda_oracle_maxpool_map": (c_i32, [P, c_vp, c_vp, c_f32, c_vp, c_i32, c_vp, c_vp,
+                                            c_vp]),
+        "veda_status_string": (ctypes.c_char_p, [c_i32]),
+        "veda_layout_sizeof": (c_i64, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype, fn.argtypes = res, args
+    if L.veda_layout_sizeof() != ctypes.sizeof(veda_layout):
+        raise ImportError("veda_layout size mismatch between libveda.so and the binding")
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().veda_status_string(int(status)).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise VedaError(status, call)
+
+
+# ---------------------------------------------------------------- host calls
+def veda_layout_init(T: int, H: int, W: int, head_dim: int, tile_size: int,
+                     tile_shapes: Sequence[Tuple[int, int, int]]) -> veda_layout:
+    L = veda_layout()
+    L.T, L.H, L.W = int(T), int(H), int(W)
+    L.num_heads = len(tile_shapes)
+    L.head_dim, L.tile_size = int(head_dim), int(tile_size)
+    if not 1 <= L.num_heads <= MAX_HEADS:
+        raise VedaError(-1, "veda_layout_init")
+    for h, s in enumerate(tile_shapes):
+        for a in range(3):
+            L.tile_shape[h][a] = int(s[a])
+    _check(lib().veda_layout_init(ctypes.byref(L)), "veda_layout_init")
+    return L
+
+
+def veda_keep_count(n_tiles: int, sparsity_pct: int) -> int:
+    k = c_i32(0)
+    _check(lib().veda_keep_count(int(n_tiles), int(sparsity_pct), ctypes.byref(k)),
+           "veda_keep_count")
+    return int(k.value)
+
+
+# ------------------------------------------------------------- device calls
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _dev(t, name: str, dtype, numel: int, allow_none: bool = False) -> Optional[int]:
+    torch = _torch()
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return VEDA_BF16
+    if t.dtype == torch.float32:
+        return VEDA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def tokens_numel(L: veda_layout) -> int:
+    return L.tokens * L.num_heads * L.head_dim
+
+
+def tiles_numel(L: veda_layout) -> int:
+    return L.total_tiles * L.tile_size * L.head_dim
+
+
+def veda_tile_permute(L: veda_layout, x, y, direction: int = VEDA_FWD, stream=None) -> None:
+    torch = _torch()
+    dt = _code(x)
+    src_n = tiles_numel(L) if direction == VEDA_INV else tokens_numel(L)
+    dst_n = tokens_numel(L) if direction == VEDA_INV else tiles_numel(L)
+    px = _dev(x, "x", (torch.bfloat16, torch.float32), src_n)
+    py = _dev(y, "y", x.dtype, dst_n)
+    _check(lib().veda_tile_permute(ctypes.byref(L), dt, int(direction), px, py, _stream(stream)),
+           "veda_tile_permute")
+
+
+def veda_tripool_score(L: veda_layout, q_perm, k_perm, w_q, w_k, desc, phi, scores,
+                       b_q=None, b_k=None, stream=None) -> None:
+    torch = _torch()
+    f32 = torch.float32
+    H, d = L.num_heads, L.head_dim
+    d_e = int(w_q.shape[1])
+    if tuple(w_q.shape) != (H, d_e, 3 * d) or tuple(w_k.shape) != (H, d_e, 3 * d):
+        raise ValueError("w_q/w_k must be [heads][d_e][3*head_dim]")
+    dt = _code(q_perm)
+    args = [
+        _dev(q_perm, "q_perm", (torch.bfloat16, f32), tiles_numel(L)),
+        _dev(k_perm, "k_perm", q_perm.dtype, tiles_numel(L)),
+        _dev(w_q, "w_q", f32, H * d_e * 3 * d), _dev(w_k, "w_k", f32, H * d_e * 3 * d),
+        _dev(b_q, "b_q", f32, H * d_e, True), _dev(b_k, "b_k", f32, H * d_e, True),
+    ]
+    outs = [_dev(desc, "desc", f32, 2 * L.total_tiles * 3 * d),
+            _dev(phi, "phi", f32, 2 * L.total_tiles * d_e),
+            _dev(scores, "scores", f32, L.total_scores)]
+    _check(lib().veda_tripool_score(ctypes.byref(L), dt, args[0], args[1], args[2], args[3],
+                                    args[4], args[5], d_e, *outs, _stream(stream)),
+           "veda_tripool_score")
+
+
+def csr_nnz(L: veda_layout, k_per_head: Sequence[int]) -> int:
+    return sum(L.n(h) * int(k_per_head[h]) for h in range(L.num_heads))
+
+
+def veda_select_tiles(L: veda_layout, scores, k_per_head: Sequence[int], row_ptr, col_idx,
+                      stream=None) -> None:
+    torch = _torch()
+    if len(k_per_head) != L.num_heads:
+        raise ValueError("k_per_head needs one entry per head")
+    kh = (c_i32 * L.num_heads)(*[int(v) for v in k_per_head])
+    ps = _dev(scores, "scores", torch.float32, L.total_scores)
+    prp = _dev(row_ptr, "row_ptr", torch.int32, L.total_tiles + 1)
+    pci = _dev(col_idx, "col_idx", torch.int32, csr_nnz(L, k_per_head))
+    _check(lib().veda_select_tiles(ctypes.byref(L), ps, kh, prp, pci, _stream(stream)),
+           "veda_select_tiles")
+
+
+def veda_sparse_attn_fwd(L: veda_layout, q_perm, k_perm, vt_perm, row_ptr, col_idx,
+                         sm_scale: float, o_perm, lse=None, stream=None) -> None:
+    torch = _torch()
+    bf = torch.bfloat16
+    n = tiles_numel(L)
+    args = [_dev(q_perm, "q_perm", bf, n), _dev(k_perm, "k_perm", bf, n),
+            _dev(vt_perm, "vt_perm", bf, n),
+            _dev(row_ptr, "row_ptr", torch.int32, L.total_tiles + 1),
+            _dev(col_idx, "col_idx", torch.int32, 0)]
+    po = _dev(o_perm, "o_perm", bf, n)
+    pl = _dev(lse, "lse", torch.float32, L.total_tiles * L.tile_size, True)
+    _check(lib().veda_sparse_attn_fwd(ctypes.byref(L), *args, float(sm_scale), po, pl,
+                                      _stream(stream)),
+           "veda_sparse_attn_fwd")
+
+
+def veda_oracle_maxpool_map(L: veda_layout, q_perm, k_perm, sm_scale: float, q_tiles, lse, out_map,
+                            stream=None) -> None:
+    torch = _torch()
+    bf = torch.bfloat16
+    n_sub = int(q_tiles.numel())
+    n = tiles_numel(L)
+    args = [_dev(q_perm, "q_perm", bf, n), _dev(k_perm, "k_perm", bf, n)]
+    pq = _dev(q_tiles, "q_tiles", torch.int32, n_sub)
+    pl = _dev(lse, "lse", torch.float32, n_sub * L.tile_size)
+    pm = _dev(out_map, "map", torch.float32, n_sub * L.max_tiles)
+    _check(lib().veda_oracle_maxpool_map(ctypes.byref(L), args[0], args[1], float(sm_scale), pq,
+                                         n_sub, pl, pm, _stream(stream)),
+           "veda_oracle_maxpool_map")

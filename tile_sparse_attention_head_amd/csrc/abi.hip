@@ -1,0 +1,263 @@
+// C ABI of libveda.so: argument validation, layout derivation and launches.
+// Every check runs on the host before anything is enqueued; see veda.h for
+// the contract of each call.
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "veda_internal.hpp"
+
+namespace veda {
+
+DevLayout make_dev_layout(const veda_layout* L) {
+  DevLayout d;
+  std::memset(&d, 0, sizeof(d));
+  d.T = L->T; d.H = L->H; d.W = L->W;
+  d.heads = L->num_heads; d.d = L->head_dim; d.S = L->tile_size;
+  d.max_tiles = L->max_tiles;
+  for (int h = 0; h < L->num_heads; ++h)
+    for (int a = 0; a < 3; ++a) {
+      d.shape[h][a] = L->tile_shape[h][a];
+      d.grid[h][a] = L->tile_grid[h][a];
+    }
+  for (int h = 0; h <= L->num_heads; ++h) {
+    d.tile_off[h] = L->tile_off[h];
+    d.score_off[h] = L->score_off[h];
+  }
+  return d;
+}
+
+namespace {
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("VEDA_DEBUG_SYNC");
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
+}
+
+int finish(int st, void* stream) {
+  if (st != VEDA_OK || !debug_sync()) return st;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return VEDA_ERR_LAUNCH;
+  return hipGetLastError() == hipSuccess ? VEDA_OK : VEDA_ERR_LAUNCH;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Derive every field from the inputs into `out`; false if the inputs are bad.
+bool derive(const veda_layout* L, veda_layout* out) {
+  if (L == nullptr) return false;
+  if (L->T < 1 || L->H < 1 || L->W < 1) return false;
+  if (L->num_heads < 1 || L->num_heads > VEDA_MAX_HEADS) return false;
+  if (L->head_dim < 1 || L->tile_size < 1) return false;
+  if ((int64_t)L->T * L->H * L->W > INT32_MAX) return false;
+  *out = *L;
+  int64_t toff = 0, soff = 0;
+  int32_t mx = 0;
+  for (int h = 0; h < L->num_heads; ++h) {
+    const int32_t* p = L->tile_shape[h];
+    if (p[0] < 1 || p[1] < 1 || p[2] < 1) return false;
+    if ((int64_t)p[0] * p[1] * p[2] != L->tile_size) return false;
+    const int64_t nT = ceil_div(L->T, p[0]), nH = ceil_div(L->H, p[1]), nW = ceil_div(L->W, p[2]);
+    const int64_t n = nT * nH * nW;
+    if (n > INT32_MAX) return false;
+    out->tile_grid[h][0] = (int32_t)nT;
+    out->tile_grid[h][1] = (int32_t)nH;
+    out->tile_grid[h][2] = (int32_t)nW;
+    out->n_tiles[h] = (int32_t)n;
+    out->tile_off[h] = toff;
+    out->score_off[h] = soff;
+    toff += n;
+    soff += n * n;
+    if (n > mx) mx = (int32_t)n;
+  }
+  for (int h = L->num_heads; h < VEDA_MAX_HEADS; ++h) {
+    out->tile_grid[h][0] = out->tile_grid[h][1] = out->tile_grid[h][2] = 0;
+    out->n_tiles[h] = 0;
+  }
+  out->tile_off[L->num_heads] = toff;
+  out->score_off[L->num_heads] = soff;
+  for (int h = L->num_heads + 1; h <= VEDA_MAX_HEADS; ++h) {
+    out->tile_off[h] = toff;
+    out->score_off[h] = soff;
+  }
+  out->max_tiles = mx;
+  out->reserved0 = 0;
+  // CSR rows and entries are int32: rows = tiles, entries <= sum n^2.
+  if (toff + 1 > INT32_MAX || soff > INT32_MAX) return false;
+  return true;
+}
+
+// A layout passed to a device call must be exactly what veda_layout_init made.
+bool layout_ok(const veda_layout* L) {
+  veda_layout d;
+  if (!derive(L, &d)) return false;
+  for (int h = 0; h < L->num_heads; ++h) {
+    if (d.n_tiles[h] != L->n_tiles[h]) return false;
+    for (int a = 0; a < 3; ++a)
+      if (d.tile_grid[h][a] != L->tile_grid[h][a]) return false;
+  }
+  for (int h = 0; h <= L->num_heads; ++h)
+    if (d.tile_off[h] != L->tile_off[h] || d.score_off[h] != L->score_off[h]) return false;
+  return d.max_tiles == L->max_tiles;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool disjoint(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x + na <= y || y + nb <= x;
+}
+
+bool attn_shape_ok(const veda_layout* L) {
+  return (L->head_dim == 128 && L->tile_size == 128) || (L->head_dim == 64 && L->tile_size == 64);
+}
+
+}  // namespace
+}  // namespace veda
+
+using namespace veda;
+
+extern "C" {
+
+int veda_layout_init(veda_layout* L) {
+  veda_layout d;
+  if (!derive(L, &d)) return VEDA_ERR_INVALID_ARG;
+  *L = d;
+  return VEDA_OK;
+}
+
+int veda_keep_count(int32_t n_tiles, int32_t sparsity_pct, int32_t* k_out) {
+  if (k_out == nullptr || n_tiles < 1 || sparsity_pct < 0 || sparsity_pct > 100)
+    return VEDA_ERR_INVALID_ARG;
+  const int64_t k = ceil_div((int64_t)n_tiles * (100 - sparsity_pct), 100);
+  *k_out = (int32_t)(k < 1 ? 1 : k);
+  return VEDA_OK;
+}
+
+int veda_tile_permute(const veda_layout* L, int32_t dtype, int32_t dir, const void* x, void* y,
+                      void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (dtype != VEDA_BF16 && dtype != VEDA_F32) return VEDA_ERR_INVALID_ARG;
+  if (dir != VEDA_FWD && dir != VEDA_INV && dir != VEDA_FWD_T) return VEDA_ERR_INVALID_ARG;
+  if (x == nullptr || y == nullptr) return VEDA_ERR_INVALID_ARG;
+  const int esize = dtype == VEDA_F32 ? 4 : 2;
+  if ((L->head_dim * esize) % 16 != 0) return VEDA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(y)) return VEDA_ERR_UNSUPPORTED;
+  if (dir == VEDA_FWD_T) {
+    if ((L->tile_size * esize) % 16 != 0) return VEDA_ERR_UNSUPPORTED;
+    if ((size_t)L->head_dim * (L->tile_size + 16 / esize) * esize > 65536) return VEDA_ERR_UNSUPPORTED;
+  }
+  const size_t tok = (size_t)L->T * L->H * L->W * L->num_heads * L->head_dim * esize;
+  const size_t til = (size_t)L->tile_off[L->num_heads] * L->tile_size * L->head_dim * esize;
+  if (!disjoint(x, dir == VEDA_INV ? til : tok, y, dir == VEDA_INV ? tok : til))
+    return VEDA_ERR_INVALID_ARG;
+  const DevLayout dl = make_dev_layout(L);
+  return finish(launch_permute(dl, dtype, dir, x, y, (hipStream_t)stream), stream);
+}
+
+int veda_tripool_score(const veda_layout* L, int32_t dtype, const void* q_perm,
+                       const void* k_perm, const float* w_q, const float* w_k, const float* b_q,
+                       const float* b_k, int32_t d_e, float* desc, float* phi, float* scores,
+                       void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (dtype != VEDA_BF16 && dtype != VEDA_F32) return VEDA_ERR_INVALID_ARG;
+  if (q_perm == nullptr || k_perm == nullptr || w_q == nullptr || w_k == nullptr ||
+      desc == nullptr || phi == nullptr || scores == nullptr)
+    return VEDA_ERR_INVALID_ARG;
+  if (d_e < 1) return VEDA_ERR_INVALID_ARG;
+  if (d_e > 256) return VEDA_ERR_UNSUPPORTED;
+  if (L->head_dim != 64 && L->head_dim != 128) return VEDA_ERR_UNSUPPORTED;
+  if (!aligned16(q_perm) || !aligned16(k_perm)) return VEDA_ERR_UNSUPPORTED;
+  const DevLayout dl = make_dev_layout(L);
+  return finish(launch_tripool_score(dl, dtype, q_perm, k_perm, w_q, w_k, b_q, b_k, d_e, desc, phi,
+                                     scores, (hipStream_t)stream),
+                stream);
+}
+
+int veda_select_tiles(const veda_layout* L, const float* scores, const int32_t* k_per_head,
+                      int32_t* row_ptr, int32_t* col_idx, void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (scores == nullptr || k_per_head == nullptr || row_ptr == nullptr || col_idx == nullptr)
+    return VEDA_ERR_INVALID_ARG;
+  int64_t nnz = 0;
+  for (int h = 0; h < L->num_heads; ++h) {
+    if (k_per_head[h] < 1 || k_per_head[h] > L->n_tiles[h]) return VEDA_ERR_INVALID_ARG;
+    nnz += (int64_t)L->n_tiles[h] * k_per_head[h];
+  }
+  if (nnz > INT32_MAX) return VEDA_ERR_INVALID_ARG;
+  if (L->max_tiles > 8192) return VEDA_ERR_UNSUPPORTED;
+  const DevLayout dl = make_dev_layout(L);
+  return finish(launch_select(dl, scores, k_per_head, row_ptr, col_idx, (hipStream_t)stream),
+                stream);
+}
+
+int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k_perm,
+                         const void* vt_perm, const int32_t* row_ptr, const int32_t* col_idx,
+                         float sm_scale, void* o_perm, float* lse, void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (q_perm == nullptr || k_perm == nullptr || vt_perm == nullptr || row_ptr == nullptr ||
+      col_idx == nullptr || o_perm == nullptr)
+    return VEDA_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return VEDA_ERR_INVALID_ARG;
+  if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
+  if (!aligned16(q_perm) || !aligned16(k_perm) || !aligned16(vt_perm) || !aligned16(o_perm))
+    return VEDA_ERR_UNSUPPORTED;
+  if (debug_sync()) {   // host-side CSR validation (synchronous, debug only)
+    const int64_t rows = L->tile_off[L->num_heads];
+    std::vector<int32_t> rp(rows + 1);
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return VEDA_ERR_LAUNCH;
+    if (hipMemcpy(rp.data(), row_ptr, (rows + 1) * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+      return VEDA_ERR_LAUNCH;
+    if (rp[0] < 0) return VEDA_ERR_BAD_CSR;
+    for (int64_t r = 0; r < rows; ++r)
+      if (rp[r + 1] < rp[r]) return VEDA_ERR_BAD_CSR;
+    std::vector<int32_t> ci(rp[rows]);
+    if (!ci.empty() && hipMemcpy(ci.data(), col_idx, ci.size() * sizeof(int32_t),
+                                 hipMemcpyDeviceToHost) != hipSuccess)
+      return VEDA_ERR_LAUNCH;
+    for (int h = 0; h < L->num_heads; ++h)
+      for (int64_t r = L->tile_off[h]; r < L->tile_off[h + 1]; ++r)
+        for (int32_t p = rp[r]; p < rp[r + 1]; ++p)
+          if (ci[p] < 0 || ci[p] >= L->n_tiles[h]) return VEDA_ERR_BAD_CSR;
+  }
+  const DevLayout dl = make_dev_layout(L);
+  return finish(launch_sparse_attn(dl, q_perm, k_perm, vt_perm, row_ptr, col_idx, sm_scale, o_perm,
+                                   lse, (hipStream_t)stream),
+                stream);
+}
+
+int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void* k_perm,
+                            float sm_scale, const int32_t* q_tiles, int32_t n_sub, float* lse,
+                            float* map, void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (n_sub < 0) return VEDA_ERR_INVALID_ARG;
+  if (n_sub > 0 && (q_perm == nullptr || k_perm == nullptr || q_tiles == nullptr ||
+                    lse == nullptr || map == nullptr))
+    return VEDA_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return VEDA_ERR_INVALID_ARG;
+  if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
+  if (n_sub > 0 && (!aligned16(q_perm) || !aligned16(k_perm))) return VEDA_ERR_UNSUPPORTED;
+  const DevLayout dl = make_dev_layout(L);
+  return finish(launch_oracle_map(dl, q_perm, k_perm, sm_scale, q_tiles, n_sub, lse, map,
+                                  (hipStream_t)stream),
+                stream);
+}
+
+int64_t veda_layout_sizeof(void) { return (int64_t)sizeof(veda_layout); }
+
+const char* veda_status_string(int status) {
+  switch (status) {
+    case VEDA_OK: return "VEDA_OK";
+    case VEDA_ERR_INVALID_ARG: return "VEDA_ERR_INVALID_ARG: invalid argument";
+    case VEDA_ERR_UNSUPPORTED: return "VEDA_ERR_UNSUPPORTED: outside the supported set";
+    case VEDA_ERR_LAUNCH: return "VEDA_ERR_LAUNCH: HIP launch or kernel failure";
+    case VEDA_ERR_BAD_CSR: return "VEDA_ERR_BAD_CSR: invalid CSR";
+    default: return "unknown veda status";
+  }
+}
+
+}  // extern "C"

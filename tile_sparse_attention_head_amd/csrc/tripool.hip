@@ -1,0 +1,204 @@
+// Distilled tile-score estimator (Veda §2.1): TripPool descriptor per tile
+// (mean | max | min of the tile's real tokens, per channel), one projection
+// per head, and the query-tile x key-tile score product.
+//
+// Three kernels:
+//  1. pool:    one workgroup per (tile, side).  Lanes read the tile's rows as
+//              16-byte chunks (coalesced), keep per-lane running sum/max/min of
+//              8 (bf16) or 4 (f32) channels, then reduce across row groups in
+//              LDS.  HBM-bound: reads the tile once, writes 3d floats.
+//  2. project: phi = desc W^T + b, batched over (side, head).
+//  3. score:   scores = phi_q phi_k^T, batched over heads.
+// 2 and 3 share one LDS-tiled f32 "C = A B^T" kernel (64x64 tile, 4x4 outputs
+// per lane); both operands are read along their contiguous K dimension.
+#include "veda_internal.hpp"
+
+namespace veda {
+namespace {
+
+constexpr int kPoolThreads = 256;
+
+template <typename E>
+struct Vec16;  // 16 bytes of E
+template <>
+struct Vec16<__bf16> { __bf16 v[8]; };
+template <>
+struct Vec16<float> { float v[4]; };
+
+template <typename E, int D>
+__global__ __launch_bounds__(kPoolThreads) void tripool_pool_kernel(DevLayout L,
+                                                                    const E* __restrict__ q,
+                                                                    const E* __restrict__ k,
+                                                                    float* __restrict__ desc) {
+  constexpr int VEC = 16 / sizeof(E);
+  constexpr int CH = D / VEC;                 // chunks per row
+  constexpr int RG = kPoolThreads / CH;       // row groups
+  __shared__ float red[3][RG][D];
+  const int side = blockIdx.y;
+  const int64_t g = blockIdx.x;
+  const int h = head_of_tile(L, g);
+  const TileExtent e = tile_extent(L, h, (int)(g - L.tile_off[h]));
+  const E* x = (side ? k : q) + g * (int64_t)L.S * D;
+  const int ch = threadIdx.x % CH, rg = threadIdx.x / CH;
+  float sum[VEC], mx[VEC], mn[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) { sum[c] = 0.f; mx[c] = -INFINITY; mn[c] = INFINITY; }
+  const bool full = e.full();
+  for (int u = rg; u < L.S; u += RG) {
+    if (!full && !e.slot_real(u)) continue;
+    const Vec16<E> v = reinterpret_cast<const Vec16<E>*>(x + (int64_t)u * D)[ch];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      const float f = (float)v.v[c];
+      sum[c] += f;
+      mx[c] = fmaxf(mx[c], f);
+      mn[c] = fminf(mn[c], f);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) {
+    red[0][rg][ch * VEC + c] = sum[c];
+    red[1][rg][ch * VEC + c] = mx[c];
+    red[2][rg][ch * VEC + c] = mn[c];
+  }
+  __syncthreads();
+  const float inv_cnt = 1.0f / (float)e.count();
+  float* out = desc + ((int64_t)side * L.tile_off[L.heads] + g) * 3 * D;
+  for (int c = threadIdx.x; c < D; c += kPoolThreads) {
+    float s = 0.f, a = -INFINITY, b = INFINITY;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      s += red[0][r][c];
+      a = fmaxf(a, red[1][r][c]);
+      b = fminf(b, red[2][r][c]);
+    }
+    out[c] = s * inv_cnt;
+    out[D + c] = a;
+    out[2 * D + c] = b;
+  }
+}
+
+// ---- batched f32 C[m][n] = sum_k A[m][k] B[n][k] (+ bias[n]) -------------
+constexpr int BM = 64, BN = 64, BK = 16, kGemmThreads = 256;
+
+struct GemmArgs {
+  const float* A; const float* B; const float* bias; float* C;
+  int M, N, K; int64_t lda, ldb, ldc;
+};
+
+__device__ __forceinline__ void gemm_abt_tile(const GemmArgs& a, int m0, int n0) {
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[BK][BN + 4];
+  const int t = threadIdx.x;
+  const int tm = (t / 16) * 4, tn = (t % 16) * 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < a.K; k0 += BK) {
+    // each lane stages 4 elements of A and 4 of B (row = t/4, k = (t%4)*4 + c)
+    const int r = t / 4, kc = (t % 4) * 4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int kk = k0 + kc + c;
+      const int am = m0 + r, bn = n0 + r;
+      As[kc + c][r] = (am < a.M && kk < a.K) ? a.A[am * a.lda + kk] : 0.f;
+      Bs[kc + c][r] = (bn < a.N && kk < a.K) ? a.B[bn * a.ldb + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { av[i] = As[kk][tm + i]; bv[i] = Bs[kk][tn + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + tm + i;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nn = n0 + tn + j;
+      if (nn >= a.N) continue;
+      a.C[m * a.ldc + nn] = acc[i][j] + (a.bias ? a.bias[nn] : 0.f);
+    }
+  }
+}
+
+// batch = side*heads + h: desc rows of head h -> phi rows of head h.
+__global__ __launch_bounds__(kGemmThreads) void project_kernel(DevLayout L, int d_e,
+                                                               const float* __restrict__ desc,
+                                                               const float* __restrict__ wq,
+                                                               const float* __restrict__ wk,
+                                                               const float* bq, const float* bk,
+                                                               float* __restrict__ phi) {
+  const int side = blockIdx.z / L.heads, h = blockIdx.z % L.heads;
+  const int64_t total = L.tile_off[L.heads];
+  const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  if (m0 >= n_h || n0 >= d_e) return;
+  const int K = 3 * L.d;
+  GemmArgs a;
+  a.A = desc + ((int64_t)side * total + L.tile_off[h]) * K;
+  a.B = (side ? wk : wq) + (int64_t)h * d_e * K;
+  const float* b = side ? bk : bq;
+  a.bias = b ? b + (int64_t)h * d_e : nullptr;
+  a.C = phi + ((int64_t)side * total + L.tile_off[h]) * d_e;
+  a.M = n_h; a.N = d_e; a.K = K; a.lda = K; a.ldb = K; a.ldc = d_e;
+  gemm_abt_tile(a, m0, n0);
+}
+
+__global__ __launch_bounds__(kGemmThreads) void score_kernel(DevLayout L, int d_e,
+                                                             const float* __restrict__ phi,
+                                                             float* __restrict__ scores) {
+  const int h = blockIdx.z;
+  const int64_t total = L.tile_off[L.heads];
+  const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  if (m0 >= n_h || n0 >= n_h) return;
+  GemmArgs a;
+  a.A = phi + L.tile_off[h] * d_e;
+  a.B = phi + (total + L.tile_off[h]) * d_e;
+  a.bias = nullptr;
+  a.C = scores + L.score_off[h];
+  a.M = n_h; a.N = n_h; a.K = d_e; a.lda = d_e; a.ldb = d_e; a.ldc = n_h;
+  gemm_abt_tile(a, m0, n0);
+}
+
+}  // namespace
+
+int launch_tripool_score(const DevLayout& L, int dtype, const void* q, const void* k,
+                         const float* wq, const float* wk, const float* bq, const float* bk,
+                         int d_e, float* desc, float* phi, float* scores, hipStream_t s) {
+  const unsigned tiles = (unsigned)L.tile_off[L.heads];
+  if (tiles == 0) return VEDA_OK;
+  const dim3 pg(tiles, 2);
+  if (dtype == VEDA_F32) {
+    if (L.d == 128)
+      hipLaunchKernelGGL((tripool_pool_kernel<float, 128>), pg, dim3(kPoolThreads), 0, s, L,
+                         (const float*)q, (const float*)k, desc);
+    else
+      hipLaunchKernelGGL((tripool_pool_kernel<float, 64>), pg, dim3(kPoolThreads), 0, s, L,
+                         (const float*)q, (const float*)k, desc);
+  } else {
+    if (L.d == 128)
+      hipLaunchKernelGGL((tripool_pool_kernel<__bf16, 128>), pg, dim3(kPoolThreads), 0, s, L,
+                         (const __bf16*)q, (const __bf16*)k, desc);
+    else
+      hipLaunchKernelGGL((tripool_pool_kernel<__bf16, 64>), pg, dim3(kPoolThreads), 0, s, L,
+                         (const __bf16*)q, (const __bf16*)k, desc);
+  }
+  if (launch_status() != VEDA_OK) return VEDA_ERR_LAUNCH;
+  const unsigned mb = (unsigned)((L.max_tiles + BM - 1) / BM);
+  hipLaunchKernelGGL(project_kernel, dim3((d_e + BN - 1) / BN, mb, 2 * L.heads),
+                     dim3(kGemmThreads), 0, s, L, d_e, desc, wq, wk, bq, bk, phi);
+  if (launch_status() != VEDA_OK) return VEDA_ERR_LAUNCH;
+  hipLaunchKernelGGL(score_kernel, dim3(mb, mb, L.heads), dim3(kGemmThreads), 0, s, L, d_e,
+                     phi, scores);
+  return launch_status();
+}
+
+}  // namespace veda

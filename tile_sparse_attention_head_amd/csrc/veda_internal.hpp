@@ -1,0 +1,86 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "veda.h"
+
+namespace veda {
+
+// Geometry handed to kernels by value (kernel-argument memory, scalar loads).
+struct DevLayout {
+  int32_t T, H, W;
+  int32_t heads;
+  int32_t d;
+  int32_t S;
+  int32_t max_tiles;
+  int32_t pad0;
+  int32_t shape[VEDA_MAX_HEADS][3];   // pt, ph, pw
+  int32_t grid[VEDA_MAX_HEADS][3];    // nT, nH, nW
+  int64_t tile_off[VEDA_MAX_HEADS + 1];
+  int64_t score_off[VEDA_MAX_HEADS + 1];
+};
+
+DevLayout make_dev_layout(const veda_layout* L);
+
+// Head owning global tile index g (tile_off[h] <= g < tile_off[h+1]).  The
+// value is uniform across a workgroup, so this runs on the scalar unit.
+__device__ __forceinline__ int head_of_tile(const DevLayout& L, int64_t g) {
+  int h = 0;
+  while (h + 1 < L.heads && g >= L.tile_off[h + 1]) ++h;
+  return h;
+}
+
+// Number of real slots along each axis of tile j of head h, i.e. how much of
+// the (pt, ph, pw) box lies inside the T x H x W grid.
+struct TileExtent {
+  int it, ih, iw;      // tile coordinates
+  int lt, lh, lw;      // real extent along t, h, w (<= pt, ph, pw)
+  int pt, ph, pw;
+  __device__ __forceinline__ bool full() const { return lt == pt && lh == ph && lw == pw; }
+  __device__ __forceinline__ int count() const { return lt * lh * lw; }
+  // slot u = (dt*ph + dh)*pw + dw is real iff dt < lt, dh < lh, dw < lw
+  __device__ __forceinline__ bool slot_real(int u) const {
+    const int dw = u % pw;
+    const int r = u / pw;
+    const int dh = r % ph;
+    const int dt = r / ph;
+    return dt < lt && dh < lh && dw < lw;
+  }
+};
+
+__device__ __forceinline__ TileExtent tile_extent(const DevLayout& L, int h, int j) {
+  TileExtent e;
+  e.pt = L.shape[h][0]; e.ph = L.shape[h][1]; e.pw = L.shape[h][2];
+  const int nH = L.grid[h][1], nW = L.grid[h][2];
+  e.iw = j % nW;
+  e.ih = (j / nW) % nH;
+  e.it = j / (nW * nH);
+  e.lt = min(e.pt, L.T - e.it * e.pt);
+  e.lh = min(e.ph, L.H - e.ih * e.ph);
+  e.lw = min(e.pw, L.W - e.iw * e.pw);
+  return e;
+}
+
+// Launchers (each returns a veda_status; arguments already validated).
+int launch_permute(const DevLayout& L, int dtype, int dir, const void* x, void* y,
+                   hipStream_t s);
+int launch_tripool_score(const DevLayout& L, int dtype, const void* q, const void* k,
+                         const float* wq, const float* wk, const float* bq,
+                         const float* bk, int d_e, float* desc, float* phi,
+                         float* scores, hipStream_t s);
+int launch_select(const DevLayout& L, const float* scores, const int32_t* k_host,
+                  int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
+int launch_sparse_attn(const DevLayout& L, const void* q, const void* k, const void* vt,
+                       const int32_t* row_ptr, const int32_t* col_idx, float sm_scale,
+                       void* o, float* lse, hipStream_t s);
+int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm_scale,
+                      const int32_t* q_tiles, int n_sub, float* lse, float* map,
+                      hipStream_t s);
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? VEDA_OK : VEDA_ERR_LAUNCH;
+}
+
+}  // namespace veda

@@ -1,0 +1,101 @@
+"""One tile-sparse attention layer on the GPU: buffers plus the call order.
+
+``TileSparseAttention`` owns the device buffers one layer needs (allocated
+once with torch; the library itself never allocates) and enqueues the
+library's calls in the order of the method (Veda §2.1-§2.3):
+
+  1. veda_tile_permute   Q, K -> tile order; V -> tile-transposed order
+  2. veda_tripool_score  TripPool + per-head projection + tile scores
+  3. veda_select_tiles   top-k key tiles per query tile -> CSR
+  4. veda_sparse_attn_fwd
+  5. veda_tile_permute   O -> token order
+
+and, on request, veda_oracle_maxpool_map for a subset of query tiles.  All
+calls go on the current torch stream without synchronising.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+from . import _lib as V
+
+
+class TileSparseAttention:
+    def __init__(self, T: int, H: int, W: int, head_dim: int, tile_size: int,
+                 tile_shapes: Sequence[Tuple[int, int, int]], sparsity_pct: Optional[int] = None,
+                 k_per_head: Optional[Sequence[int]] = None, d_e: Optional[int] = None,
+                 device="cuda"):
+        import torch
+        self.torch = torch
+        self.L = V.veda_layout_init(T, H, W, head_dim, tile_size, tile_shapes)
+        L = self.L
+        if k_per_head is None:
+            if sparsity_pct is None:
+                raise ValueError("give sparsity_pct or k_per_head")
+            k_per_head = [V.veda_keep_count(L.n(h), sparsity_pct) for h in range(L.num_heads)]
+        self.k_per_head = [int(v) for v in k_per_head]
+        self.d_e = int(d_e or head_dim)
+        self.nnz = V.csr_nnz(L, self.k_per_head)
+        nt = V.tiles_numel(L)
+        bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+        dev = torch.device(device)
+        self.q_perm = torch.empty(nt, dtype=bf, device=dev)
+        self.k_perm = torch.empty(nt, dtype=bf, device=dev)
+        self.vt_perm = torch.empty(nt, dtype=bf, device=dev)
+        self.o_perm = torch.empty(nt, dtype=bf, device=dev)
+        self.lse = torch.empty(L.total_tiles * tile_size, dtype=f32, device=dev)
+        self.desc = torch.empty(2 * L.total_tiles * 3 * head_dim, dtype=f32, device=dev)
+        self.phi = torch.empty(2 * L.total_tiles * self.d_e, dtype=f32, device=dev)
+        self.scores = torch.empty(L.total_scores, dtype=f32, device=dev)
+        self.row_ptr = torch.empty(L.total_tiles + 1, dtype=i32, device=dev)
+        self.col_idx = torch.empty(max(1, self.nnz), dtype=i32, device=dev)
+
+    # individual stages ---------------------------------------------------
+    def permute_inputs(self, q, k, v, stream=None):
+        V.veda_tile_permute(self.L, q, self.q_perm, V.VEDA_FWD, stream)
+        V.veda_tile_permute(self.L, k, self.k_perm, V.VEDA_FWD, stream)
+        V.veda_tile_permute(self.L, v, self.vt_perm, V.VEDA_FWD_T, stream)
+
+    def score(self, w_q, w_k, b_q=None, b_k=None, stream=None):
+        V.veda_tripool_score(self.L, self.q_perm, self.k_perm, w_q, w_k, self.desc, self.phi,
+                             self.scores, b_q, b_k, stream)
+
+    def select(self, stream=None):
+        V.veda_select_tiles(self.L, self.scores, self.k_per_head, self.row_ptr, self.col_idx,
+                            stream)
+
+    def attend(self, sm_scale: float, with_lse: bool = True, stream=None):
+        V.veda_sparse_attn_fwd(self.L, self.q_perm, self.k_perm, self.vt_perm, self.row_ptr,
+                               self.col_idx, sm_scale, self.o_perm,
+                               self.lse if with_lse else None, stream)
+
+    def unpermute(self, out, stream=None):
+        V.veda_tile_permute(self.L, self.o_perm, out, V.VEDA_INV, stream)
+
+    # whole layer -----------------------------------------------------------
+    def forward(self, q, k, v, w_q, w_k, sm_scale: float, out=None, b_q=None, b_k=None,
+                stream=None):
+        """q, k, v: bf16 [N][heads][d] (token order).  Returns O, same shape."""
+        if out is None:
+            out = self.torch.empty_like(q)
+        self.permute_inputs(q, k, v, stream)
+        self.score(w_q, w_k, b_q, b_k, stream)
+        self.select(stream)
+        self.attend(sm_scale, True, stream)
+        self.unpermute(out, stream)
+        return out
+
+    def maxpool_map(self, q_tiles, sm_scale: float, lse=None, out_map=None, stream=None):
+        """Max-pooled map of the query tiles ``q_tiles`` (int32 global tile
+        indices) over the tile-ordered Q, K already in this layer's buffers."""
+        torch = self.torch
+        n_sub = int(q_tiles.numel())
+        if lse is None:
+            lse = torch.empty(max(1, n_sub * self.L.tile_size), dtype=torch.float32,
+                              device=self.q_perm.device)
+        if out_map is None:
+            out_map = torch.empty(max(1, n_sub * self.L.max_tiles), dtype=torch.float32,
+                                  device=self.q_perm.device)
+        V.veda_oracle_maxpool_map(self.L, self.q_perm, self.k_perm, sm_scale, q_tiles, lse,
+                                  out_map, stream)
+        return lse, out_map
