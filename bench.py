@@ -1,0 +1,285 @@
+"""Benchmark of the tile-sparse attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--sparsity S] [--no-cpu-baseline] [--no-context]
+
+One step is one pass of every stage of the path over one synthetic layer
+whose inputs are already resident in HBM:
+
+  veda_tile_permute (Q, K forward; V forward-transposed) -> veda_tripool_score
+  -> veda_select_tiles -> veda_sparse_attn_fwd -> veda_tile_permute (O inverse)
+  -> veda_oracle_maxpool_map (the distillation target on the workload's seeded
+     query-tile subset)
+
+W untimed steps run first, then exactly K steps are timed between two device
+synchronisations.  Every stage is also bracketed by HIP events on the stream
+the kernels run on, which gives the per-layer latency (all stages but the
+map), the map's latency and the attention kernel's average launch duration.
+
+Printed: one JSON line.  ``value`` is the effective throughput of the step in
+TFLOP/s: the matrix work the tile kernels compute (4*S^2*d per kept
+(query tile, key tile) pair of the attention, plus 2 passes x 2*S^2*d per
+(subset query tile, key tile) pair of the map) divided by the step time.
+``roofline`` is for the attention kernel, the path's matrix-core hot spot;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload.  With --gpus above 1 the benchmark refuses: this path runs on one
+GPU (heads shard across GPUs without any exchange inside the path).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E peak (published)
+ATTN_SOURCES = ("tile_sparse_attention_head_amd/csrc/sparse_attn.hip",
+                "tile_sparse_attention_head_amd/csrc/attn_common.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_fwd_traffic_wan1.3b-480p-81f.md")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, sparsity: int):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, or None when it is missing, for another
+    workload, or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("TRAFFIC_JSON "):
+            rec = json.loads(line[len("TRAFFIC_JSON "):])
+            if (rec.get("kernel_hash") == kernel_hash() and rec.get("workload") == workload
+                    and int(rec.get("sparsity_pct", -1)) == sparsity):
+                return rec
+    return None
+
+
+def attn_flops(L, k_per_head, S, d):
+    pairs = sum(L.n(h) * k_per_head[h] for h in range(L.num_heads))
+    return 4.0 * S * S * d * pairs, pairs
+
+
+def map_flops(n_sub_per_head, L, S, d):
+    return sum(2 * 2.0 * S * S * d * n_sub_per_head[h] * L.n(h) for h in range(L.num_heads))
+
+
+class Bench:
+    def __init__(self, name: str, sparsity: int, seed: int = 0):
+        import torch
+
+        import tile_sparse_attention_head_amd as V
+        import workloads
+        self.torch, self.V = torch, V
+        self.wl = workloads.make(name, seed)
+        cfg = self.wl.config
+        self.cfg = cfg
+        self.sparsity = sparsity
+        dev = torch.device("cuda:0")
+        up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+        self.q, self.k, self.v = up(self.wl.q), up(self.wl.k), up(self.wl.v)
+        self.w = torch.from_numpy(self.wl.w).to(dev)
+        self.layer = V.TileSparseAttention(self.wl.T, cfg.H, cfg.W, cfg.head_dim, cfg.tile_size,
+                                           self.wl.tile_shapes, sparsity_pct=sparsity, device=dev)
+        L = self.layer.L
+        self.L = L
+        subset = workloads.draw_subset(self.wl, [L.n(h) for h in range(L.num_heads)])
+        self.n_sub = [len(s) for s in subset]
+        flat = np.concatenate([int(L.tile_off[h]) + s for h, s in enumerate(subset)]).astype(np.int32)
+        self.q_tiles = torch.from_numpy(flat).to(dev)
+        self.map_lse = torch.empty(max(1, flat.size * cfg.tile_size), dtype=torch.float32, device=dev)
+        self.map_out = torch.empty(max(1, flat.size * L.max_tiles), dtype=torch.float32, device=dev)
+        self.out = torch.empty_like(self.q)
+        self.flops_c, self.pairs = attn_flops(L, self.layer.k_per_head, cfg.tile_size, cfg.head_dim)
+        self.flops_d = map_flops(self.n_sub, L, cfg.tile_size, cfg.head_dim)
+        self.stages = ["permute_in", "tripool_score", "select", "sparse_attn", "permute_out", "map"]
+        self.ev = None
+
+    def _events(self, reps):
+        E = self.torch.cuda.Event
+        return [[E(enable_timing=True) for _ in range(len(self.stages) + 1)] for _ in range(reps)]
+
+    def step(self, ev=None, with_map=True):
+        ly, sm = self.layer, self.cfg.sm_scale
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        ly.permute_inputs(self.q, self.k, self.v)
+        rec(1)
+        ly.score(self.w, self.w)
+        rec(2)
+        ly.select()
+        rec(3)
+        ly.attend(sm, with_lse=True)
+        rec(4)
+        ly.unpermute(self.out)
+        rec(5)
+        if with_map:
+            ly.maxpool_map(self.q_tiles, sm, self.map_lse, self.map_out)
+        rec(6)
+
+    def run(self, steps: int, warmup: int, with_map=True):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(with_map=with_map)
+        ev = self._events(steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(ev[i], with_map=with_map)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps * 1e3
+        per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(self.stages))] for e in ev])
+        return wall, per.mean(axis=0), per
+
+
+def cpu_baseline(wl, sparsity: int, budget_s: float = 12.0):
+    """The oracle (as it stands) on whole heads of the same workload, head by
+    head until ``budget_s`` has passed: gather Q/K/V, TripPool + projection +
+    scores, top-k, sparse attention of every query tile, inverse scatter, and
+    the max-pooled map on the head's query-tile subset."""
+    import oracle
+    import workloads
+    from workloads import bf16_to_f64
+    cfg = wl.config
+    T, H, W, S, d = wl.T, cfg.H, cfg.W, cfg.tile_size, cfg.head_dim
+    tilings = [oracle.HeadTiling(T, H, W, s) for s in wl.tile_shapes]
+    subset = workloads.draw_subset(wl, [t.n for t in tilings])
+    flops, heads = 0.0, 0
+    t0 = time.perf_counter()
+    for h in range(cfg.heads):
+        ht = tilings[h]
+        q, k, v = (bf16_to_f64(a[:, h, :]) for a in (wl.q, wl.k, wl.v))
+        qp, kp, vp = (oracle.gather(a, T, H, W, ht.shape) for a in (q, k, v))
+        w = wl.w[h].astype(np.float64)
+        s = oracle.tile_scores(oracle.project(oracle.tripool(qp, ht.valid, S), w),
+                               oracle.project(oracle.tripool(kp, ht.valid, S), w))
+        kk = oracle.keep_count(ht.n, sparsity)
+        rp, ci = oracle.select_topk(s, kk)
+        o, _ = oracle.sparse_attention(qp, kp, vp, ht.valid, S, rp, ci, cfg.sm_scale)
+        oracle.scatter(np.nan_to_num(o), T, H, W, ht.shape)
+        oracle.maxpool_map(qp, kp, ht.valid, S, subset[h], cfg.sm_scale)
+        flops += 4.0 * S * S * d * ht.n * kk + 2 * 2.0 * S * S * d * len(subset[h]) * ht.n
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {cfg.heads} heads, whole path per head (gather, TripPool/score, "
+                      f"top-k, sparse attention of all query tiles, scatter, map on the head's "
+                      f"{cfg.map_subset_pct}% query-tile subset), {dt:.1f} s, fp64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan1.3b-480p-81f")
+    ap.add_argument("--sparsity", type=int, default=90)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the 95 %% and 0 %% (dense) context runs")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one torch copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path shards by "
+                                   "head across GPUs with no exchange inside it, so --gpus N>1 "
+                                   "is not measured here"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+
+    b = Bench(args.workload, args.sparsity)
+    wall_ms, stage_ms, per = b.run(args.steps, args.warmup)
+    names = b.stages
+    st = dict(zip(names, [float(x) for x in stage_ms]))
+    layer_ms = sum(st[n] for n in names if n != "map")
+    attn_ms = st["sparse_attn"]
+    total_flops = b.flops_c + b.flops_d
+    value = total_flops / (wall_ms * 1e-3) / 1e12
+    achieved = b.flops_c / (attn_ms * 1e-3) / 1e12
+    cfg, L = b.cfg, b.L
+    traffic = read_traffic(args.workload, args.sparsity)
+
+    context = {}
+    if not args.no_context:
+        for s in (95, 0):
+            if s == args.sparsity:
+                continue
+            c = Bench(args.workload, s)
+            w2, sm2, _ = c.run(max(3, args.steps // 4), 2, with_map=False)
+            d2 = dict(zip(names, [float(x) for x in sm2]))
+            a_ms = d2["sparse_attn"]
+            context[f"sparsity_{s}"] = {
+                "ms_per_layer": sum(d2[n] for n in names if n != "map"),
+                "attn_ms": a_ms, "attn_tflops": c.flops_c / (a_ms * 1e-3) / 1e12,
+                "attn_frac_peak": c.flops_c / (a_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "kept_pairs": c.pairs}
+            del c
+            torch.cuda.empty_cache()
+        if "sparsity_0" in context:
+            context["attn_speedup_vs_dense"] = context["sparsity_0"]["attn_ms"] / attn_ms
+            context["density"] = b.pairs / context["sparsity_0"]["kept_pairs"]
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(b.wl, args.sparsity)
+
+    line = {
+        "metric": "ms/layer and effective TFLOP/s (% bf16 MFMA peak) at 90/95% tile sparsity",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}; {args.sparsity}% tile sparsity; "
+                        f"max-pooled map on a {cfg.map_subset_pct}% query-tile subset",
+            "tokens": L.tokens, "heads": L.num_heads, "head_dim": cfg.head_dim,
+            "tile_size": cfg.tile_size, "tile_shapes": sorted(set(b.wl.tile_shapes)),
+            "sparsity_pct": args.sparsity, "kept_tiles_per_row": sorted(set(b.layer.k_per_head)),
+            "map_subset_tiles": int(sum(b.n_sub)), "parallelism": "single GPU"},
+        "ms_per_layer": layer_ms,
+        "layer_tflops_effective": b.flops_c / (layer_ms * 1e-3) / 1e12,
+        "stage_ms": st,
+        "roofline": {"kernel": "veda_sparse_attn_fwd", "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "algorithmic_flops_per_launch": b.flops_c, "avg_launch_ms": attn_ms},
+        "map_kernel": {"kernel": "veda_oracle_maxpool_map", "avg_launch_ms": st["map"],
+                       "tflops": b.flops_d / (st["map"] * 1e-3) / 1e12,
+                       "frac": b.flops_d / (st["map"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "context": context,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

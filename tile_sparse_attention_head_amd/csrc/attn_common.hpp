@@ -1,24 +1,35 @@
 // Building blocks shared by the tile-skipping attention forward and the
 // max-pooled map kernels: bf16 matrix-core (MFMA) tile products on gfx950.
 //
-// Orientation.  Each wave owns 32 query rows.  Logits are computed transposed,
-// S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the key tile (from LDS) is the
-// A operand and the wave's queries (held in registers for the whole kernel)
-// are the B operand.  In the 32x32 accumulator layout lane l holds column
-// l % 32 -- one query -- and 16 rows, so every row statistic of softmax is a
-// reduction inside the lane plus one exchange with lane l ^ 32.  The output
-// is accumulated transposed too, O^T = V^T P^T: V^T (from LDS) is the A
-// operand and P^T, the probabilities already sitting in the lane that owns
-// the query, is the B operand without any data movement.
+// Orientation.  Logits are computed transposed, S^T = K Q^T, with
+// v_mfma_f32_32x32x16_bf16: key rows (from LDS) are the A operand and a
+// wave's 32 queries (held in registers for the whole kernel) the B operand.
+// In the 32x32 accumulator layout lane l holds column l % 32 -- one query --
+// and 16 rows, so every softmax row statistic is a reduction inside the lane
+// plus one exchange with lane l ^ 32.  The output is accumulated transposed
+// too, O^T = V^T P^T: V^T rows (from LDS) are the A operand and P^T, the
+// probabilities already sitting in the lane that owns the query, the B
+// operand, with no data movement.
 //
 // Key order inside a 32-key block.  Accumulator element i of lane l is row
-// m = 8(i/4) + 4(l/32) + i%4.  The key tile is written to LDS with bits 2 and
-// 3 of the key index swapped, so row m of the A operand is key swap23(m) and
-// element i of lane l is key 16(i/8) + 8(l/32) + i%8: each lane then holds 8
-// consecutive keys per half block, exactly the 8 contraction indices the B
-// operand of the P V product wants from it (lane half l/32 supplies k-indices
-// 8(l/32) .. 8(l/32)+7).  Both operands of each product take their k-indices
-// by the same rule, so the products are exact contractions.
+// m = 8(i/4) + 4(l/32) + i%4.  Key rows are placed in LDS with bits 2 and 3
+// of the key index swapped, so A-operand row m is key swap23(m) and element
+// i of lane l is key 16(i/8) + 8(l/32) + i%8: each lane holds 8 consecutive
+// keys per half block, which are exactly the 8 contraction indices that lane
+// supplies to the P V product.  Both operands of each product take their
+// contraction indices by the same rule, so the products are exact.
+//
+// Waves.  A workgroup owns one query tile of S queries with 2*S/32 waves:
+// wave w takes query block w % (S/32) and key half w / (S/32) of every key
+// tile, so two waves share each SIMD and one's softmax can run while the
+// other's matrix products do.  The two halves are merged at the end.
+//
+// LDS staging.  Tiles are copied global -> LDS with global_load_lds_dwordx4
+// (no register staging): one instruction moves 64 lanes x 16 bytes into 1 KiB
+// of consecutive LDS, and each lane picks the global 16-byte chunk that must
+// land at its LDS position.  Rows are stored unpadded with their 16-byte
+// chunks XOR-swizzled by the row index, so the lanes that read one chunk
+// column of consecutive rows hit distinct banks.
 #pragma once
 
 #include "veda_internal.hpp"
@@ -29,6 +40,7 @@ namespace attn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct Chunk { uint32_t x, y, z, w; };
 
@@ -40,66 +52,61 @@ __device__ __forceinline__ int swap23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-// Key index (within the tile) of accumulator element i of lane half `hf`
-// in key block kb.
-__device__ __forceinline__ int key_of(int kb, int i, int hf) {
-  return kb * 32 + 16 * (i >> 3) + 8 * hf + (i & 7);
+// Key index (within its 32-key block) of accumulator element i, lane half hf.
+__device__ __forceinline__ int key_in_block(int i, int hf) {
+  return 16 * (i >> 3) + 8 * hf + (i & 7);
 }
 
 template <int D, int S>
 struct Cfg {
-  static constexpr int NW = S / 32;                // waves per workgroup
-  static constexpr int NT = NW * 64;               // threads per workgroup
-  static constexpr int KB = S / 32;                // 32-key blocks per tile
-  static constexpr int KS = D / 16;                // MFMA k-steps over head_dim
-  static constexpr int DB = D / 32;                // 32-row blocks of O^T
-  static constexpr int PS = S / 16;                // MFMA k-steps over keys
-  static constexpr int KROW = D * 2 + 16;          // LDS bytes per key row (padded)
-  static constexpr int VROW = S * 2 + 16;          // LDS bytes per V^T row (padded)
-  static constexpr int KBYTES = S * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int CHUNKS = S * D * 2 / 16;    // 16-byte chunks per K (or V) tile
-  static constexpr int CPT = CHUNKS / NT;          // chunks per thread
-  static_assert(CHUNKS % NT == 0, "tile chunks must split evenly");
+  static constexpr int QB = S / 32;            // 32-query blocks per tile
+  static constexpr int KH = 2;                 // key halves (waves per query block)
+  static constexpr int NW = QB * KH;           // waves per workgroup
+  static constexpr int NT = NW * 64;           // threads per workgroup
+  static constexpr int KPW = S / KH;           // keys per wave per tile
+  static constexpr int KBW = KPW / 32;         // 32-key blocks per wave
+  static constexpr int KS = D / 16;            // MFMA k-steps over head_dim
+  static constexpr int DB = D / 32;            // 32-row blocks of O^T
+  static constexpr int PSW = KPW / 16;         // MFMA k-steps over a wave's keys
+  static constexpr int CPR_K = D / 8;          // 16-byte chunks per key row
+  static constexpr int CPR_V = S / 8;          // 16-byte chunks per V^T row
+  static constexpr int TILE_BYTES = S * D * 2; // one bf16 tile
+  static constexpr int CHUNKS = TILE_BYTES / 16;
+  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / NW;
+  static_assert(TILE_BYTES % (1024 * NW) == 0, "tile must split into whole DMA rounds");
+  static_assert(KBW >= 1, "a wave needs at least one key block");
 };
 
-// Global -> registers: chunk c = tid + q*NT of a contiguous 16-byte-chunked tile.
-template <int CPT, int NT>
-__device__ __forceinline__ void load_tile_regs(Chunk (&r)[CPT], const Chunk* __restrict__ src,
-                                               int tid) {
-#pragma unroll
-  for (int q = 0; q < CPT; ++q) r[q] = src[tid + q * NT];
+// Byte offset of logical 16-byte chunk c of row r in a swizzled LDS tile.
+template <int CPR>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return (r * CPR + (c ^ (r & (CPR - 1)))) * 16;
 }
 
-// Registers -> LDS for a K tile ([S][D] row-major in memory): key rows go to
-// LDS row swap23(key) of their 32-key block, padded row pitch KROW.
-template <int D, int S>
-__device__ __forceinline__ void store_k_lds(unsigned char* lds, const Chunk (&r)[D / 16],
-                                            int tid) {
-  using C = Cfg<D, S>;
-  constexpr int CPR = D / 8;
+template <int CPR>
+__device__ __forceinline__ bf16x8 lds_chunk(const unsigned char* tile, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(tile + lds_off<CPR>(r, c));
+}
+
+// Issue this wave's share of the global -> LDS copy of one tile (rows of CPR
+// chunks).  SWAP places key rows at LDS row swap23(row) within 32-row blocks.
+template <int CPR, int PER_WAVE, bool SWAP>
+__device__ __forceinline__ void dma_tile(const Chunk* __restrict__ g, unsigned char* lds, int wave,
+                                         int lane) {
 #pragma unroll
-  for (int q = 0; q < C::CPT; ++q) {
-    const int c = tid + q * C::NT;
-    const int key = c / CPR, col = c % CPR;
-    const int row = (key & ~31) | swap23(key & 31);
-    *reinterpret_cast<Chunk*>(lds + row * C::KROW + col * 16) = r[q];
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int q = wave * PER_WAVE + i;           // 1 KiB block of the LDS tile
+    const int lc = q * 64 + lane;                // LDS chunk this lane fills
+    const int r = lc / CPR, p = lc % CPR;
+    const int c = p ^ (r & (CPR - 1));
+    const int gr = SWAP ? ((r & ~31) | swap23(r & 31)) : r;
+    __builtin_amdgcn_global_load_lds((const void*)(g + gr * CPR + c), (lds_void*)(lds + q * 1024),
+                                     16, 0, 0);
   }
 }
 
-// Registers -> LDS for a V^T tile ([D][S] in memory), padded pitch VROW.
-template <int D, int S>
-__device__ __forceinline__ void store_vt_lds(unsigned char* lds, const Chunk (&r)[D / 16],
-                                             int tid) {
-  using C = Cfg<D, S>;
-  constexpr int CPR = S / 8;
-#pragma unroll
-  for (int q = 0; q < C::CPT; ++q) {
-    const int c = tid + q * C::NT;
-    const int dd = c / CPR, col = c % CPR;
-    *reinterpret_cast<Chunk*>(lds + dd * C::VROW + col * 16) = r[q];
-  }
-}
+// Wait for this wave's outstanding memory operations (including LDS DMA).
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 // The wave's 32 query rows as MFMA B operands: qr[s] holds dims
 // 16s + 8(l/32) .. +7 of query row (l % 32).
@@ -110,35 +117,96 @@ __device__ __forceinline__ void load_q_regs(bf16x8 (&qr)[D / 16], const __bf16* 
   for (int s = 0; s < D / 16; ++s) qr[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hf);
 }
 
-// S^T for one tile: acc[kb] = K[kb block] Q^T (raw dot products, f32).
-template <int D, int S>
-__device__ __forceinline__ void qk_tile(f32x16 (&acc)[S / 32], const unsigned char* klds,
-                                        const bf16x8 (&qr)[D / 16], int n, int hf) {
-  using C = Cfg<D, S>;
+// S^T of NKB key blocks starting at block kb0: acc[b] = K[block] Q^T.  The
+// blocks are independent accumulation chains, interleaved, and the operands
+// of step s+1 are read from LDS while the products of step s run.
+template <int D, int NKB>
+__device__ __forceinline__ void qk_blocks(f32x16 (&acc)[NKB], const unsigned char* ktile, int kb0,
+                                          const bf16x8 (&qr)[D / 16], int n, int hf) {
+  constexpr int CPR = D / 8;
+  constexpr int KS = D / 16;
 #pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb) {
-    f32x16 a = {};
-    const unsigned char* rowp = klds + (kb * 32 + n) * C::KROW + hf * 16;
+  for (int b = 0; b < NKB; ++b) acc[b] = f32x16{};
+  bf16x8 a[2][NKB];
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(rowp + s * 32);
-      a = mfma32(kv, qr[s], a);
+  for (int b = 0; b < NKB; ++b) a[0][b] = lds_chunk<CPR>(ktile, (kb0 + b) * 32 + n, hf);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (s + 1 < KS) {
+#pragma unroll
+      for (int b = 0; b < NKB; ++b)
+        a[(s + 1) & 1][b] = lds_chunk<CPR>(ktile, (kb0 + b) * 32 + n, 2 * (s + 1) + hf);
     }
-    acc[kb] = a;
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) acc[b] = mfma32(a[s & 1][b], qr[s], acc[b]);
   }
 }
 
-// Padding keys of a boundary tile -> -inf.
-template <int KB>
-__device__ __forceinline__ void mask_keys(f32x16 (&acc)[KB], const TileExtent& e, int hf) {
+// Validity of the S slots of a tile, as S/32 32-bit words (bit u of word w is
+// slot 32w + u), for each of the 8 ways a tile can be cut by the grid:
+// combo bit 2/1/0 set = the tile's t/h/w extent is the partial one at the
+// far edge of the grid.  Built once per workgroup by S threads.
+template <int S>
+struct MaskTable {
+  uint32_t w[8][S / 32];
+};
+
+template <int S>
+__device__ __forceinline__ void build_mask_table(MaskTable<S>& mt, const DevLayout& L, int h,
+                                                 int tid) {
+  const int pt = L.shape[h][0], ph = L.shape[h][1], pw = L.shape[h][2];
+  const int et = L.T - (L.grid[h][0] - 1) * pt;   // extent of the last tile along t
+  const int eh = L.H - (L.grid[h][1] - 1) * ph;
+  const int ew = L.W - (L.grid[h][2] - 1) * pw;
+  if (tid < S) {
+    const int dw = tid % pw, r = tid / pw, dh = r % ph, dt = r / ph;
+    const int lane = tid & 63;
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
+    for (int c = 0; c < 8; ++c) {
+      const bool ok = (!(c & 4) || dt < et) && (!(c & 2) || dh < eh) && (!(c & 1) || dw < ew);
+      const uint64_t bal = __ballot(ok);
+      if (lane == 0) {
+        mt.w[c][(tid >> 5)] = (uint32_t)bal;
+        if (S >= 64) mt.w[c][(tid >> 5) + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+  }
+}
+
+// Which of the 8 cuts tile e is (0 = whole tile).
+__device__ __forceinline__ int cut_of(const TileExtent& e) {
+  return (e.lt < e.pt ? 4 : 0) | (e.lh < e.ph ? 2 : 0) | (e.lw < e.pw ? 1 : 0);
+}
+
+// Padding keys -> -inf for key blocks kb0 .. kb0+NKB-1, given the tile's
+// validity words.  Lane half hf holds keys 8hf..8hf+7 and 16+8hf..16+8hf+7 of
+// each block, i.e. bytes hf and 2+hf of the block's word.
+template <int NKB, int S>
+__device__ __forceinline__ void mask_keys(f32x16 (&acc)[NKB], const MaskTable<S>& mt, int cut,
+                                          int kb0, int hf) {
+#pragma unroll
+  for (int b = 0; b < NKB; ++b) {
+    const uint32_t wbits = mt.w[cut][kb0 + b] >> (8 * hf);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (!e.slot_real(key_of(kb, i, hf))) acc[kb][i] = -INFINITY;
+      if (!((wbits >> (16 * (i >> 3) + (i & 7))) & 1u)) acc[b][i] = -INFINITY;
+  }
+}
+
+template <int NKB>
+__device__ __forceinline__ float max_of(const f32x16 (&acc)[NKB]) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < NKB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) m = fmaxf(m, fmaxf(acc[b][i], acc[b][i + 1]));
+  return m;
 }
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// exp2 whose argument is finite or -inf; (-inf) - (-inf) never reaches it.
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Global -> local XCD-aware workgroup order: hardware places workgroup b on
 // XCD b % 8; give each XCD a contiguous range of logical work items so that

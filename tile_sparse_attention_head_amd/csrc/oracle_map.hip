@@ -3,15 +3,16 @@
 // key-tile blocks; Veda §2.3: built in two passes over a random subset of
 // query tiles).
 //
-// One workgroup per subset query tile; the wave layout and MFMA products are
-// those of the attention kernel (queries in registers, key tiles staged
-// through two LDS buffers one tile ahead).  A single loop runs 2*n_h steps over
-// the head's key tiles:
-//   pass 1 (steps 0 .. n_h-1):   online row maximum and sum of exp2 -> lse;
+// One workgroup per subset query tile with the wave layout of the attention
+// kernel (wave (qb, kh): 32 queries in registers, key half kh of every key
+// tile; key tiles copied straight into two LDS stages one tile ahead).  A
+// single loop runs 2*n_h steps over the head's key tiles:
+//   pass 1 (steps 0 .. n_h-1): online row maximum and sum of exp2 over the
+//     wave's keys; the two key halves are combined through LDS -> lse;
 //   pass 2 (steps n_h .. 2n_h-1): per key tile, each query's largest logit,
-//     p = exp2(max - lse), max over the tile's real queries (inside the wave
-//     by lane exchanges, across waves through LDS) -> map[s][j].
-// Pass 2 takes one exp per (query, key tile) rather than per logit.
+//     p = exp2(max - lse), then the maximum over the tile's real queries
+//     (inside the wave by lane exchanges, across waves through LDS) -> map.
+// Pass 2 takes one exp per (query, key tile) rather than one per logit.
 #include "attn_common.hpp"
 
 namespace veda {
@@ -20,16 +21,19 @@ namespace {
 using namespace attn;
 
 template <int D, int S>
-__global__ __launch_bounds__(2 * S, 1) void oracle_map_kernel(
+__global__ __launch_bounds__(4 * S, S / 64) void oracle_map_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
     const int32_t* __restrict__ q_tiles, float* __restrict__ lse_out, float* __restrict__ map) {
   using C = Cfg<D, S>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2][C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][C::TILE_BYTES];
+  __shared__ float ml[C::NW][2][64];
   __shared__ float red[2][C::NW];
+  __shared__ MaskTable<S> mtab;
 
   const int64_t sidx = xcd_remap(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, hf = lane >> 5;
+  const int qb = wave % C::QB, kh = wave / C::QB;
   float* mrow = map + sidx * (int64_t)L.max_tiles;
   const int64_t g = q_tiles[sidx];
   if (g < 0 || g >= L.tile_off[L.heads]) {           // out-of-range entry: zero row
@@ -40,15 +44,15 @@ __global__ __launch_bounds__(2 * S, 1) void oracle_map_kernel(
   const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
   const int64_t head_base = L.tile_off[h];
   const TileExtent eq = tile_extent(L, h, (int)(g - head_base));
-  const bool q_real = eq.slot_real(wave * 32 + n);
+  const bool q_real = eq.slot_real(qb * 32 + n);
 
   bf16x8 qr[C::KS];
-  load_q_regs<D>(qr, q + (g * S + wave * 32 + n) * D, hf);
+  load_q_regs<D>(qr, q + (g * S + qb * 32 + n) * D, hf);
 
-  Chunk kreg[C::CPT];
   const Chunk* kc = reinterpret_cast<const Chunk*>(k) + head_base * (int64_t)C::CHUNKS;
-  load_tile_regs<C::CPT, C::NT>(kreg, kc, tid);
-  store_k_lds<D, S>(smem[0], kreg, tid);
+  dma_tile<C::CPR_K, C::DMA_PER_WAVE, true>(kc, smem[0], wave, lane);
+  build_mask_table<S>(mtab, L, h, tid);
+  wait_all();
   __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.f, lse2 = 0.f;
@@ -56,56 +60,56 @@ __global__ __launch_bounds__(2 * S, 1) void oracle_map_kernel(
   int stage = 0;
   for (int it = 0; it < steps; ++it) {
     const int j = it < n_h ? it : it - n_h;
-    const bool more = it + 1 < steps;
-    if (more) {
-      const int jn = (it + 1) % n_h;
-      load_tile_regs<C::CPT, C::NT>(kreg, kc + (int64_t)jn * C::CHUNKS, tid);
-    }
+    if (it + 1 < steps)
+      dma_tile<C::CPR_K, C::DMA_PER_WAVE, true>(kc + (int64_t)((it + 1) % n_h) * C::CHUNKS,
+                                                 smem[stage ^ 1], wave, lane);
     if (it == n_h) {
-      // end of pass 1: combine the half-lanes' (max, sum) -> base-2 lse
-      const float mo = xor32(m_run), lo = xor32(l_run);
-      const float mt = fmaxf(m_run, mo);
-      const float lt = l_run * __builtin_amdgcn_exp2f(m_run - mt) + lo * __builtin_amdgcn_exp2f(mo - mt);
+      // end of pass 1: combine with the other key half -> base-2 lse per query
+      const int partner = (kh ^ 1) * C::QB + qb;
+      const float m_a = m_run, l_a = l_run + xor32(l_run);
+      const float m_b = ml[partner][0][lane], l_b = ml[partner][1][lane];
+      const float mt = fmaxf(m_a, m_b);
+      const float lt = (m_a == -INFINITY ? 0.f : l_a * exp2_(m_a - mt)) +
+                       (m_b == -INFINITY ? 0.f : l_b * exp2_(m_b - mt));
       lse2 = mt + __log2f(lt);
-      if (hf == 0) lse_out[sidx * S + wave * 32 + n] = lse2 * 0.69314718055994531f;
+      if (kh == 0 && hf == 0) lse_out[sidx * S + qb * 32 + n] = lse2 * 0.69314718055994531f;
     }
-    if (it > n_h && tid == 0) {   // flush the previous key tile's block maximum
+    if (it > n_h && tid == 0) {   // publish the previous key tile's block maximum
       float v = red[(it - 1) & 1][0];
 #pragma unroll
       for (int w = 1; w < C::NW; ++w) v = fmaxf(v, red[(it - 1) & 1][w]);
       mrow[j - 1] = v;
     }
 
-    f32x16 sacc[C::KB];
-    qk_tile<D, S>(sacc, smem[stage], qr, n, hf);
-    const TileExtent e = tile_extent(L, h, j);
-    if (!e.full()) mask_keys<C::KB>(sacc, e, hf);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    f32x16 sacc[C::KBW];
+    qk_blocks<D, C::KBW>(sacc, smem[stage], kh * C::KBW, qr, n, hf);
+    const int cut = cut_of(tile_extent(L, h, j));
+    if (cut != 0) mask_keys<C::KBW, S>(sacc, mtab, cut, kh * C::KBW, hf);
+    float mx = max_of<C::KBW>(sacc);
+    mx = fmaxf(mx, xor32(mx));
 
     if (it < n_h) {
-      mx = fmaxf(mx, xor32(mx));
       const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
       float psum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+      for (int b = 0; b < C::KBW; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          psum += __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], scale_log2, -m_new));
-      l_run = fmaf(l_run, __builtin_amdgcn_exp2f(m_run - m_new), psum);
+        for (int i = 0; i < 16; ++i) psum += exp2_(fmaf(sacc[b][i], scale_log2, neg_m));
+      l_run = (m_run == -INFINITY ? 0.f : l_run * exp2_(m_run - m_new)) + psum;
       m_run = m_new;
+      if (it == n_h - 1) {
+        ml[wave][0][lane] = m_run;
+        ml[wave][1][lane] = l_run + xor32(l_run);
+      }
     } else {
-      mx = fmaxf(mx, xor32(mx));
-      float pr = q_real ? __builtin_amdgcn_exp2f(fmaf(mx, scale_log2, -lse2)) : 0.f;
+      float pr = (q_real && mx != -INFINITY) ? exp2_(fmaf(mx, scale_log2, -lse2)) : 0.f;
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) pr = fmaxf(pr, __shfl_xor(pr, o, 64));
       if (lane == 0) red[it & 1][wave] = pr;
     }
 
-    if (more) store_k_lds<D, S>(smem[stage ^ 1], kreg, tid);
+    wait_all();
     __syncthreads();
     stage ^= 1;
   }
