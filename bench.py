@@ -20,9 +20,13 @@ Printed: one JSON line.  ``value`` is the effective throughput of the step in
 TFLOP/s: the matrix work the tile kernels compute (4*S^2*d per kept
 (query tile, key tile) pair of the attention, plus 2 passes x 2*S^2*d per
 (subset query tile, key tile) pair of the map) divided by the step time.
-``roofline`` is for the attention kernel, the path's matrix-core hot spot;
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload.  With --gpus above 1 the benchmark refuses: this path runs on one
+``roofline`` is for the stage that takes the longest (the dominant kernel);
+``kernels`` gives the same record for every stage: matrix-bound kernels in
+TFLOP/s against the bf16 peak, data-movement kernels in GB/s of algorithmic
+bytes against the HBM peak, with ``traffic`` the HBM bytes per launch read
+from the committed rocprofv3 counter summaries under profiles/ (null when the
+kernel's sources changed since).  ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload.  With --gpus above 1 the benchmark refuses: this path runs on one
 GPU (heads shard across GPUs without any exchange inside the path).
 """
 from __future__ import annotations
@@ -41,28 +45,43 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E peak (published)
-ATTN_SOURCES = ("tile_sparse_attention_head_amd/csrc/sparse_attn.hip",
-                "tile_sparse_attention_head_amd/csrc/attn_common.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_fwd_traffic_wan1.3b-480p-81f.md")
+CSRC = "tile_sparse_attention_head_amd/csrc/"
+# sources whose change invalidates a kernel's committed counter readings
+KERNEL_SOURCES = {
+    "sparse_attn_fwd_kernel": ("sparse_attn.hip", "attn_common.hpp", "veda_internal.hpp"),
+    "oracle_map_kernel": ("oracle_map.hip", "attn_common.hpp", "veda_internal.hpp"),
+    "permute_fwd_kernel": ("permute.hip", "veda_internal.hpp"),
+    "permute_fwd_t_kernel": ("permute.hip", "veda_internal.hpp"),
+    "permute_inv_kernel": ("permute.hip", "veda_internal.hpp"),
+    "tripool_pool_kernel": ("tripool.hip", "veda_internal.hpp"),
+    "select_kernel": ("select.hip", "veda_internal.hpp"),
+}
+PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_hash() -> str:
+def kernel_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in ATTN_SOURCES:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str, sparsity: int):
-    """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 counter summary, or None when it is missing, for another
-    workload, or taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(kernel: str, workload: str, sparsity: int):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
+    summaries (lines starting TRAFFIC_JSON), or None when none matches this
+    workload or the kernel's sources changed since the counters were taken."""
+    if not os.path.isdir(PROFILES):
         return None
-    for line in open(TRAFFIC_FILE):
-        if line.startswith("TRAFFIC_JSON "):
+    want = kernel_hash(kernel)
+    for f in sorted(os.listdir(PROFILES)):
+        if not f.endswith(".md"):
+            continue
+        for line in open(os.path.join(PROFILES, f)):
+            if not line.startswith("TRAFFIC_JSON "):
+                continue
             rec = json.loads(line[len("TRAFFIC_JSON "):])
-            if (rec.get("kernel_hash") == kernel_hash() and rec.get("workload") == workload
+            if (rec.get("kernel") == kernel and rec.get("kernel_hash") == want
+                    and rec.get("workload") == workload
                     and int(rec.get("sparsity_pct", -1)) == sparsity):
                 return rec
     return None
@@ -105,7 +124,8 @@ class Bench:
         self.out = torch.empty_like(self.q)
         self.flops_c, self.pairs = attn_flops(L, self.layer.k_per_head, cfg.tile_size, cfg.head_dim)
         self.flops_d = map_flops(self.n_sub, L, cfg.tile_size, cfg.head_dim)
-        self.stages = ["permute_in", "tripool_score", "select", "sparse_attn", "permute_out", "map"]
+        self.stages = ["permute_q", "permute_k", "permute_vt", "tripool_score", "select",
+                       "sparse_attn", "permute_o", "map"]
         self.ev = None
 
     def _events(self, reps):
@@ -113,22 +133,45 @@ class Bench:
         return [[E(enable_timing=True) for _ in range(len(self.stages) + 1)] for _ in range(reps)]
 
     def step(self, ev=None, with_map=True):
-        ly, sm = self.layer, self.cfg.sm_scale
+        import tile_sparse_attention_head_amd as V
+        ly, sm, L = self.layer, self.cfg.sm_scale, self.L
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
-        ly.permute_inputs(self.q, self.k, self.v)
+        V.veda_tile_permute(L, self.q, ly.q_perm, V.VEDA_FWD)
         rec(1)
-        ly.score(self.w, self.w)
+        V.veda_tile_permute(L, self.k, ly.k_perm, V.VEDA_FWD)
         rec(2)
-        ly.select()
+        V.veda_tile_permute(L, self.v, ly.vt_perm, V.VEDA_FWD_T)
         rec(3)
-        ly.attend(sm, with_lse=True)
+        ly.score(self.w, self.w)
         rec(4)
-        ly.unpermute(self.out)
+        ly.select()
         rec(5)
+        ly.attend(sm, with_lse=True)
+        rec(6)
+        ly.unpermute(self.out)
+        rec(7)
         if with_map:
             ly.maxpool_map(self.q_tiles, sm, self.map_lse, self.map_out)
-        rec(6)
+        rec(8)
+
+    def kernel_work(self):
+        """Algorithmic work of each stage: ("hbm", bytes) or ("mfma", flops)."""
+        L, d, S = self.L, self.cfg.head_dim, self.cfg.tile_size
+        tok = L.tokens * L.num_heads * d * 2            # real rows, bf16
+        til = L.total_tiles * S * d * 2                 # tile order incl. padding
+        nnz = sum(L.n(h) * self.layer.k_per_head[h] for h in range(L.num_heads))
+        return {
+            "permute_q": ("hbm", tok + til, "permute_fwd_kernel"),
+            "permute_k": ("hbm", tok + til, "permute_fwd_kernel"),
+            "permute_vt": ("hbm", tok + til, "permute_fwd_t_kernel"),
+            "tripool_score": ("hbm", 2 * tok + 4 * L.total_scores, "tripool_pool_kernel"),
+            "select": ("hbm", 4 * L.total_scores + 4 * nnz + 4 * (L.total_tiles + 1),
+                       "select_kernel"),
+            "sparse_attn": ("mfma", self.flops_c, "sparse_attn_fwd_kernel"),
+            "permute_o": ("hbm", 2 * tok, "permute_inv_kernel"),
+            "map": ("mfma", self.flops_d, "oracle_map_kernel"),
+        }
 
     def run(self, steps: int, warmup: int, with_map=True):
         torch = self.torch
@@ -218,9 +261,23 @@ def main():
     attn_ms = st["sparse_attn"]
     total_flops = b.flops_c + b.flops_d
     value = total_flops / (wall_ms * 1e-3) / 1e12
-    achieved = b.flops_c / (attn_ms * 1e-3) / 1e12
     cfg, L = b.cfg, b.L
-    traffic = read_traffic(args.workload, args.sparsity)
+
+    kernels = {}
+    for name, (bound, work, kname) in b.kernel_work().items():
+        t = st[name] * 1e-3
+        if bound == "mfma":
+            ach, peak, unit = work / t / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = work / t / 1e9, PEAK_HBM_GBS, "GB/s"
+        tr = read_traffic(kname, args.workload, args.sparsity)
+        kernels[name] = {"kernel": kname, "bound": bound, "achieved": ach, "peak": peak,
+                         "unit": unit, "frac": ach / peak,
+                         "traffic": None if tr is None else tr["bytes_per_launch"],
+                         "algorithmic": work, "avg_launch_ms": st[name]}
+    dominant = max(kernels, key=lambda n: kernels[n]["avg_launch_ms"])
+    roofline = dict(kernels[dominant])
+    roofline["stage"] = dominant
 
     context = {}
     if not args.no_context:
@@ -267,14 +324,8 @@ def main():
         "ms_per_layer": layer_ms,
         "layer_tflops_effective": b.flops_c / (layer_ms * 1e-3) / 1e12,
         "stage_ms": st,
-        "roofline": {"kernel": "veda_sparse_attn_fwd", "bound": "mfma", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                     "algorithmic_flops_per_launch": b.flops_c, "avg_launch_ms": attn_ms},
-        "map_kernel": {"kernel": "veda_oracle_maxpool_map", "avg_launch_ms": st["map"],
-                       "tflops": b.flops_d / (st["map"] * 1e-3) / 1e12,
-                       "frac": b.flops_d / (st["map"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "roofline": roofline,
+        "kernels": kernels,
         "context": context,
         "cpu_baseline": cpu,
     }
