@@ -33,6 +33,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -59,10 +60,18 @@ KERNEL_SOURCES = {
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that a
+    comment edit does not mark counter readings as stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        h.update(open(os.path.join(ROOT, CSRC, f), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, CSRC, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

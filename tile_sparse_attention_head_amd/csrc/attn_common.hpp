@@ -41,6 +41,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const unsigned char gbyte;
 
 struct Chunk { uint32_t x, y, z, w; };
 
@@ -88,21 +89,35 @@ __device__ __forceinline__ bf16x8 lds_chunk(const unsigned char* tile, int r, in
   return *reinterpret_cast<const bf16x8*>(tile + lds_off<CPR>(r, c));
 }
 
-// Issue this wave's share of the global -> LDS copy of one tile (rows of CPR
-// chunks).  SWAP places key rows at LDS row swap23(row) within 32-row blocks.
+// Per-lane byte offsets (within a tile in HBM) of the 16-byte chunks this
+// lane copies into LDS, one per DMA round of the wave.  LDS block q of the
+// tile receives, at lane l, logical chunk (p ^ (r & (CPR-1))) of row r, where
+// lc = 64q + l = r*CPR + p; SWAP places key rows at LDS row swap23(row)
+// within 32-row blocks.
 template <int CPR, int PER_WAVE, bool SWAP>
-__device__ __forceinline__ void dma_tile(const Chunk* __restrict__ g, unsigned char* lds, int wave,
-                                         int lane) {
+__device__ __forceinline__ void dma_offsets(uint32_t (&off)[PER_WAVE], int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
-    const int q = wave * PER_WAVE + i;           // 1 KiB block of the LDS tile
-    const int lc = q * 64 + lane;                // LDS chunk this lane fills
+    const int q = wave * PER_WAVE + i;
+    const int lc = q * 64 + lane;
     const int r = lc / CPR, p = lc % CPR;
     const int c = p ^ (r & (CPR - 1));
     const int gr = SWAP ? ((r & ~31) | swap23(r & 31)) : r;
-    __builtin_amdgcn_global_load_lds((const void*)(g + gr * CPR + c), (lds_void*)(lds + q * 1024),
-                                     16, 0, 0);
+    off[i] = (uint32_t)((gr * CPR + c) * 16);
   }
+}
+
+// Issue this wave's share of the global -> LDS copy of one tile: `g` is the
+// tile's address in HBM and `wave` the wave index, both uniform across the
+// wave (scalar base + 32-bit lane offset; scalar LDS destination).
+template <int PER_WAVE>
+__device__ __forceinline__ void dma_tile(const unsigned char* g, unsigned char* lds,
+                                         const uint32_t (&off)[PER_WAVE], int wave) {
+  gbyte* gg = (gbyte*)g;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i)
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(gg + off[i]),
+                                     (lds_void*)(lds + (wave * PER_WAVE + i) * 1024), 16, 0, 0);
 }
 
 // Wait for this wave's outstanding memory operations (including LDS DMA).
@@ -180,27 +195,38 @@ __device__ __forceinline__ int cut_of(const TileExtent& e) {
 
 // Padding keys -> -inf for key blocks kb0 .. kb0+NKB-1, given the tile's
 // validity words.  Lane half hf holds keys 8hf..8hf+7 and 16+8hf..16+8hf+7 of
-// each block, i.e. bytes hf and 2+hf of the block's word.
+// each block, i.e. bytes hf and 2+hf of the block's word.  Per element: a
+// sign-extended one-bit extract (all ones or all zeros) selects the logit or
+// -inf bitwise.
 template <int NKB, int S>
 __device__ __forceinline__ void mask_keys(f32x16 (&acc)[NKB], const MaskTable<S>& mt, int cut,
                                           int kb0, int hf) {
 #pragma unroll
   for (int b = 0; b < NKB; ++b) {
-    const uint32_t wbits = mt.w[cut][kb0 + b] >> (8 * hf);
+    const int wbits = (int)(mt.w[cut][kb0 + b] >> (8 * hf));
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (!((wbits >> (16 * (i >> 3) + (i & 7))) & 1u)) acc[b][i] = -INFINITY;
+    for (int i = 0; i < 16; ++i) {
+      const int keep = __builtin_amdgcn_sbfe(wbits, 16 * (i >> 3) + (i & 7), 1);
+      acc[b][i] = __int_as_float((__float_as_int(acc[b][i]) & keep) | (0xff800000 & ~keep));
+    }
   }
 }
 
+// Maximum of the wave's logits in this lane, as a tree of 3-input maxima.
 template <int NKB>
 __device__ __forceinline__ float max_of(const f32x16 (&acc)[NKB]) {
-  float m = -INFINITY;
+  float m[NKB];
 #pragma unroll
-  for (int b = 0; b < NKB; ++b)
+  for (int b = 0; b < NKB; ++b) {
+    float x = fmaxf(fmaxf(acc[b][0], acc[b][1]), acc[b][2]);
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) m = fmaxf(m, fmaxf(acc[b][i], acc[b][i + 1]));
-  return m;
+    for (int i = 3; i < 15; i += 2) x = fmaxf(fmaxf(x, acc[b][i]), acc[b][i + 1]);
+    m[b] = fmaxf(x, acc[b][15]);
+  }
+  float r = m[0];
+#pragma unroll
+  for (int b = 1; b < NKB; ++b) r = fmaxf(r, m[b]);
+  return r;
 }
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }

@@ -3,9 +3,9 @@
 // key-tile blocks; Veda §2.3: built in two passes over a random subset of
 // query tiles).
 //
-// One workgroup per subset query tile with the wave layout of the attention
-// kernel (wave (qb, kh): 32 queries in registers, key half kh of every key
-// tile; key tiles copied straight into two LDS stages one tile ahead).  A
+// One workgroup per subset query tile, 2*S/32 waves: wave (qb, kh) holds 32
+// queries in registers and takes key half kh of every key tile; key tiles are
+// copied straight into two LDS stages one tile ahead.  A
 // single loop runs 2*n_h steps over the head's key tiles:
 //   pass 1 (steps 0 .. n_h-1): online row maximum and sum of exp2 over the
 //     wave's keys; the two key halves are combined through LDS -> lse;
@@ -49,8 +49,10 @@ __global__ __launch_bounds__(4 * S, S / 64) void oracle_map_kernel(
   bf16x8 qr[C::KS];
   load_q_regs<D>(qr, q + (g * S + qb * 32 + n) * D, hf);
 
-  const Chunk* kc = reinterpret_cast<const Chunk*>(k) + head_base * (int64_t)C::CHUNKS;
-  dma_tile<C::CPR_K, C::DMA_PER_WAVE, true>(kc, smem[0], wave, lane);
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(k) + head_base * C::TILE_BYTES;
+  uint32_t koff[C::DMA_PER_WAVE];
+  dma_offsets<C::CPR_K, C::DMA_PER_WAVE, true>(koff, wave, lane);
+  dma_tile<C::DMA_PER_WAVE>(kg, smem[0], koff, wave);
   build_mask_table<S>(mtab, L, h, tid);
   wait_all();
   __syncthreads();
@@ -61,8 +63,8 @@ __global__ __launch_bounds__(4 * S, S / 64) void oracle_map_kernel(
   for (int it = 0; it < steps; ++it) {
     const int j = it < n_h ? it : it - n_h;
     if (it + 1 < steps)
-      dma_tile<C::CPR_K, C::DMA_PER_WAVE, true>(kc + (int64_t)((it + 1) % n_h) * C::CHUNKS,
-                                                 smem[stage ^ 1], wave, lane);
+      dma_tile<C::DMA_PER_WAVE>(kg + (int64_t)((it + 1) % n_h) * C::TILE_BYTES, smem[stage ^ 1],
+                                koff, wave);
     if (it == n_h) {
       // end of pass 1: combine with the other key half -> base-2 lse per query
       const int partner = (kh ^ 1) * C::QB + qb;
