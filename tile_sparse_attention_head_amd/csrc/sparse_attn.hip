@@ -3,22 +3,31 @@
 // fetch behind dense matrix math).
 //
 // One workgroup per (head, query tile), S/32 waves: wave w owns queries
-// 32w..32w+31, held in registers as MFMA operands, and every key of each kept
-// tile.  The workgroup walks its CSR row.  A kept key tile K [S][D] and value
-// tile V^T [D][S] are contiguous blocks in HBM that the waves copy straight
-// into LDS (global_load_lds, no register staging).  K and V^T have one LDS
-// buffer each, so two workgroups fit on a CU and the two waves sharing a SIMD
-// come from different, unsynchronised workgroups: one's softmax runs while the
-// other's matrix products do.  Within a workgroup the copy of K(t+1) is issued
-// as soon as every wave has finished S^T = K(t) Q^T, and that of V(t+1) once
-// O^T += V(t)^T P^T is done, so each fetch overlaps half a tile of compute.
+// 32w..32w+31, held in registers as MFMA operands.  The workgroup walks the
+// kept key tiles of its CSR row in steps of 64 keys (half a 128-key tile).
+// Per step s and wave, one straight-line block holds three independent
+// pieces of work, so the matrix cores and the vector ALUs of the wave stay
+// busy together:
+//   softmax(s)   logits S(s) -> probabilities P(s) (vector ALU),
+//   QK(s+1)      S(s+1)^T = K(s+1) Q^T             (MFMA, K from LDS),
+//   PV(s-1)      O^T += V(s-1)^T P(s-1)^T           (MFMA, V^T from LDS).
+// The block is laid out by hand in slots of one MFMA each, with the LDS read
+// of a later slot's operand and a share of the softmax; the compiler may not
+// move work across slots.
 //
-// Per tile and wave: S^T = K Q^T (MFMA 32x32x16 bf16, f32 accumulate), the
-// padding keys of boundary tiles -> -inf, online softmax in base 2 with
-// sm_scale*log2(e) folded into one FMA, P rounded to bf16, O^T += V^T P^T.
-// The running maximum is raised only when a new logit exceeds it by more than
-// 2^8, so the accumulator is rescaled rarely; the result is the same softmax
-// (numerator and denominator share one reference).
+// K and V^T steps are copied HBM -> LDS with buffer_load ... lds (no register
+// staging) into two slots each.  The copies of K(s+2) and V(s) are spread
+// over the slots of step s and land by its end: one barrier per step.  K and
+// V^T slots and the mask table take 74 KiB, so two workgroups share a CU and
+// the two waves on a SIMD come from different, unsynchronised workgroups.
+//
+// Per logit: padding keys of boundary tiles start their accumulation at -inf
+// (the S^T accumulator is seeded from a per-workgroup mask table), online
+// softmax in base 2 with sm_scale*log2(e) folded into one FMA, P rounded to
+// bf16, f32 accumulation.  The running maximum is raised only when a new
+// logit exceeds it by more than 2^8, so the accumulator is rescaled rarely;
+// the result is the same softmax (numerator and denominator share one
+// reference).  The CSR row is read with scalar loads.
 //
 // Workgroups are ordered XCD-aware and head-major, so the query tiles running
 // together on one XCD are spatial neighbours whose kept key tiles overlap in
@@ -32,27 +41,156 @@ namespace {
 
 using namespace attn;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// f(integral_constant<int, I>) for I = B .. E-1, expanded at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 constexpr float kLazyRescale = 8.0f;   // log2 of the largest unnormalised p
 
-// LDS: K and V^T buffers of S*D*2 bytes each (2 x 32 KiB at S = d = 128) plus
-// the mask table.  Per kept tile t:
-//   [K(t) ready]  S^T = K Q^T           barrier -> DMA K(t+1) into the K buffer
-//   softmax; [V(t) ready]  O^T += V^T P^T  barrier -> DMA V(t+1) into the V buffer
+// A step buffer in LDS: R rows of CPR 16-byte chunks, each row followed by
+// one 16-byte pad, so that 16 lanes reading one chunk column of 16
+// consecutive rows hit 16 distinct bank groups (row stride (CPR+1)*16 bytes
+// is an odd number of 16-byte units) and a lane's reads along a row are one
+// base address plus immediate offsets.  It is filled by 1 KiB copy rounds
+// (64 lanes x 16 bytes of consecutive LDS); a lane whose 16 bytes fall on a
+// pad re-reads chunk 0 of the tile.
+template <int R, int CPR, bool SWAP, int GSTRIDE, int NW>
+struct StepBuf {
+  static constexpr int ROWB = (CPR + 1) * 16;
+  static constexpr int ROUNDS = (R * (CPR + 1) + 63) / 64;
+  static constexpr int BYTES = ROUNDS * 1024;
+  static constexpr int PER_WAVE = (ROUNDS + NW - 1) / NW;
+  // round i of wave w fills LDS block w + NW*i; past the last block it fills
+  // block w again with the same bytes, so that every wave issues PER_WAVE
+  // rounds with no branch
+  static __device__ __forceinline__ int block(int wave, int i) {
+    const int q = wave + NW * i;
+    return q < ROUNDS ? q : wave;
+  }
+
+  // per-lane HBM byte offsets of this lane's chunks, one per round of the wave
+  static __device__ __forceinline__ void offsets(uint32_t (&off)[PER_WAVE], int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int u = block(wave, i) * 64 + lane;   // 16-byte unit of the buffer
+      const int r = u / (CPR + 1), c = u % (CPR + 1);
+      const int gr = SWAP ? ((r & ~31) | swap23(r & 31)) : r;
+      off[i] = (c == CPR || r >= R) ? 0u : (uint32_t)(gr * GSTRIDE + c * 16);
+    }
+  }
+  // issue round i of this wave: buffer `rs` at byte offset `so` (uniform)
+  static __device__ __forceinline__ void round(int i, __amdgpu_buffer_rsrc_t rs, uint32_t so,
+                                               unsigned char* lds, const uint32_t (&off)[PER_WAVE],
+                                               int wave) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + block(wave, i) * 1024), 16,
+                                             off[i], so, 0, 0);
+  }
+  static __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, uint32_t so,
+                                              unsigned char* lds, const uint32_t (&off)[PER_WAVE],
+                                              int wave) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) round(i, rs, so, lds, off, wave);
+  }
+  static __device__ __forceinline__ bf16x8 read(const unsigned char* buf, int r, int c) {
+    return *reinterpret_cast<const bf16x8*>(buf + r * ROWB + c * 16);
+  }
+};
+
+template <int D, int S>
+struct Pipe {
+  static constexpr int NW = S / 32;             // waves per workgroup
+  static constexpr int SK = 64;                 // keys per step
+  static constexpr int SPT = S / SK;            // steps per key tile
+  static constexpr int KS = D / 16;             // MFMA k-steps over head_dim
+  static constexpr int DB = D / 32;             // 32-row blocks of O^T
+  static constexpr int TILE = S * D * 2;
+  static constexpr int KSTEP = SK * D * 2;      // HBM bytes of one K step
+  using KBuf = StepBuf<SK, D / 8, true, D * 2, NW>;    // K rows (keys), swap23 order
+  using VBuf = StepBuf<D, SK / 8, false, S * 2, NW>;   // V^T rows (dims), SK keys
+  static_assert(S % SK == 0, "tile must hold whole steps");
+};
+
+__device__ __forceinline__ float swap32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Read-only, wave-uniform data through the constant address space, so that
+// it is fetched with scalar loads (which never wait on the LDS copies).
+typedef __attribute__((address_space(4))) const int32_t cint32;
+
+// Walks the valid entries of a CSR row: one cursor per copy stream.
+struct Cursor {
+  cint32* col;
+  int pos, end, n_h, j;
+  __device__ __forceinline__ void next() {
+    ++pos;
+    while (pos < end) {
+      const int c = col[pos];
+      if (c >= 0 && c < n_h) { j = c; return; }
+      ++pos;
+    }
+    j = 0;
+  }
+};
+
+// Additive key mask of one step, as the initial value of the S^T accumulator:
+// 0 for a real key slot, -inf for padding.  Entry [cut][half][b][hf] is the
+// 16 accumulator elements of 32-key block b of step `half` of a tile with
+// that cut, for lanes of half hf (element i is key 16(i/8) + 8hf + i%8).
+template <int SPT>
+struct BiasTable {
+  f32x4 v[8][SPT][2][2][4];
+};
+
+template <int S, int SPT>
+__device__ __forceinline__ void build_bias_table(BiasTable<SPT>& bt, const DevLayout& L, int h,
+                                                 int tid, int nthreads) {
+  const int pt = L.shape[h][0], ph = L.shape[h][1], pw = L.shape[h][2];
+  const int et = L.T - (L.grid[h][0] - 1) * pt;   // extent of the last tile along t
+  const int eh = L.H - (L.grid[h][1] - 1) * ph;
+  const int ew = L.W - (L.grid[h][2] - 1) * pw;
+  float* flat = reinterpret_cast<float*>(&bt);
+  constexpr int ENTRIES = 8 * SPT * 2 * 2 * 16;
+  for (int x = tid; x < ENTRIES; x += nthreads) {
+    const int i = x & 15, hf = (x >> 4) & 1, b = (x >> 5) & 1, half = (x >> 6) % SPT;
+    const int cut = (x >> 6) / SPT;
+    const int u = half * 64 + 32 * b + 16 * (i >> 3) + 8 * hf + (i & 7);   // slot in tile
+    const int dw = u % pw, r = u / pw, dh = r % ph, dt = r / ph;
+    const bool ok = (!(cut & 4) || dt < et) && (!(cut & 2) || dh < eh) && (!(cut & 1) || dw < ew);
+    flat[x] = ok ? 0.f : -INFINITY;
+  }
+}
+
 template <int D, int S>
 __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ vt, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, float scale_log2, __bf16* __restrict__ o,
     float* __restrict__ lse) {
-  constexpr int NW = S / 32;
-  constexpr int KB = S / 32, KS = D / 16, DB = D / 32, PS = S / 16;
-  constexpr int CPR_K = D / 8, CPR_V = S / 8;
-  constexpr int TILE = S * D * 2, DMA_PW = TILE / 1024 / NW;
-  static_assert(TILE % (1024 * NW) == 0, "tile must split into whole DMA rounds");
-  // separate objects, so that reads of one are not ordered after copies into the other
-  __shared__ __attribute__((aligned(1024))) unsigned char kl[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char vl[TILE];
-  __shared__ MaskTable<S> mtab;
+  using P = Pipe<D, S>;
+  using KB = typename P::KBuf;
+  using VB = typename P::VBuf;
+  constexpr int SPT = P::SPT, KS = P::KS, DB = P::DB, TILE = P::TILE;
+  static_assert(KS == 8 || KS == 4, "head_dim 128 or 64");
+  // four separate objects: reads of one slot are never ordered after copies
+  // into another
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[KB::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[KB::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[VB::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[VB::BYTES];
+  __shared__ BiasTable<SPT> btab;
 
   const int64_t g = xcd_remap(blockIdx.x, gridDim.x);
   const int h = head_of_tile(L, g);
@@ -66,89 +204,254 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   const int64_t qrow = g * S + wave * 32 + n;
   load_q_regs<D>(qr, q + qrow * D, hf);
 
-  int beg = row_ptr[g], end = row_ptr[g + 1];
+  cint32* rp = (cint32*)row_ptr;
+  cint32* ci = (cint32*)col_idx;
+  int beg = rp[g], end = rp[g + 1];
   if (end < beg) end = beg;
-  auto next_valid = [&](int p) {
-    while (p < end) {
-      const int j = col_idx[p];
-      if (j >= 0 && j < n_h) break;
-      ++p;
-    }
-    return p;
+  int kept = 0;
+  for (int p = beg; p < end; ++p) {
+    const int c = ci[p];
+    kept += (c >= 0 && c < n_h) ? 1 : 0;
+  }
+  const int N = kept * SPT;   // steps
+
+  // the head's K and V^T tiles as buffer resources (raw, bounds = the head)
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const unsigned char*>(k) + head_base * TILE), (short)0,
+      n_h * TILE, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const unsigned char*>(vt) + head_base * TILE), (short)0,
+      n_h * TILE, 0x00020000);
+  uint32_t koff[KB::PER_WAVE], voff[VB::PER_WAVE];
+  KB::offsets(koff, wave, lane);
+  VB::offsets(voff, wave, lane);
+
+  // Three walks over the row's kept tiles, one step (SK keys) at a time:
+  // copies of K run two steps ahead of the logits, copies of V^T with them.
+  Cursor kc{ci, beg - 1, end, n_h, 0}, vc = kc, qc = kc;
+  uint32_t kg_last = 0;
+  int kstep = 0, vstep = 0, qstep = 0, qcut = 0;
+  // HBM address of the next K step / V^T step to copy (cursors advance)
+  auto next_k = [&]() {
+    if (kstep % SPT == 0) kc.next();
+    const uint32_t r = (uint32_t)(kc.j * TILE + (kstep % SPT) * P::KSTEP);
+    ++kstep;
+    return r;
   };
-  const unsigned char* kg = reinterpret_cast<const unsigned char*>(k) + head_base * TILE;
-  const unsigned char* vg = reinterpret_cast<const unsigned char*>(vt) + head_base * TILE;
-  uint32_t koff[DMA_PW], voff[DMA_PW];
-  dma_offsets<CPR_K, DMA_PW, true>(koff, wave, lane);
-  dma_offsets<CPR_V, DMA_PW, false>(voff, wave, lane);
+  auto next_v = [&]() {
+    if (vstep % SPT == 0) vc.next();
+    const uint32_t r = (uint32_t)(vc.j * TILE + (vstep % SPT) * (P::SK * 2));
+    ++vstep;
+    return r;
+  };
+  // mask row of the next step whose logits are computed
+  auto next_bias = [&]() -> const f32x4* {
+    if (qstep % SPT == 0) {
+      qc.next();
+      qcut = cut_of(tile_extent(L, h, qc.j));
+    }
+    const f32x4* r = &btab.v[qcut][qstep % SPT][0][hf][0];
+    ++qstep;
+    return r;
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  f32x16 sA[2], sB[2];
+  bf16x8 pA[4], pB[4];
 
-  int p = next_valid(beg);
-  int cur_j = p < end ? col_idx[p] : 0;
-  if (p < end) {
-    dma_tile<DMA_PW>(kg + (int64_t)cur_j * TILE, kl, koff, wave);
-    dma_tile<DMA_PW>(vg + (int64_t)cur_j * TILE, vl, voff, wave);
-  }
-  build_mask_table<S>(mtab, L, h, tid);
-  wait_all();
-  __syncthreads();
+  auto load_bias = [&](f32x16 (&acc)[2], const f32x4* bp) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 x = bp[b * 8 + c];   // [b][hf][c] with hf fixed: stride 2*4 per b
+        acc[b][4 * c + 0] = x[0];
+        acc[b][4 * c + 1] = x[1];
+        acc[b][4 * c + 2] = x[2];
+        acc[b][4 * c + 3] = x[3];
+      }
+  };
 
-  static_assert(DMA_PW == 8 || DMA_PW == 4, "barrier wait counts below assume 8 or 4 copies");
-  while (p < end) {
-    const int pn = next_valid(p + 1);
-    const int nxt_j = pn < end ? col_idx[pn] : 0;
-    f32x16 sacc[KB];
-    qk_blocks<D, KB>(sacc, kl, 0, qr, n, hf);
-    wait_all();                                        // own share of V(t) landed
-    __syncthreads();                                   // K buffer free, V(t) visible
-    if (pn < end) dma_tile<DMA_PW>(kg + (int64_t)nxt_j * TILE, kl, koff, wave);
+  // One step s.  PAR = s & 1 picks slots and register sets at compile time.
+  // The matrix products, their LDS operand reads and the softmax are laid out
+  // by hand in 32 slots of one MFMA each (even: QK(s+1), odd: PV(s-1)); the
+  // compiler may not move work across slots.
+  auto step = [&](auto has_qk, auto has_pv, auto par, int s) {
+    constexpr bool QK = decltype(has_qk)::value, PV = decltype(has_pv)::value;
+    constexpr int PAR = decltype(par)::value;
+    f32x16 (&scur)[2] = PAR ? sB : sA;
+    f32x16 (&snext)[2] = PAR ? sA : sB;
+    bf16x8 (&pcur)[4] = PAR ? pB : pA;
+    const bf16x8 (&pprev)[4] = PAR ? pA : pB;
+    const unsigned char* ksrc = PAR ? k0 : k1;
+    const unsigned char* vsrc = PAR ? v0 : v1;
 
-    const int cut = cut_of(tile_extent(L, h, cur_j));
-    if (cut != 0) mask_keys<KB, S>(sacc, mtab, cut, 0, hf);
-    float mx = max_of<KB>(sacc);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_cand = fmaxf(m_run, mx * scale_log2);
-    if (__any(m_cand > m_run + kLazyRescale)) {
-      const float alpha = m_cand == -INFINITY ? 1.f : exp2_(m_run - m_cand);
-      m_run = m_cand;
+    // mask rows first: no copy of this step is in flight yet
+    if constexpr (QK) load_bias(snext, next_bias());
+    // K(s+2) over K(s) and V(s) over V(s-2), issued spread over the slots
+    // below; with no step s+2 the K rounds re-copy the last K step into the
+    // free slot
+    const uint32_t kgs = s + 2 < N ? next_k() : kg_last;
+    kg_last = kgs;
+    const uint32_t vgs = next_v();
+    unsigned char* kdst = PAR ? k1 : k0;
+    unsigned char* vdst = PAR ? v1 : v0;
+    constexpr int RW = KB::PER_WAVE + VB::PER_WAVE;
+    // the addresses come from scalar loads: have them land before the slots,
+    // whose LDS waits then count the operand reads alone
+    asm volatile("" :: "s"(kgs), "s"(vgs));
+
+    constexpr int LA = 3;          // operand reads run LA slots ahead of their MFMA
+    constexpr int NSLOT = D / 4;   // D/8 QK and D/8 PV products
+    auto has_mfma = [](int i) constexpr { return (i & 1) ? PV : QK; };
+    auto operand = [&](int i) -> bf16x8 {
+      const int j = i >> 1;
+      if (i & 1) return VB::read(vsrc, (j % DB) * 32 + n, 2 * (j / DB) + hf);
+      return KB::read(ksrc, (j & 1) * 32 + n, 2 * (j >> 1) + hf);
+    };
+    bf16x8 opnd[LA + 1];
+    static_for<0, LA>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (has_mfma(i)) opnd[i % (LA + 1)] = operand(i);
+    });
+
+    float pm[4], e[32];
+    float mxs = 0.f, m_new = 0.f, neg_m = 0.f, psum0 = 0.f, psum1 = 0.f;
+    bool raise = false;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NSLOT>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      static_for<0, RW>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr ((m * (NSLOT - 4)) / RW == i) {
+          if constexpr (m < KB::PER_WAVE) KB::round(m, krs, kgs, kdst, koff, wave);
+          else VB::round(m - KB::PER_WAVE, vrs, vgs, vdst, voff, wave);
+        }
+      });
+      if constexpr (i + LA < NSLOT && has_mfma(i + LA))
+        opnd[(i + LA) % (LA + 1)] = operand(i + LA);
+      if constexpr (has_mfma(i)) {
+        constexpr int j = i >> 1;
+        if constexpr (i & 1) oacc[j % DB] = mfma32(opnd[i % (LA + 1)], pprev[j / DB], oacc[j % DB]);
+        else snext[j & 1] = mfma32(opnd[i % (LA + 1)], qr[j >> 1], snext[j & 1]);
+      }
+      // softmax(s): row maximum in slots 0..4, then the elements
+      if constexpr (i < 4) {
+        constexpr int b = i >> 1, o8 = (i & 1) * 8;
+        float x = fmaxf(fmaxf(scur[b][o8], scur[b][o8 + 1]), scur[b][o8 + 2]);
+        x = fmaxf(fmaxf(x, scur[b][o8 + 3]), scur[b][o8 + 4]);
+        x = fmaxf(fmaxf(x, scur[b][o8 + 5]), scur[b][o8 + 6]);
+        pm[i] = fmaxf(x, scur[b][o8 + 7]);
+        asm volatile("" : "+v"(pm[i]));
+      }
+      if constexpr (i == 3) {
+        mxs = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+        mxs = swap32_max(mxs);
+        asm volatile("" : "+v"(mxs));
+      }
+      if constexpr (i == 4) {
+        const float m_cand = fmaxf(m_run, mxs * scale_log2);
+        raise = m_cand > m_run + kLazyRescale;
+        m_new = raise ? m_cand : m_run;
+        neg_m = m_new == -INFINITY ? 0.f : -m_new;
+        asm volatile("" : "+v"(neg_m));
+      }
+      // element pairs get their FMAs in slot fs(k), exps in fs(k)+1, sums and
+      // bf16 conversion in fs(k)+2; an empty asm statement pins each value to
+      // its slot
+      static_for<0, 16>([&](auto kc_) {
+        constexpr int kp = decltype(kc_)::value;
+        constexpr int f = 5 + (kp * (NSLOT - 7)) / 16;
+        constexpr int el0 = 2 * kp, b = el0 >> 4, ii = el0 & 15;
+        if constexpr (f == i) {
+          e[el0] = fmaf(scur[b][ii], scale_log2, neg_m);
+          e[el0 + 1] = fmaf(scur[b][ii + 1], scale_log2, neg_m);
+          asm volatile("" : "+v"(e[el0]), "+v"(e[el0 + 1]));
+        }
+        if constexpr (f + 1 == i) {
+          e[el0] = exp2_(e[el0]);
+          e[el0 + 1] = exp2_(e[el0 + 1]);
+          asm volatile("" : "+v"(e[el0]), "+v"(e[el0 + 1]));
+        }
+        if constexpr (f + 2 == i) {
+          psum0 += e[el0];
+          psum1 += e[el0 + 1];
+          pcur[2 * b + (ii >> 3)][ii & 7] = (__bf16)e[el0];
+          pcur[2 * b + (ii >> 3)][(ii & 7) + 1] = (__bf16)e[el0 + 1];
+          asm volatile("" : "+v"(psum0), "+v"(psum1));
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+
+    // O and l to the new reference (rare), after PV(s-1), before PV(s)
+    if (__builtin_expect(__any(raise), 0)) {
+      const float alpha = raise ? exp2_(m_run - m_new) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
-    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-    bf16x8 pb[PS];
-    float psum = 0.f;
+    m_run = m_new;
+    l_run += psum0 + psum1;
+    // own copies landed, and every wave is past its reads of the slots the
+    // next step overwrites
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+  using Z = std::integral_constant<int, 0>;
+  using O1 = std::integral_constant<int, 1>;
+  if (N > 0) {
+    kg_last = next_k();
+    KB::copy(krs, kg_last, k0, koff, wave);
+    if (N > 1) {
+      kg_last = next_k();
+      KB::copy(krs, kg_last, k1, koff, wave);
+    }
+    build_bias_table<S, SPT>(btab, L, h, tid, 2 * S);
+    wait_all();
+    __syncthreads();
+    // logits of step 0
+    load_bias(sA, next_bias());
 #pragma unroll
-    for (int b = 0; b < KB; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = exp2_(fmaf(sacc[b][i], scale_log2, neg_m));
-        psum += pv;
-        pb[2 * b + (i >> 3)][i & 7] = (__bf16)pv;
+    for (int s = 0; s < KS; ++s) {
+      sA[0] = mfma32(KB::read(k0, n, 2 * s + hf), qr[s], sA[0]);
+      sA[1] = mfma32(KB::read(k0, 32 + n, 2 * s + hf), qr[s], sA[1]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // k0 free
+    if (N == 1) {
+      step(F{}, F{}, Z{}, 0);
+    } else {
+      step(T{}, F{}, Z{}, 0);
+      int s = 1;
+      for (; s + 1 <= N - 2; s += 2) {
+        step(T{}, T{}, O1{}, s);
+        step(T{}, T{}, Z{}, s + 1);
       }
-    l_run += psum;
+      if (s <= N - 2) {
+        step(T{}, T{}, O1{}, s);
+        ++s;
+      }
+      if (s & 1) step(F{}, T{}, O1{}, s);
+      else step(F{}, T{}, Z{}, s);
+    }
+    // PV of the last step
+    auto pv_last = [&](const bf16x8 (&pb)[4], const unsigned char* vb) {
 #pragma unroll
-    for (int t = 0; t < PS; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        oacc[db] = mfma32(lds_chunk<CPR_V>(vl, db * 32 + n, 2 * t + hf), pb[t], oacc[db]);
-    // V buffer free: this wave's LDS reads are done (the K(t+1) copy may still fly)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (pn < end) dma_tile<DMA_PW>(vg + (int64_t)nxt_j * TILE, vl, voff, wave);
-    // own share of K(t+1) landed (V(t+1) may still be in flight), then barrier
-    if constexpr (DMA_PW == 8)
-      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    p = pn;
-    cur_j = nxt_j;
+        for (int db = 0; db < DB; ++db)
+          oacc[db] = mfma32(VB::read(vb, db * 32 + n, 2 * t + hf), pb[t], oacc[db]);
+    };
+    if ((N - 1) & 1) pv_last(pB, v1);
+    else pv_last(pA, v0);
   }
 
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = swap32_sum(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   __bf16* orow = o + qrow * D;
 #pragma unroll
