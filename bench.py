@@ -18,8 +18,9 @@ map), the map's latency and the attention kernel's average launch duration.
 
 Printed: one JSON line.  ``value`` is the effective throughput of the step in
 TFLOP/s: the matrix work the tile kernels compute (4*S^2*d per kept
-(query tile, key tile) pair of the attention, plus 2 passes x 2*S^2*d per
-(subset query tile, key tile) pair of the map) divided by the step time.
+(query tile, key tile) pair of the attention, plus 2*S^2*d per (subset query
+tile, key tile) pair of the map -- its one Q K^T product; the second pass
+reads the row maxima the first one stored) divided by the step time.
 ``roofline`` is for the stage that takes the longest (the dominant kernel);
 ``kernels`` gives the same record for every stage: matrix-bound kernels in
 TFLOP/s against the bf16 peak, data-movement kernels in GB/s of algorithmic
@@ -50,7 +51,8 @@ CSRC = "tile_sparse_attention_head_amd/csrc/"
 # sources whose change invalidates a kernel's committed counter readings
 KERNEL_SOURCES = {
     "sparse_attn_fwd_kernel": ("sparse_attn.hip", "attn_common.hpp", "veda_internal.hpp"),
-    "oracle_map_kernel": ("oracle_map.hip", "attn_common.hpp", "veda_internal.hpp"),
+    "map_stats_kernel": ("oracle_map.hip", "attn_common.hpp", "veda_internal.hpp"),
+    "map_reduce_kernel": ("oracle_map.hip", "attn_common.hpp", "veda_internal.hpp"),
     "permute_fwd_kernel": ("permute.hip", "veda_internal.hpp"),
     "permute_fwd_t_kernel": ("permute.hip", "veda_internal.hpp"),
     "permute_inv_kernel": ("permute.hip", "veda_internal.hpp"),
@@ -102,7 +104,8 @@ def attn_flops(L, k_per_head, S, d):
 
 
 def map_flops(n_sub_per_head, L, S, d):
-    return sum(2 * 2.0 * S * S * d * n_sub_per_head[h] * L.n(h) for h in range(L.num_heads))
+    """One Q K^T product (2*S^2*d) per (subset query tile, key tile) pair."""
+    return sum(2.0 * S * S * d * n_sub_per_head[h] * L.n(h) for h in range(L.num_heads))
 
 
 class Bench:
@@ -179,7 +182,7 @@ class Bench:
                        "select_kernel"),
             "sparse_attn": ("mfma", self.flops_c, "sparse_attn_fwd_kernel"),
             "permute_o": ("hbm", 2 * tok, "permute_inv_kernel"),
-            "map": ("mfma", self.flops_d, "oracle_map_kernel"),
+            "map": ("mfma", self.flops_d, "map_stats_kernel"),
         }
 
     def run(self, steps: int, warmup: int, with_map=True):

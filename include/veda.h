@@ -159,6 +159,7 @@ int veda_select_tiles(const veda_layout* L, const float* scores,
  *  o_perm          bf16, tile order (output); padding query rows unspecified
  *  lse             f32 [tile_off[num_heads]*S] natural-log log-sum-exp per
  *                  query slot, or NULL (output)
+ *  sm_scale        finite and > 0 (else VEDA_ERR_INVALID_ARG)
  * A query row whose CSR row is empty gets O = 0 and lse = -inf.  Entries of
  * col_idx outside [0, n_tiles[hd]) are skipped.  Supported: (head_dim,
  * tile_size) in {(64,64), (128,128)}, 16-byte aligned tensors. */
@@ -177,14 +178,30 @@ int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k
  *               exp(sm_scale q_r.k_c - lse_r)
  * and map[s][j] = 0 for n_tiles[hd] <= j < max_tiles.
  *  q_perm, k_perm  bf16, tile order
+ *  sm_scale        finite and > 0 (else VEDA_ERR_INVALID_ARG)
  *  q_tiles         int32 [n_sub] global query-tile indices; an entry outside
  *                  [0, tile_off[num_heads]) gets a map row of zeros
+ *  workspace       device scratch of at least workspace_bytes >=
+ *                  veda_oracle_maxpool_map_workspace(L, n_sub) bytes, 16-byte
+ *                  aligned (smaller: VEDA_ERR_INVALID_ARG); owned by the
+ *                  caller, contents on entry and exit unspecified, must not
+ *                  overlap any other argument; calls sharing a workspace
+ *                  must be ordered on one stream
  *  lse             f32 [n_sub*S] (output); padding query rows unspecified
  *  map             f32 [n_sub][max_tiles] (output)
+ * Pass 1 also records, per query row and key tile, the largest logit, so
+ * pass 2 reads n_sub*max_tiles*S floats instead of recomputing Q K^T.
  * Supported: (head_dim, tile_size) in {(64,64), (128,128)}. */
 int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void* k_perm,
                             float sm_scale, const int32_t* q_tiles, int32_t n_sub,
-                            float* lse, float* map, void* stream);
+                            void* workspace, int64_t workspace_bytes, float* lse,
+                            float* map, void* stream);
+
+/* Workspace bytes veda_oracle_maxpool_map needs for n_sub subset entries of
+ * layout L (0 for n_sub = 0): n_sub*max_tiles*S*4 for the row maxima plus
+ * n_sub*chunks*S*8 for per-chunk partial sums.  Host-only, no device work.
+ *  bytes  (host) output */
+int veda_oracle_maxpool_map_workspace(const veda_layout* L, int32_t n_sub, int64_t* bytes);
 
 /* Static text for a veda_status value. */
 const char* veda_status_string(int status);

@@ -131,15 +131,44 @@ def test_device_calls_reject_before_launch(lib):
     assert lib.veda_select_tiles(Lp, fake, kh, fake, fake, None) == -1
     kh = (ctypes.c_int32 * 2)(3, L.n(1) + 1)
     assert lib.veda_select_tiles(Lp, fake, kh, fake, fake, None) == -1
-    # attention: nulls, NaN scale, unsupported shape
+    # attention: nulls, NaN / zero / negative scale (the kernels scale the row
+    # maximum of the raw logits, which is the maximum of the scaled logits only
+    # for a positive scale), unsupported shape
     assert lib.veda_sparse_attn_fwd(Lp, fake, fake, None, fake, fake, 0.1, fake, None, None) == -1
-    assert lib.veda_sparse_attn_fwd(Lp, fake, fake, fake, fake, fake, float("nan"), fake, None, None) == -1
+    for bad in (float("nan"), 0.0, -0.1, float("inf")):
+        assert lib.veda_sparse_attn_fwd(Lp, fake, fake, fake, fake, fake, bad, fake, None, None) == -1
     L3 = V.veda_layout_init(5, 9, 20, 96, 128, [(8, 4, 4)])
     assert lib.veda_sparse_attn_fwd(ctypes.byref(L3), fake, fake, fake, fake, fake, 0.1, fake, None, None) == -2
-    # map: negative count, nulls
-    assert lib.veda_oracle_maxpool_map(Lp, fake, fake, 0.1, fake, -1, fake, fake, None) == -1
-    assert lib.veda_oracle_maxpool_map(Lp, None, fake, 0.1, fake, 3, fake, fake, None) == -1
-    assert lib.veda_oracle_maxpool_map(Lp, fake, fake, float("inf"), fake, 3, fake, fake, None) == -1
+    # map: negative count, nulls, bad scale, missing / short / misaligned workspace
+    ws = ctypes.c_int64(0)
+    assert lib.veda_oracle_maxpool_map_workspace(Lp, 3, ctypes.byref(ws)) == 0
+    big = 1 << 40
+    M = lib.veda_oracle_maxpool_map
+    assert M(Lp, fake, fake, 0.1, fake, -1, fake, big, fake, fake, None) == -1
+    assert M(Lp, None, fake, 0.1, fake, 3, fake, big, fake, fake, None) == -1
+    for bad in (float("inf"), float("nan"), 0.0, -1.0):
+        assert M(Lp, fake, fake, bad, fake, 3, fake, big, fake, fake, None) == -1
+    assert M(Lp, fake, fake, 0.1, fake, 3, None, big, fake, fake, None) == -1
+    assert M(Lp, fake, fake, 0.1, fake, 3, fake, ws.value - 1, fake, fake, None) == -1
+    assert M(Lp, fake, fake, 0.1, fake, 3, fake + 8, big, fake, fake, None) == -2
+
+
+def test_map_workspace_size(lib):
+    # row maxima (n_sub x max_tiles x S f32, rounded up to 256 bytes) followed by
+    # the per-chunk (m, l) pairs (n_sub x chunks x S x 2 f32)
+    L = _layout()
+    out = ctypes.c_int64(-5)
+    assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(L), 0, ctypes.byref(out)) == 0
+    assert out.value == 0
+    for n_sub in (1, 3, 400):
+        assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(L), n_sub, ctypes.byref(out)) == 0
+        rm = -(-n_sub * L.max_tiles * L.tile_size * 4 // 256) * 256
+        rest = out.value - rm
+        assert rest > 0 and rest % (n_sub * L.tile_size * 8) == 0
+        chunks = rest // (n_sub * L.tile_size * 8)
+        assert 1 <= chunks <= min(16, L.max_tiles)
+    assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(L), -1, ctypes.byref(out)) == -1
+    assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(L), 3, None) == -1
 
 
 def test_status_strings(lib):

@@ -88,8 +88,9 @@ def lib() -> ctypes.CDLL:
         "veda_select_tiles": (c_i32, [P, c_vp, ctypes.POINTER(c_i32), c_vp, c_vp, c_vp]),
         "veda_sparse_attn_fwd": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_vp, c_vp,
                                          c_vp]),
-        "veda_oracle_maxpool_map": (c_i32, [P, c_vp, c_vp, c_f32, c_vp, c_i32, c_vp, c_vp,
-                                            c_vp]),
+        "veda_oracle_maxpool_map": (c_i32, [P, c_vp, c_vp, c_f32, c_vp, c_i32, c_vp, c_i64,
+                                            c_vp, c_vp, c_vp]),
+        "veda_oracle_maxpool_map_workspace": (c_i32, [P, c_i32, ctypes.POINTER(c_i64)]),
         "veda_status_string": (ctypes.c_char_p, [c_i32]),
         "veda_layout_sizeof": (c_i64, []),
     }
@@ -248,16 +249,31 @@ def veda_sparse_attn_fwd(L: veda_layout, q_perm, k_perm, vt_perm, row_ptr, col_i
            "veda_sparse_attn_fwd")
 
 
-def veda_oracle_maxpool_map(L: veda_layout, q_perm, k_perm, sm_scale: float, q_tiles, lse, out_map,
-                            stream=None) -> None:
+def veda_oracle_maxpool_map_workspace(L: veda_layout, n_sub: int) -> int:
+    """Bytes of device workspace veda_oracle_maxpool_map needs for n_sub entries."""
+    out = c_i64(0)
+    _check(lib().veda_oracle_maxpool_map_workspace(ctypes.byref(L), int(n_sub), ctypes.byref(out)),
+           "veda_oracle_maxpool_map_workspace")
+    return int(out.value)
+
+
+def veda_oracle_maxpool_map(L: veda_layout, q_perm, k_perm, sm_scale: float, q_tiles, workspace,
+                            lse, out_map, stream=None) -> None:
+    """workspace: a contiguous GPU tensor of at least
+    veda_oracle_maxpool_map_workspace(L, n_sub) bytes (any dtype)."""
     torch = _torch()
     bf = torch.bfloat16
     n_sub = int(q_tiles.numel())
     n = tiles_numel(L)
     args = [_dev(q_perm, "q_perm", bf, n), _dev(k_perm, "k_perm", bf, n)]
     pq = _dev(q_tiles, "q_tiles", torch.int32, n_sub)
+    need = veda_oracle_maxpool_map_workspace(L, n_sub)
+    pw = _dev(workspace, "workspace", None, 0)
+    have = workspace.numel() * workspace.element_size()
+    if have < need:
+        raise ValueError(f"workspace holds {have} bytes, needs {need}")
     pl = _dev(lse, "lse", torch.float32, n_sub * L.tile_size)
     pm = _dev(out_map, "map", torch.float32, n_sub * L.max_tiles)
     _check(lib().veda_oracle_maxpool_map(ctypes.byref(L), args[0], args[1], float(sm_scale), pq,
-                                         n_sub, pl, pm, _stream(stream)),
+                                         n_sub, pw, have, pl, pm, _stream(stream)),
            "veda_oracle_maxpool_map")

@@ -200,8 +200,7 @@ int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k
   if (q_perm == nullptr || k_perm == nullptr || vt_perm == nullptr || row_ptr == nullptr ||
       col_idx == nullptr || o_perm == nullptr)
     return VEDA_ERR_INVALID_ARG;
-  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
-    return VEDA_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.f) || sm_scale == INFINITY) return VEDA_ERR_INVALID_ARG;
   if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
   if (!aligned16(q_perm) || !aligned16(k_perm) || !aligned16(vt_perm) || !aligned16(o_perm))
     return VEDA_ERR_UNSUPPORTED;
@@ -229,21 +228,29 @@ int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k
                 stream);
 }
 
+int veda_oracle_maxpool_map_workspace(const veda_layout* L, int32_t n_sub, int64_t* bytes) {
+  if (L == nullptr || bytes == nullptr || !layout_ok(L) || n_sub < 0) return VEDA_ERR_INVALID_ARG;
+  *bytes = map_workspace_bytes(make_dev_layout(L), n_sub);
+  return VEDA_OK;
+}
+
 int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void* k_perm,
-                            float sm_scale, const int32_t* q_tiles, int32_t n_sub, float* lse,
-                            float* map, void* stream) {
+                            float sm_scale, const int32_t* q_tiles, int32_t n_sub,
+                            void* workspace, int64_t workspace_bytes, float* lse, float* map,
+                            void* stream) {
   if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
   if (n_sub < 0) return VEDA_ERR_INVALID_ARG;
   if (n_sub > 0 && (q_perm == nullptr || k_perm == nullptr || q_tiles == nullptr ||
-                    lse == nullptr || map == nullptr))
+                    lse == nullptr || map == nullptr || workspace == nullptr))
     return VEDA_ERR_INVALID_ARG;
-  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
-    return VEDA_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.f) || sm_scale == INFINITY) return VEDA_ERR_INVALID_ARG;
   if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
-  if (n_sub > 0 && (!aligned16(q_perm) || !aligned16(k_perm))) return VEDA_ERR_UNSUPPORTED;
   const DevLayout dl = make_dev_layout(L);
-  return finish(launch_oracle_map(dl, q_perm, k_perm, sm_scale, q_tiles, n_sub, lse, map,
-                                  (hipStream_t)stream),
+  if (n_sub > 0 && workspace_bytes < map_workspace_bytes(dl, n_sub)) return VEDA_ERR_INVALID_ARG;
+  if (n_sub > 0 && (!aligned16(q_perm) || !aligned16(k_perm) || !aligned16(workspace)))
+    return VEDA_ERR_UNSUPPORTED;
+  return finish(launch_oracle_map(dl, q_perm, k_perm, sm_scale, q_tiles, n_sub, workspace, lse,
+                                  map, (hipStream_t)stream),
                 stream);
 }
 

@@ -6,10 +6,10 @@
 // wave's 32 queries (held in registers for the whole kernel) the B operand.
 // In the 32x32 accumulator layout lane l holds column l % 32 -- one query --
 // and 16 rows, so every softmax row statistic is a reduction inside the lane
-// plus one exchange with lane l ^ 32.  The output is accumulated transposed
-// too, O^T = V^T P^T: V^T rows (from LDS) are the A operand and P^T, the
-// probabilities already sitting in the lane that owns the query, the B
-// operand, with no data movement.
+// plus one exchange with lane l ^ 32.  The attention output is accumulated
+// transposed too, O^T = V^T P^T: V^T rows (from LDS) are the A operand and
+// P^T, the probabilities already sitting in the lane that owns the query, the
+// B operand, with no data movement.
 //
 // Key order inside a 32-key block.  Accumulator element i of lane l is row
 // m = 8(i/4) + 4(l/32) + i%4.  Key rows are placed in LDS with bits 2 and 3
@@ -19,18 +19,17 @@
 // supplies to the P V product.  Both operands of each product take their
 // contraction indices by the same rule, so the products are exact.
 //
-// Waves.  A workgroup owns one query tile of S queries with 2*S/32 waves:
-// wave w takes query block w % (S/32) and key half w / (S/32) of every key
-// tile, so two waves share each SIMD and one's softmax can run while the
-// other's matrix products do.  The two halves are merged at the end.
+// LDS staging.  Tiles are copied HBM -> LDS with buffer_load ... lds (no
+// register staging): one instruction moves 64 lanes x 16 bytes into 1 KiB of
+// consecutive LDS, and each lane picks the HBM chunk that must land at its
+// LDS position.  Rows are padded by 16 bytes (see StepBuf).
 //
-// LDS staging.  Tiles are copied global -> LDS with global_load_lds_dwordx4
-// (no register staging): one instruction moves 64 lanes x 16 bytes into 1 KiB
-// of consecutive LDS, and each lane picks the global 16-byte chunk that must
-// land at its LDS position.  Rows are stored unpadded with their 16-byte
-// chunks XOR-swizzled by the row index, so the lanes that read one chunk
-// column of consecutive rows hit distinct banks.
+// Padding key slots of boundary tiles are masked by seeding the S^T
+// accumulator with 0 or -inf per key slot (see BiasTable), so masking costs
+// no vector instruction.
 #pragma once
+
+#include <type_traits>
 
 #include "veda_internal.hpp"
 
@@ -40,10 +39,11 @@ namespace attn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const unsigned char gbyte;
-
-struct Chunk { uint32_t x, y, z, w; };
+// Read-only, wave-uniform data through the constant address space, so that
+// it is fetched with scalar loads (which never wait on the LDS copies).
+typedef __attribute__((address_space(4))) const int32_t cint32;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -53,74 +53,16 @@ __device__ __forceinline__ int swap23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-// Key index (within its 32-key block) of accumulator element i, lane half hf.
-__device__ __forceinline__ int key_in_block(int i, int hf) {
-  return 16 * (i >> 3) + 8 * hf + (i & 7);
-}
-
-template <int D, int S>
-struct Cfg {
-  static constexpr int QB = S / 32;            // 32-query blocks per tile
-  static constexpr int KH = 2;                 // key halves (waves per query block)
-  static constexpr int NW = QB * KH;           // waves per workgroup
-  static constexpr int NT = NW * 64;           // threads per workgroup
-  static constexpr int KPW = S / KH;           // keys per wave per tile
-  static constexpr int KBW = KPW / 32;         // 32-key blocks per wave
-  static constexpr int KS = D / 16;            // MFMA k-steps over head_dim
-  static constexpr int DB = D / 32;            // 32-row blocks of O^T
-  static constexpr int PSW = KPW / 16;         // MFMA k-steps over a wave's keys
-  static constexpr int CPR_K = D / 8;          // 16-byte chunks per key row
-  static constexpr int CPR_V = S / 8;          // 16-byte chunks per V^T row
-  static constexpr int TILE_BYTES = S * D * 2; // one bf16 tile
-  static constexpr int CHUNKS = TILE_BYTES / 16;
-  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / NW;
-  static_assert(TILE_BYTES % (1024 * NW) == 0, "tile must split into whole DMA rounds");
-  static_assert(KBW >= 1, "a wave needs at least one key block");
-};
-
-// Byte offset of logical 16-byte chunk c of row r in a swizzled LDS tile.
-template <int CPR>
-__device__ __forceinline__ int lds_off(int r, int c) {
-  return (r * CPR + (c ^ (r & (CPR - 1)))) * 16;
-}
-
-template <int CPR>
-__device__ __forceinline__ bf16x8 lds_chunk(const unsigned char* tile, int r, int c) {
-  return *reinterpret_cast<const bf16x8*>(tile + lds_off<CPR>(r, c));
-}
-
-// Per-lane byte offsets (within a tile in HBM) of the 16-byte chunks this
-// lane copies into LDS, one per DMA round of the wave.  LDS block q of the
-// tile receives, at lane l, logical chunk (p ^ (r & (CPR-1))) of row r, where
-// lc = 64q + l = r*CPR + p; SWAP places key rows at LDS row swap23(row)
-// within 32-row blocks.
-template <int CPR, int PER_WAVE, bool SWAP>
-__device__ __forceinline__ void dma_offsets(uint32_t (&off)[PER_WAVE], int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int q = wave * PER_WAVE + i;
-    const int lc = q * 64 + lane;
-    const int r = lc / CPR, p = lc % CPR;
-    const int c = p ^ (r & (CPR - 1));
-    const int gr = SWAP ? ((r & ~31) | swap23(r & 31)) : r;
-    off[i] = (uint32_t)((gr * CPR + c) * 16);
+// f(integral_constant<int, I>) for I = B .. E-1, expanded at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
-// Issue this wave's share of the global -> LDS copy of one tile: `g` is the
-// tile's address in HBM and `wave` the wave index, both uniform across the
-// wave (scalar base + 32-bit lane offset; scalar LDS destination).
-template <int PER_WAVE>
-__device__ __forceinline__ void dma_tile(const unsigned char* g, unsigned char* lds,
-                                         const uint32_t (&off)[PER_WAVE], int wave) {
-  gbyte* gg = (gbyte*)g;
-#pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i)
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(gg + off[i]),
-                                     (lds_void*)(lds + (wave * PER_WAVE + i) * 1024), 16, 0, 0);
-}
-
-// Wait for this wave's outstanding memory operations (including LDS DMA).
+// Wait for this wave's outstanding memory operations (including LDS copies).
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 // The wave's 32 query rows as MFMA B operands: qr[s] holds dims
@@ -132,104 +74,15 @@ __device__ __forceinline__ void load_q_regs(bf16x8 (&qr)[D / 16], const __bf16* 
   for (int s = 0; s < D / 16; ++s) qr[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hf);
 }
 
-// S^T of NKB key blocks starting at block kb0: acc[b] = K[block] Q^T.  The
-// blocks are independent accumulation chains, interleaved, and the operands
-// of step s+1 are read from LDS while the products of step s run.
-template <int D, int NKB>
-__device__ __forceinline__ void qk_blocks(f32x16 (&acc)[NKB], const unsigned char* ktile, int kb0,
-                                          const bf16x8 (&qr)[D / 16], int n, int hf) {
-  constexpr int CPR = D / 8;
-  constexpr int KS = D / 16;
-#pragma unroll
-  for (int b = 0; b < NKB; ++b) acc[b] = f32x16{};
-  bf16x8 a[2][NKB];
-#pragma unroll
-  for (int b = 0; b < NKB; ++b) a[0][b] = lds_chunk<CPR>(ktile, (kb0 + b) * 32 + n, hf);
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (s + 1 < KS) {
-#pragma unroll
-      for (int b = 0; b < NKB; ++b)
-        a[(s + 1) & 1][b] = lds_chunk<CPR>(ktile, (kb0 + b) * 32 + n, 2 * (s + 1) + hf);
-    }
-#pragma unroll
-    for (int b = 0; b < NKB; ++b) acc[b] = mfma32(a[s & 1][b], qr[s], acc[b]);
-  }
+// Maximum / sum of a value over lanes l and l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float swap32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-// Validity of the S slots of a tile, as S/32 32-bit words (bit u of word w is
-// slot 32w + u), for each of the 8 ways a tile can be cut by the grid:
-// combo bit 2/1/0 set = the tile's t/h/w extent is the partial one at the
-// far edge of the grid.  Built once per workgroup by S threads.
-template <int S>
-struct MaskTable {
-  uint32_t w[8][S / 32];
-};
-
-template <int S>
-__device__ __forceinline__ void build_mask_table(MaskTable<S>& mt, const DevLayout& L, int h,
-                                                 int tid) {
-  const int pt = L.shape[h][0], ph = L.shape[h][1], pw = L.shape[h][2];
-  const int et = L.T - (L.grid[h][0] - 1) * pt;   // extent of the last tile along t
-  const int eh = L.H - (L.grid[h][1] - 1) * ph;
-  const int ew = L.W - (L.grid[h][2] - 1) * pw;
-  if (tid < S) {
-    const int dw = tid % pw, r = tid / pw, dh = r % ph, dt = r / ph;
-    const int lane = tid & 63;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const bool ok = (!(c & 4) || dt < et) && (!(c & 2) || dh < eh) && (!(c & 1) || dw < ew);
-      const uint64_t bal = __ballot(ok);
-      if (lane == 0) {
-        mt.w[c][(tid >> 5)] = (uint32_t)bal;
-        if (S >= 64) mt.w[c][(tid >> 5) + 1] = (uint32_t)(bal >> 32);
-      }
-    }
-  }
+__device__ __forceinline__ float swap32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
-// Which of the 8 cuts tile e is (0 = whole tile).
-__device__ __forceinline__ int cut_of(const TileExtent& e) {
-  return (e.lt < e.pt ? 4 : 0) | (e.lh < e.ph ? 2 : 0) | (e.lw < e.pw ? 1 : 0);
-}
-
-// Padding keys -> -inf for key blocks kb0 .. kb0+NKB-1, given the tile's
-// validity words.  Lane half hf holds keys 8hf..8hf+7 and 16+8hf..16+8hf+7 of
-// each block, i.e. bytes hf and 2+hf of the block's word.  Per element: a
-// sign-extended one-bit extract (all ones or all zeros) selects the logit or
-// -inf bitwise.
-template <int NKB, int S>
-__device__ __forceinline__ void mask_keys(f32x16 (&acc)[NKB], const MaskTable<S>& mt, int cut,
-                                          int kb0, int hf) {
-#pragma unroll
-  for (int b = 0; b < NKB; ++b) {
-    const int wbits = (int)(mt.w[cut][kb0 + b] >> (8 * hf));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int keep = __builtin_amdgcn_sbfe(wbits, 16 * (i >> 3) + (i & 7), 1);
-      acc[b][i] = __int_as_float((__float_as_int(acc[b][i]) & keep) | (0xff800000 & ~keep));
-    }
-  }
-}
-
-// Maximum of the wave's logits in this lane, as a tree of 3-input maxima.
-template <int NKB>
-__device__ __forceinline__ float max_of(const f32x16 (&acc)[NKB]) {
-  float m[NKB];
-#pragma unroll
-  for (int b = 0; b < NKB; ++b) {
-    float x = fmaxf(fmaxf(acc[b][0], acc[b][1]), acc[b][2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) x = fmaxf(fmaxf(x, acc[b][i]), acc[b][i + 1]);
-    m[b] = fmaxf(x, acc[b][15]);
-  }
-  float r = m[0];
-#pragma unroll
-  for (int b = 1; b < NKB; ++b) r = fmaxf(r, m[b]);
-  return r;
-}
-
-__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
 // exp2 whose argument is finite or -inf; (-inf) - (-inf) never reaches it.
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -241,6 +94,110 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t G) {
   constexpr int X = 8;
   const int64_t xcd = b % X, per = G / X, rem = G % X;
   return xcd * per + (xcd < rem ? xcd : rem) + b / X;
+}
+
+// A step buffer in LDS: R rows of CPR 16-byte chunks, each row followed by
+// one 16-byte pad, so that 16 lanes reading one chunk column of 16
+// consecutive rows hit 16 distinct bank groups (row stride (CPR+1)*16 bytes
+// is an odd number of 16-byte units) and a lane's reads along a row are one
+// base address plus immediate offsets.  Row r holds HBM row (SWAP ? swap23 :
+// id)(r), rows GSTRIDE bytes apart.  It is filled by 1 KiB copy rounds (64
+// lanes x 16 bytes of consecutive LDS) shared by NW waves; a lane whose 16
+// bytes fall on a pad re-reads chunk 0 of the source.
+template <int R, int CPR, bool SWAP, int GSTRIDE, int NW>
+struct StepBuf {
+  static constexpr int ROWB = (CPR + 1) * 16;
+  static constexpr int ROUNDS = (R * (CPR + 1) + 63) / 64;
+  static constexpr int BYTES = ROUNDS * 1024;
+  static constexpr int PER_WAVE = (ROUNDS + NW - 1) / NW;
+  // round i of wave w fills LDS block w + NW*i; past the last block it fills
+  // block w again with the same bytes, so that every wave issues PER_WAVE
+  // rounds with no branch
+  static __device__ __forceinline__ int block(int wave, int i) {
+    const int q = wave + NW * i;
+    return q < ROUNDS ? q : wave;
+  }
+  // per-lane byte offsets of this lane's chunks, one per round of the wave
+  static __device__ __forceinline__ void offsets(uint32_t (&off)[PER_WAVE], int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int u = block(wave, i) * 64 + lane;   // 16-byte unit of the buffer
+      const int r = u / (CPR + 1), c = u % (CPR + 1);
+      const int gr = SWAP ? ((r & ~31) | swap23(r & 31)) : r;
+      off[i] = (c == CPR || r >= R) ? 0u : (uint32_t)(gr * GSTRIDE + c * 16);
+    }
+  }
+  // issue round i of this wave: buffer `rs` at byte offset `so` (uniform)
+  static __device__ __forceinline__ void round(int i, __amdgpu_buffer_rsrc_t rs, uint32_t so,
+                                               unsigned char* lds, const uint32_t (&off)[PER_WAVE],
+                                               int wave) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + block(wave, i) * 1024), 16,
+                                             off[i], so, 0, 0);
+  }
+  static __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, uint32_t so,
+                                              unsigned char* lds, const uint32_t (&off)[PER_WAVE],
+                                              int wave) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) round(i, rs, so, lds, off, wave);
+  }
+  static __device__ __forceinline__ bf16x8 read(const unsigned char* buf, int r, int c) {
+    return *reinterpret_cast<const bf16x8*>(buf + r * ROWB + c * 16);
+  }
+};
+
+// Raw buffer resource over `bytes` bytes at `base` (range-checked loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Which of the 8 cuts tile e is (0 = whole tile): bit 2/1/0 set = the tile's
+// t/h/w extent is the partial one at the far edge of the grid.
+__device__ __forceinline__ int cut_of(const TileExtent& e) {
+  return (e.lt < e.pt ? 4 : 0) | (e.lh < e.ph ? 2 : 0) | (e.lw < e.pw ? 1 : 0);
+}
+
+// Additive key mask of a 64-key step, as the initial value of the S^T
+// accumulator: 0 for a real key slot, -inf for padding.  Entry
+// [cut][half][b][hf] holds the 16 accumulator elements of 32-key block b of
+// step `half` of a tile with that cut, for lanes of half hf (element i is
+// key 16(i/8) + 8hf + i%8).  Built once per workgroup.
+template <int SPT>
+struct BiasTable {
+  f32x4 v[8][SPT][2][2][4];
+};
+
+template <int SPT>
+__device__ __forceinline__ void build_bias_table(BiasTable<SPT>& bt, const DevLayout& L, int h,
+                                                 int tid, int nthreads) {
+  const int pt = L.shape[h][0], ph = L.shape[h][1], pw = L.shape[h][2];
+  const int et = L.T - (L.grid[h][0] - 1) * pt;   // extent of the last tile along t
+  const int eh = L.H - (L.grid[h][1] - 1) * ph;
+  const int ew = L.W - (L.grid[h][2] - 1) * pw;
+  float* flat = reinterpret_cast<float*>(&bt);
+  constexpr int ENTRIES = 8 * SPT * 2 * 2 * 16;
+  for (int x = tid; x < ENTRIES; x += nthreads) {
+    const int i = x & 15, hf = (x >> 4) & 1, b = (x >> 5) & 1, half = (x >> 6) % SPT;
+    const int cut = (x >> 6) / SPT;
+    const int u = half * 64 + 32 * b + 16 * (i >> 3) + 8 * hf + (i & 7);   // slot in tile
+    const int dw = u % pw, r = u / pw, dh = r % ph, dt = r / ph;
+    const bool ok = (!(cut & 4) || dt < et) && (!(cut & 2) || dh < eh) && (!(cut & 1) || dw < ew);
+    flat[x] = ok ? 0.f : -INFINITY;
+  }
+}
+
+// Seed a step's two S^T accumulators (32-key blocks) from mask rows bp.
+__device__ __forceinline__ void load_bias(f32x16 (&acc)[2], const f32x4* bp) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 x = bp[b * 8 + c];   // [b][hf][c] with hf fixed: stride 2*4 per b
+      acc[b][4 * c + 0] = x[0];
+      acc[b][4 * c + 1] = x[1];
+      acc[b][4 * c + 2] = x[2];
+      acc[b][4 * c + 3] = x[3];
+    }
 }
 
 }  // namespace attn

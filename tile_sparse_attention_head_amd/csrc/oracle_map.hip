@@ -3,16 +3,24 @@
 // key-tile blocks; Veda §2.3: built in two passes over a random subset of
 // query tiles).
 //
-// One workgroup per subset query tile, 2*S/32 waves: wave (qb, kh) holds 32
-// queries in registers and takes key half kh of every key tile; key tiles are
-// copied straight into two LDS stages one tile ahead.  A
-// single loop runs 2*n_h steps over the head's key tiles:
-//   pass 1 (steps 0 .. n_h-1): online row maximum and sum of exp2 over the
-//     wave's keys; the two key halves are combined through LDS -> lse;
-//   pass 2 (steps n_h .. 2n_h-1): per key tile, each query's largest logit,
-//     p = exp2(max - lse), then the maximum over the tile's real queries
-//     (inside the wave by lane exchanges, across waves through LDS) -> map.
-// Pass 2 takes one exp per (query, key tile) rather than one per logit.
+// Because exp is monotone, the block maximum of the probabilities of query
+// row r over key tile j is exp(sm_scale * max_{c in j} q_r.k_c - lse_r): it
+// needs one logit maximum per (row, key tile), not the probabilities
+// themselves.  So
+//   pass 1 (map_stats_kernel) computes every logit once: per subset query
+//     tile and chunk of the head's key tiles, the online row maximum and sum
+//     of exp2 (a partial log-sum-exp) and, per key tile, each row's largest
+//     logit, written to the workspace;
+//   pass 2 (map_reduce_kernel) merges the chunk partials into lse and takes,
+//     per key tile, the maximum over the tile's real rows of
+//     exp2(largest logit - lse).
+// Splitting the key tiles into chunks gives pass 1 enough workgroups to fill
+// the chip whatever the subset size.
+//
+// Pass 1 uses the tile products of the attention kernel: 4 waves of 32
+// queries, K copied HBM -> LDS in 64-key steps two steps ahead, and per step
+// one hand-laid block interleaving the MFMAs of QK(s+1) with the statistics
+// of step s.  Padding keys are masked by seeding the accumulator with -inf.
 #include "attn_common.hpp"
 
 namespace veda {
@@ -20,122 +28,301 @@ namespace {
 
 using namespace attn;
 
-template <int D, int S>
-__global__ __launch_bounds__(4 * S, S / 64) void oracle_map_kernel(
-    DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
-    const int32_t* __restrict__ q_tiles, float* __restrict__ lse_out, float* __restrict__ map) {
-  using C = Cfg<D, S>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][C::TILE_BYTES];
-  __shared__ float ml[C::NW][2][64];
-  __shared__ float red[2][C::NW];
-  __shared__ MaskTable<S> mtab;
+constexpr float kLazyRescale = 8.0f;   // log2 of the largest unnormalised term
 
-  const int64_t sidx = xcd_remap(blockIdx.x, gridDim.x);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+template <int D, int S>
+struct MapPipe {
+  static constexpr int NW = S / 32;             // waves per workgroup
+  static constexpr int SK = 64;                 // keys per step
+  static constexpr int SPT = S / SK;            // steps per key tile
+  static constexpr int KS = D / 16;             // MFMA k-steps over head_dim
+  static constexpr int TILE = S * D * 2;
+  static constexpr int KSTEP = SK * D * 2;      // HBM bytes of one K step
+  using KBuf = StepBuf<SK, D / 8, true, D * 2, NW>;
+};
+
+// Pass 1.  Workgroup (subset entry `sub`, chunk `c`) covers key tiles
+// [c n_h / chunks, (c+1) n_h / chunks) of the head.  Writes, per real or
+// padding query slot q of the tile:
+//   rowmax[sub][j][q] = sm_scale*log2(e) * max over real keys of tile j of q.k
+//   ml[sub][c][q]     = (m, l) with sum over the chunk's real keys of
+//                       exp2(sm_scale*log2(e) q.k) = l * 2^m  (m = -inf, l = 0
+//                       for an empty chunk)
+template <int D, int S>
+__global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
+    DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
+    const int32_t* __restrict__ q_tiles, int chunks, float* __restrict__ rowmax,
+    float2* __restrict__ ml) {
+  using P = MapPipe<D, S>;
+  using KB = typename P::KBuf;
+  constexpr int SPT = P::SPT, KS = P::KS, TILE = P::TILE;
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[KB::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[KB::BYTES];
+  __shared__ BiasTable<SPT> btab;
+
+  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  const int sub = (int)(b / chunks), c = (int)(b % chunks);
+  const int64_t g = ((cint32*)q_tiles)[sub];
+  if (g < 0 || g >= L.tile_off[L.heads]) return;   // the reduce pass writes a zero row
+  const int h = head_of_tile(L, g);
+  const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
+  const int64_t head_base = L.tile_off[h];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hf = lane >> 5;
-  const int qb = wave % C::QB, kh = wave / C::QB;
-  float* mrow = map + sidx * (int64_t)L.max_tiles;
-  const int64_t g = q_tiles[sidx];
-  if (g < 0 || g >= L.tile_off[L.heads]) {           // out-of-range entry: zero row
-    for (int j = tid; j < L.max_tiles; j += C::NT) mrow[j] = 0.f;
+  const int j0 = (int)((int64_t)c * n_h / chunks), j1 = (int)((int64_t)(c + 1) * n_h / chunks);
+  const int N = (j1 - j0) * SPT;   // steps
+
+  bf16x8 qr[KS];
+  const int qslot = wave * 32 + n;
+  load_q_regs<D>(qr, q + (g * S + qslot) * D, hf);
+
+  const auto krs = make_rsrc(reinterpret_cast<const unsigned char*>(k) + head_base * TILE,
+                             (int64_t)n_h * TILE);
+  uint32_t koff[KB::PER_WAVE];
+  KB::offsets(koff, wave, lane);
+  auto k_off = [&](int t) { return (uint32_t)((j0 + t / SPT) * TILE + (t % SPT) * P::KSTEP); };
+  int qcut = 0;   // cut of the tile whose logits are computed next
+  auto bias_of = [&](int t) -> const f32x4* {
+    if (t % SPT == 0) qcut = cut_of(tile_extent(L, h, j0 + t / SPT));
+    return &btab.v[qcut][t % SPT][0][hf][0];
+  };
+
+  float m_run = -INFINITY, l_run = 0.f, tmax = -INFINITY;
+  float* rm_row = rowmax + ((int64_t)sub * L.max_tiles + j0) * S + qslot;
+  f32x16 sA[2], sB[2];
+
+  // One step s: statistics of step s and, in the same hand-laid block,
+  // S^T(s+1) = K(s+1) Q^T, with the copy of K(s+2) spread over the slots.
+  auto step = [&](auto has_qk, auto par, int s) {
+    constexpr bool QK = decltype(has_qk)::value;
+    constexpr int PAR = decltype(par)::value;
+    f32x16 (&scur)[2] = PAR ? sB : sA;
+    f32x16 (&snext)[2] = PAR ? sA : sB;
+    const unsigned char* ksrc = PAR ? k0 : k1;
+    unsigned char* kdst = PAR ? k1 : k0;
+
+    if constexpr (QK) load_bias(snext, bias_of(s + 1));
+    // K(s+2) over K(s); with no step s+2 the rounds re-copy K(s) into its
+    // own, no longer read, slot
+    const uint32_t kgs = s + 2 < N ? k_off(s + 2) : k_off(s);
+    asm volatile("" :: "s"(kgs));
+
+    constexpr int LA = 3;          // operand reads run LA slots ahead of their MFMA
+    constexpr int NSLOT = D / 8;   // QK products of one step
+    constexpr int RW = KB::PER_WAVE;
+    auto operand = [&](int i) -> bf16x8 {
+      return KB::read(ksrc, (i & 1) * 32 + n, 2 * (i >> 1) + hf);
+    };
+    bf16x8 opnd[LA + 1];
+    if constexpr (QK) {
+      static_for<0, LA>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        opnd[i % (LA + 1)] = operand(i);
+      });
+    }
+    float pm[4], e[32];
+    float mxs = 0.f, m_new = 0.f, neg_m = 0.f, psum0 = 0.f, psum1 = 0.f;
+    bool raise = false;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NSLOT>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      static_for<0, RW>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr ((m * (NSLOT - 2)) / RW == i) KB::round(m, krs, kgs, kdst, koff, wave);
+      });
+      if constexpr (QK) {
+        if constexpr (i + LA < NSLOT) opnd[(i + LA) % (LA + 1)] = operand(i + LA);
+        snext[i & 1] = mfma32(opnd[i % (LA + 1)], qr[i >> 1], snext[i & 1]);
+      }
+      // statistics of step s: row maximum in slots 0..4, then the elements
+      if constexpr (i < 4) {
+        constexpr int bb = i >> 1, o8 = (i & 1) * 8;
+        float x = fmaxf(fmaxf(scur[bb][o8], scur[bb][o8 + 1]), scur[bb][o8 + 2]);
+        x = fmaxf(fmaxf(x, scur[bb][o8 + 3]), scur[bb][o8 + 4]);
+        x = fmaxf(fmaxf(x, scur[bb][o8 + 5]), scur[bb][o8 + 6]);
+        pm[i] = fmaxf(x, scur[bb][o8 + 7]);
+        asm volatile("" : "+v"(pm[i]));
+      }
+      if constexpr (i == 3) {
+        mxs = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+        mxs = swap32_max(mxs) * scale_log2;
+        asm volatile("" : "+v"(mxs));
+      }
+      if constexpr (i == 4) {
+        const float m_cand = fmaxf(m_run, mxs);
+        raise = m_cand > m_run + kLazyRescale;
+        m_new = raise ? m_cand : m_run;
+        neg_m = m_new == -INFINITY ? 0.f : -m_new;
+        asm volatile("" : "+v"(neg_m));
+      }
+      // element pairs: FMA in slot fs(k), exp in fs(k)+1, sum in fs(k)+2
+      static_for<0, 16>([&](auto kc_) {
+        constexpr int kp = decltype(kc_)::value;
+        constexpr int f = 5 + (kp * (NSLOT - 7)) / 16;
+        constexpr int el0 = 2 * kp, bb = el0 >> 4, ii = el0 & 15;
+        if constexpr (f == i) {
+          e[el0] = fmaf(scur[bb][ii], scale_log2, neg_m);
+          e[el0 + 1] = fmaf(scur[bb][ii + 1], scale_log2, neg_m);
+          asm volatile("" : "+v"(e[el0]), "+v"(e[el0 + 1]));
+        }
+        if constexpr (f + 1 == i) {
+          e[el0] = exp2_(e[el0]);
+          e[el0 + 1] = exp2_(e[el0 + 1]);
+          asm volatile("" : "+v"(e[el0]), "+v"(e[el0 + 1]));
+        }
+        if constexpr (f + 2 == i) {
+          psum0 += e[el0];
+          psum1 += e[el0 + 1];
+          asm volatile("" : "+v"(psum0), "+v"(psum1));
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+
+    if (raise) l_run *= exp2_(m_run - m_new);
+    m_run = m_new;
+    l_run += psum0 + psum1;
+    // largest logit of the tile, once its last step is in
+    tmax = (s % SPT == 0) ? mxs : fmaxf(tmax, mxs);
+    if (s % SPT == SPT - 1 && hf == 0) rm_row[(int64_t)(s / SPT) * S] = tmax;
+    // own copies landed, and every wave is past its reads of the slot the
+    // next step overwrites
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+  using Z = std::integral_constant<int, 0>;
+  using O1 = std::integral_constant<int, 1>;
+  if (N > 0) {
+    KB::copy(krs, k_off(0), k0, koff, wave);
+    if (N > 1) KB::copy(krs, k_off(1), k1, koff, wave);
+    build_bias_table<SPT>(btab, L, h, tid, 2 * S);
+    wait_all();
+    __syncthreads();
+    load_bias(sA, bias_of(0));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      sA[0] = mfma32(KB::read(k0, n, 2 * s + hf), qr[s], sA[0]);
+      sA[1] = mfma32(KB::read(k0, 32 + n, 2 * s + hf), qr[s], sA[1]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // k0 free
+    int s = 0;
+    for (; s + 1 <= N - 2; s += 2) {
+      step(T{}, Z{}, s);
+      step(T{}, O1{}, s + 1);
+    }
+    if (s <= N - 2) {
+      step(T{}, Z{}, s);
+      ++s;
+    }
+    if (s & 1) step(F{}, O1{}, s);
+    else step(F{}, Z{}, s);
+  }
+  const float l_tot = swap32_sum(l_run);
+  if (hf == 0) ml[((int64_t)sub * chunks + c) * S + qslot] = make_float2(m_run, l_tot);
+}
+
+// Pass 2.  One workgroup of 4 waves per subset entry.  Lane l of every wave
+// holds query slots 2l, 2l+1 (S = 128) or l (S = 64): merges the chunk
+// partials into lse, then waves take key tiles j = w, w+4, ... and reduce
+// max over real slots of exp2(rowmax - lse2) across the wave.
+template <int S>
+__global__ __launch_bounds__(256) void map_reduce_kernel(
+    DevLayout L, const int32_t* __restrict__ q_tiles, int chunks,
+    const float* __restrict__ rowmax, const float2* __restrict__ ml, float* __restrict__ lse,
+    float* __restrict__ map) {
+  constexpr int QPL = S / 64;   // query slots per lane
+  const int sub = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* mrow = map + (int64_t)sub * L.max_tiles;
+  const int64_t g = q_tiles[sub];
+  if (g < 0 || g >= L.tile_off[L.heads]) {
+    for (int j = tid; j < L.max_tiles; j += 256) mrow[j] = 0.f;
     return;
   }
   const int h = head_of_tile(L, g);
   const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
-  const int64_t head_base = L.tile_off[h];
-  const TileExtent eq = tile_extent(L, h, (int)(g - head_base));
-  const bool q_real = eq.slot_real(qb * 32 + n);
+  const TileExtent eq = tile_extent(L, h, (int)(g - L.tile_off[h]));
 
-  bf16x8 qr[C::KS];
-  load_q_regs<D>(qr, q + (g * S + qb * 32 + n) * D, hf);
-
-  const unsigned char* kg = reinterpret_cast<const unsigned char*>(k) + head_base * C::TILE_BYTES;
-  uint32_t koff[C::DMA_PER_WAVE];
-  dma_offsets<C::CPR_K, C::DMA_PER_WAVE, true>(koff, wave, lane);
-  dma_tile<C::DMA_PER_WAVE>(kg, smem[0], koff, wave);
-  build_mask_table<S>(mtab, L, h, tid);
-  wait_all();
-  __syncthreads();
-
-  float m_run = -INFINITY, l_run = 0.f, lse2 = 0.f;
-  const int steps = 2 * n_h;
-  int stage = 0;
-  for (int it = 0; it < steps; ++it) {
-    const int j = it < n_h ? it : it - n_h;
-    if (it + 1 < steps)
-      dma_tile<C::DMA_PER_WAVE>(kg + (int64_t)((it + 1) % n_h) * C::TILE_BYTES, smem[stage ^ 1],
-                                koff, wave);
-    if (it == n_h) {
-      // end of pass 1: combine with the other key half -> base-2 lse per query
-      const int partner = (kh ^ 1) * C::QB + qb;
-      const float m_a = m_run, l_a = l_run + xor32(l_run);
-      const float m_b = ml[partner][0][lane], l_b = ml[partner][1][lane];
-      const float mt = fmaxf(m_a, m_b);
-      const float lt = (m_a == -INFINITY ? 0.f : l_a * exp2_(m_a - mt)) +
-                       (m_b == -INFINITY ? 0.f : l_b * exp2_(m_b - mt));
-      lse2 = mt + __log2f(lt);
-      if (kh == 0 && hf == 0) lse_out[sidx * S + qb * 32 + n] = lse2 * 0.69314718055994531f;
-    }
-    if (it > n_h && tid == 0) {   // publish the previous key tile's block maximum
-      float v = red[(it - 1) & 1][0];
+  float lse2[QPL];
+  bool real[QPL];
 #pragma unroll
-      for (int w = 1; w < C::NW; ++w) v = fmaxf(v, red[(it - 1) & 1][w]);
-      mrow[j - 1] = v;
-    }
-
-    f32x16 sacc[C::KBW];
-    qk_blocks<D, C::KBW>(sacc, smem[stage], kh * C::KBW, qr, n, hf);
-    const int cut = cut_of(tile_extent(L, h, j));
-    if (cut != 0) mask_keys<C::KBW, S>(sacc, mtab, cut, kh * C::KBW, hf);
-    float mx = max_of<C::KBW>(sacc);
-    mx = fmaxf(mx, xor32(mx));
-
-    if (it < n_h) {
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int b = 0; b < C::KBW; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) psum += exp2_(fmaf(sacc[b][i], scale_log2, neg_m));
-      l_run = (m_run == -INFINITY ? 0.f : l_run * exp2_(m_run - m_new)) + psum;
-      m_run = m_new;
-      if (it == n_h - 1) {
-        ml[wave][0][lane] = m_run;
-        ml[wave][1][lane] = l_run + xor32(l_run);
+  for (int u = 0; u < QPL; ++u) {
+    const int qs = QPL * lane + u;
+    real[u] = eq.slot_real(qs);
+    float M = -INFINITY;
+    for (int c = 0; c < chunks; ++c) M = fmaxf(M, ml[((int64_t)sub * chunks + c) * S + qs].x);
+    float Ls = 0.f;
+    if (M != -INFINITY)
+      for (int c = 0; c < chunks; ++c) {
+        const float2 p = ml[((int64_t)sub * chunks + c) * S + qs];
+        if (p.y > 0.f) Ls += p.y * exp2_(p.x - M);
       }
-    } else {
-      float pr = (q_real && mx != -INFINITY) ? exp2_(fmaf(mx, scale_log2, -lse2)) : 0.f;
+    lse2[u] = Ls > 0.f ? M + __log2f(Ls) : -INFINITY;
+    if (wave == 0) lse[(int64_t)sub * S + qs] = lse2[u] * 0.69314718055994531f;
+  }
+  const float* rm = rowmax + (int64_t)sub * L.max_tiles * S + QPL * lane;
+  for (int j = wave; j < L.max_tiles; j += 4) {
+    float v = 0.f;
+    if (j < n_h) {
+      float x[QPL];
+      if constexpr (QPL == 2) {
+        const float2 r2 = *reinterpret_cast<const float2*>(rm + (int64_t)j * S);
+        x[0] = r2.x;
+        x[1] = r2.y;
+      } else {
+        x[0] = rm[(int64_t)j * S];
+      }
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) pr = fmaxf(pr, __shfl_xor(pr, o, 64));
-      if (lane == 0) red[it & 1][wave] = pr;
+      for (int u = 0; u < QPL; ++u)
+        if (real[u] && lse2[u] != -INFINITY) v = fmaxf(v, exp2_(x[u] - lse2[u]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     }
-
-    wait_all();
-    __syncthreads();
-    stage ^= 1;
+    if (lane == 0) mrow[j] = v;
   }
-  if (tid == 0) {
-    float v = red[(steps - 1) & 1][0];
-#pragma unroll
-    for (int w = 1; w < C::NW; ++w) v = fmaxf(v, red[(steps - 1) & 1][w]);
-    mrow[n_h - 1] = v;
-  }
-  for (int j = n_h + tid; j < L.max_tiles; j += C::NT) mrow[j] = 0.f;
 }
 
 }  // namespace
 
+int64_t map_chunks(int64_t n_sub, int64_t max_tiles) {
+  if (n_sub <= 0) return 1;
+  int64_t c = (1536 + n_sub - 1) / n_sub;   // about 1.5 K workgroups in pass 1
+  if (c > 16) c = 16;
+  if (c > max_tiles) c = max_tiles;
+  return c < 1 ? 1 : c;
+}
+
+int64_t map_workspace_bytes(const DevLayout& L, int64_t n_sub) {
+  if (n_sub <= 0) return 0;
+  const int64_t S = L.S;
+  const int64_t rm = ((n_sub * L.max_tiles * S * 4) + 255) / 256 * 256;
+  const int64_t mlb = n_sub * map_chunks(n_sub, L.max_tiles) * S * 8;
+  return rm + mlb;
+}
+
 int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm_scale,
-                      const int32_t* q_tiles, int n_sub, float* lse, float* map, hipStream_t s) {
+                      const int32_t* q_tiles, int n_sub, void* workspace, float* lse, float* map,
+                      hipStream_t s) {
   if (n_sub == 0) return VEDA_OK;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
+  const int chunks = (int)map_chunks(n_sub, L.max_tiles);
+  float* rowmax = static_cast<float*>(workspace);
+  const int64_t rm = ((n_sub * (int64_t)L.max_tiles * L.S * 4) + 255) / 256 * 256;
+  float2* ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(workspace) + rm);
+  const unsigned grid1 = (unsigned)(n_sub * chunks);
   if (L.d == 128) {
-    hipLaunchKernelGGL((oracle_map_kernel<128, 128>), dim3(n_sub), dim3(Cfg<128, 128>::NT), 0, s,
-                       L, (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, lse, map);
+    hipLaunchKernelGGL((map_stats_kernel<128, 128>), dim3(grid1), dim3(256), 0, s, L,
+                       (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, chunks, rowmax, ml);
+    hipLaunchKernelGGL((map_reduce_kernel<128>), dim3(n_sub), dim3(256), 0, s, L, q_tiles, chunks,
+                       rowmax, ml, lse, map);
   } else {
-    hipLaunchKernelGGL((oracle_map_kernel<64, 64>), dim3(n_sub), dim3(Cfg<64, 64>::NT), 0, s, L,
-                       (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, lse, map);
+    hipLaunchKernelGGL((map_stats_kernel<64, 64>), dim3(grid1), dim3(128), 0, s, L,
+                       (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, chunks, rowmax, ml);
+    hipLaunchKernelGGL((map_reduce_kernel<64>), dim3(n_sub), dim3(256), 0, s, L, q_tiles, chunks,
+                       rowmax, ml, lse, map);
   }
   return launch_status();
 }

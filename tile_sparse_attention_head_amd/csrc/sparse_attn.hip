@@ -32,8 +32,6 @@
 // Workgroups are ordered XCD-aware and head-major, so the query tiles running
 // together on one XCD are spatial neighbours whose kept key tiles overlap in
 // that XCD's L2.
-#include <type_traits>
-
 #include "attn_common.hpp"
 
 namespace veda {
@@ -41,67 +39,7 @@ namespace {
 
 using namespace attn;
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// f(integral_constant<int, I>) for I = B .. E-1, expanded at compile time
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 constexpr float kLazyRescale = 8.0f;   // log2 of the largest unnormalised p
-
-// A step buffer in LDS: R rows of CPR 16-byte chunks, each row followed by
-// one 16-byte pad, so that 16 lanes reading one chunk column of 16
-// consecutive rows hit 16 distinct bank groups (row stride (CPR+1)*16 bytes
-// is an odd number of 16-byte units) and a lane's reads along a row are one
-// base address plus immediate offsets.  It is filled by 1 KiB copy rounds
-// (64 lanes x 16 bytes of consecutive LDS); a lane whose 16 bytes fall on a
-// pad re-reads chunk 0 of the tile.
-template <int R, int CPR, bool SWAP, int GSTRIDE, int NW>
-struct StepBuf {
-  static constexpr int ROWB = (CPR + 1) * 16;
-  static constexpr int ROUNDS = (R * (CPR + 1) + 63) / 64;
-  static constexpr int BYTES = ROUNDS * 1024;
-  static constexpr int PER_WAVE = (ROUNDS + NW - 1) / NW;
-  // round i of wave w fills LDS block w + NW*i; past the last block it fills
-  // block w again with the same bytes, so that every wave issues PER_WAVE
-  // rounds with no branch
-  static __device__ __forceinline__ int block(int wave, int i) {
-    const int q = wave + NW * i;
-    return q < ROUNDS ? q : wave;
-  }
-
-  // per-lane HBM byte offsets of this lane's chunks, one per round of the wave
-  static __device__ __forceinline__ void offsets(uint32_t (&off)[PER_WAVE], int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int u = block(wave, i) * 64 + lane;   // 16-byte unit of the buffer
-      const int r = u / (CPR + 1), c = u % (CPR + 1);
-      const int gr = SWAP ? ((r & ~31) | swap23(r & 31)) : r;
-      off[i] = (c == CPR || r >= R) ? 0u : (uint32_t)(gr * GSTRIDE + c * 16);
-    }
-  }
-  // issue round i of this wave: buffer `rs` at byte offset `so` (uniform)
-  static __device__ __forceinline__ void round(int i, __amdgpu_buffer_rsrc_t rs, uint32_t so,
-                                               unsigned char* lds, const uint32_t (&off)[PER_WAVE],
-                                               int wave) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + block(wave, i) * 1024), 16,
-                                             off[i], so, 0, 0);
-  }
-  static __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, uint32_t so,
-                                              unsigned char* lds, const uint32_t (&off)[PER_WAVE],
-                                              int wave) {
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) round(i, rs, so, lds, off, wave);
-  }
-  static __device__ __forceinline__ bf16x8 read(const unsigned char* buf, int r, int c) {
-    return *reinterpret_cast<const bf16x8*>(buf + r * ROWB + c * 16);
-  }
-};
 
 template <int D, int S>
 struct Pipe {
@@ -117,19 +55,6 @@ struct Pipe {
   static_assert(S % SK == 0, "tile must hold whole steps");
 };
 
-__device__ __forceinline__ float swap32_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float swap32_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Read-only, wave-uniform data through the constant address space, so that
-// it is fetched with scalar loads (which never wait on the LDS copies).
-typedef __attribute__((address_space(4))) const int32_t cint32;
-
 // Walks the valid entries of a CSR row: one cursor per copy stream.
 struct Cursor {
   cint32* col;
@@ -144,34 +69,6 @@ struct Cursor {
     j = 0;
   }
 };
-
-// Additive key mask of one step, as the initial value of the S^T accumulator:
-// 0 for a real key slot, -inf for padding.  Entry [cut][half][b][hf] is the
-// 16 accumulator elements of 32-key block b of step `half` of a tile with
-// that cut, for lanes of half hf (element i is key 16(i/8) + 8hf + i%8).
-template <int SPT>
-struct BiasTable {
-  f32x4 v[8][SPT][2][2][4];
-};
-
-template <int S, int SPT>
-__device__ __forceinline__ void build_bias_table(BiasTable<SPT>& bt, const DevLayout& L, int h,
-                                                 int tid, int nthreads) {
-  const int pt = L.shape[h][0], ph = L.shape[h][1], pw = L.shape[h][2];
-  const int et = L.T - (L.grid[h][0] - 1) * pt;   // extent of the last tile along t
-  const int eh = L.H - (L.grid[h][1] - 1) * ph;
-  const int ew = L.W - (L.grid[h][2] - 1) * pw;
-  float* flat = reinterpret_cast<float*>(&bt);
-  constexpr int ENTRIES = 8 * SPT * 2 * 2 * 16;
-  for (int x = tid; x < ENTRIES; x += nthreads) {
-    const int i = x & 15, hf = (x >> 4) & 1, b = (x >> 5) & 1, half = (x >> 6) % SPT;
-    const int cut = (x >> 6) / SPT;
-    const int u = half * 64 + 32 * b + 16 * (i >> 3) + 8 * hf + (i & 7);   // slot in tile
-    const int dw = u % pw, r = u / pw, dh = r % ph, dt = r / ph;
-    const bool ok = (!(cut & 4) || dt < et) && (!(cut & 2) || dh < eh) && (!(cut & 1) || dw < ew);
-    flat[x] = ok ? 0.f : -INFINITY;
-  }
-}
 
 template <int D, int S>
 __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
@@ -216,12 +113,10 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   const int N = kept * SPT;   // steps
 
   // the head's K and V^T tiles as buffer resources (raw, bounds = the head)
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const unsigned char*>(k) + head_base * TILE), (short)0,
-      n_h * TILE, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(reinterpret_cast<const unsigned char*>(vt) + head_base * TILE), (short)0,
-      n_h * TILE, 0x00020000);
+  const auto krs = make_rsrc(reinterpret_cast<const unsigned char*>(k) + head_base * TILE,
+                             (int64_t)n_h * TILE);
+  const auto vrs = make_rsrc(reinterpret_cast<const unsigned char*>(vt) + head_base * TILE,
+                             (int64_t)n_h * TILE);
   uint32_t koff[KB::PER_WAVE], voff[VB::PER_WAVE];
   KB::offsets(koff, wave, lane);
   VB::offsets(voff, wave, lane);
@@ -262,18 +157,6 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   f32x16 sA[2], sB[2];
   bf16x8 pA[4], pB[4];
 
-  auto load_bias = [&](f32x16 (&acc)[2], const f32x4* bp) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 x = bp[b * 8 + c];   // [b][hf][c] with hf fixed: stride 2*4 per b
-        acc[b][4 * c + 0] = x[0];
-        acc[b][4 * c + 1] = x[1];
-        acc[b][4 * c + 2] = x[2];
-        acc[b][4 * c + 3] = x[3];
-      }
-  };
 
   // One step s.  PAR = s & 1 picks slots and register sets at compile time.
   // The matrix products, their LDS operand reads and the softmax are laid out
@@ -412,7 +295,7 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
       kg_last = next_k();
       KB::copy(krs, kg_last, k1, koff, wave);
     }
-    build_bias_table<S, SPT>(btab, L, h, tid, 2 * S);
+    build_bias_table<SPT>(btab, L, h, tid, 2 * S);
     wait_all();
     __syncthreads();
     // logits of step 0

@@ -76,8 +76,12 @@ int launch_sparse_attn(const DevLayout& L, const void* q, const void* k, const v
                        const int32_t* row_ptr, const int32_t* col_idx, float sm_scale,
                        void* o, float* lse, hipStream_t s);
 int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm_scale,
-                      const int32_t* q_tiles, int n_sub, float* lse, float* map,
-                      hipStream_t s);
+                      const int32_t* q_tiles, int n_sub, void* workspace, float* lse,
+                      float* map, hipStream_t s);
+// Key-tile chunks per subset entry in the map's first pass, and the bytes of
+// workspace the map needs (row maxima, then per-chunk partial sums).
+int64_t map_chunks(int64_t n_sub, int64_t max_tiles);
+int64_t map_workspace_bytes(const DevLayout& L, int64_t n_sub);
 
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? VEDA_OK : VEDA_ERR_LAUNCH;

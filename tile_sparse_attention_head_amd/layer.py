@@ -44,6 +44,7 @@ class TileSparseAttention:
         self.vt_perm = torch.empty(nt, dtype=bf, device=dev)
         self.o_perm = torch.empty(nt, dtype=bf, device=dev)
         self.lse = torch.empty(L.total_tiles * tile_size, dtype=f32, device=dev)
+        self._map_ws = None   # veda_oracle_maxpool_map workspace, sized on first use
         self.desc = torch.empty(2 * L.total_tiles * 3 * head_dim, dtype=f32, device=dev)
         self.phi = torch.empty(2 * L.total_tiles * self.d_e, dtype=f32, device=dev)
         self.scores = torch.empty(L.total_scores, dtype=f32, device=dev)
@@ -96,6 +97,10 @@ class TileSparseAttention:
         if out_map is None:
             out_map = torch.empty(max(1, n_sub * self.L.max_tiles), dtype=torch.float32,
                                   device=self.q_perm.device)
-        V.veda_oracle_maxpool_map(self.L, self.q_perm, self.k_perm, sm_scale, q_tiles, lse,
-                                  out_map, stream)
+        need = V.veda_oracle_maxpool_map_workspace(self.L, n_sub)
+        if self._map_ws is None or self._map_ws.numel() < need:
+            # kept across calls; the pass-1 row maxima live here
+            self._map_ws = torch.empty(max(16, need), dtype=torch.uint8, device=self.q_perm.device)
+        V.veda_oracle_maxpool_map(self.L, self.q_perm, self.k_perm, sm_scale, q_tiles,
+                                  self._map_ws, lse, out_map, stream)
         return lse, out_map
