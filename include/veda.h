@@ -109,7 +109,9 @@ int veda_keep_count(int32_t n_tiles, int32_t sparsity_pct, int32_t* k_out);
  * FWD/FWD_T write zeros to padding slots; INV reads only real slots and
  * writes every element of y.  Pure data movement: bit-exact.
  * dtype VEDA_BF16 or VEDA_F32 (element size 2 or 4 bytes).  Supported:
- * head_dim*element_size a multiple of 16 bytes and pointers 16-byte aligned
+ * head_dim*element_size a multiple of 16 bytes, tile_size <= 256, pointers
+ * 16-byte aligned; FWD_T also needs tile_size*element_size a multiple of 16
+ * bytes and, for F32, head_dim*(tile_size+4)*4 + 2048 <= 65536
  * (VEDA_ERR_UNSUPPORTED otherwise).  x and y must not overlap. */
 int veda_tile_permute(const veda_layout* L, int32_t dtype, int32_t dir,
                       const void* x, void* y, void* stream);

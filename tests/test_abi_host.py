@@ -122,6 +122,11 @@ def test_device_calls_reject_before_launch(lib):
     assert lib.veda_tile_permute(Lp, 0, 9, fake, fake * 4, None) == -1
     assert lib.veda_tile_permute(Lp, 0, 0, fake + 2, fake * 4, None) == -2
     assert lib.veda_tile_permute(Lp, 0, 0, fake, fake + 4096, None) == -1      # overlap
+    # tiles above 256 slots, and an f32 FWD_T whose LDS image would not fit
+    L4 = V.veda_layout_init(8, 8, 8, 64, 512, [(8, 8, 8)])
+    assert lib.veda_tile_permute(ctypes.byref(L4), 0, 0, fake, fake * 64, None) == -2
+    L5 = V.veda_layout_init(8, 8, 8, 128, 128, [(2, 8, 8)])
+    assert lib.veda_tile_permute(ctypes.byref(L5), 1, 2, fake, fake * 64, None) == -2
     # tripool: null weights, bad d_e
     assert lib.veda_tripool_score(Lp, 0, fake, fake, None, fake, None, None, 128, fake, fake, fake, None) == -1
     assert lib.veda_tripool_score(Lp, 0, fake, fake, fake, fake, None, None, 0, fake, fake, fake, None) == -1

@@ -144,10 +144,12 @@ int veda_tile_permute(const veda_layout* L, int32_t dtype, int32_t dir, const vo
   if (x == nullptr || y == nullptr) return VEDA_ERR_INVALID_ARG;
   const int esize = dtype == VEDA_F32 ? 4 : 2;
   if ((L->head_dim * esize) % 16 != 0) return VEDA_ERR_UNSUPPORTED;
+  if (L->tile_size > 256) return VEDA_ERR_UNSUPPORTED;   // per-tile row table in LDS
   if (!aligned16(x) || !aligned16(y)) return VEDA_ERR_UNSUPPORTED;
   if (dir == VEDA_FWD_T) {
     if ((L->tile_size * esize) % 16 != 0) return VEDA_ERR_UNSUPPORTED;
-    if ((size_t)L->head_dim * (L->tile_size + 16 / esize) * esize > 65536) return VEDA_ERR_UNSUPPORTED;
+    if (esize == 4 && (size_t)L->head_dim * (L->tile_size + 4) * 4 + 2048 > 65536)
+      return VEDA_ERR_UNSUPPORTED;
   }
   const size_t tok = (size_t)L->T * L->H * L->W * L->num_heads * L->head_dim * esize;
   const size_t til = (size_t)L->tile_off[L->num_heads] * L->tile_size * L->head_dim * esize;

@@ -224,28 +224,52 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
   if (hf == 0) ml[((int64_t)sub * chunks + c) * S + qslot] = make_float2(m_run, l_tot);
 }
 
-// Pass 2.  One workgroup of 4 waves per subset entry.  Lane l of every wave
-// holds query slots 2l, 2l+1 (S = 128) or l (S = 64): merges the chunk
-// partials into lse, then waves take key tiles j = w, w+4, ... and reduce
-// max over real slots of exp2(rowmax - lse2) across the wave.
+// Pass 2.  Workgroup (subset entry, block of 32 key tiles), 4 waves.  Lane l
+// of every wave holds query slots 2l, 2l+1 (S = 128) or l (S = 64): merges
+// the chunk partials into lse2, then wave w takes key tiles jb + w, jb + w +
+// 4, ... of the block and reduces max over real slots of exp2(rowmax - lse2)
+// across the wave.  Block 0 also writes lse.
+constexpr int kReduceTiles = 32;
+constexpr int kMaxChunks = 16;   // map_chunks() never returns more
+
 template <int S>
 __global__ __launch_bounds__(256) void map_reduce_kernel(
     DevLayout L, const int32_t* __restrict__ q_tiles, int chunks,
     const float* __restrict__ rowmax, const float2* __restrict__ ml, float* __restrict__ lse,
     float* __restrict__ map) {
   constexpr int QPL = S / 64;   // query slots per lane
-  const int sub = blockIdx.x;
+  const int sub = blockIdx.y;
+  const int jb = blockIdx.x * kReduceTiles;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float* mrow = map + (int64_t)sub * L.max_tiles;
+  const int jend = min(jb + kReduceTiles, (int)L.max_tiles);
   const int64_t g = q_tiles[sub];
   if (g < 0 || g >= L.tile_off[L.heads]) {
-    for (int j = tid; j < L.max_tiles; j += 256) mrow[j] = 0.f;
+    for (int j = jb + tid; j < jend; j += 256) mrow[j] = 0.f;
     return;
   }
   const int h = head_of_tile(L, g);
   const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
   const TileExtent eq = tile_extent(L, h, (int)(g - L.tile_off[h]));
 
+  // every load of the workgroup goes out first: the chunk partials of this
+  // lane's slots and the row maxima of its key tiles
+  float2 part[QPL][kMaxChunks];
+#pragma unroll
+  for (int u = 0; u < QPL; ++u)
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      part[u][c] = c < chunks ? ml[((int64_t)sub * chunks + c) * S + QPL * lane + u]
+                              : make_float2(-INFINITY, 0.f);
+  const float* rm = rowmax + (int64_t)sub * L.max_tiles * S + QPL * lane;
+  constexpr int PER_WAVE = kReduceTiles / 4;
+  float x[PER_WAVE][QPL];
+#pragma unroll
+  for (int t = 0; t < PER_WAVE; ++t) {
+    const int j = jb + wave + 4 * t;
+#pragma unroll
+    for (int u = 0; u < QPL; ++u) x[t][u] = j < n_h ? rm[(int64_t)j * S + u] : 0.f;
+  }
   float lse2[QPL];
   bool real[QPL];
 #pragma unroll
@@ -253,35 +277,27 @@ __global__ __launch_bounds__(256) void map_reduce_kernel(
     const int qs = QPL * lane + u;
     real[u] = eq.slot_real(qs);
     float M = -INFINITY;
-    for (int c = 0; c < chunks; ++c) M = fmaxf(M, ml[((int64_t)sub * chunks + c) * S + qs].x);
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, part[u][c].x);
     float Ls = 0.f;
-    if (M != -INFINITY)
-      for (int c = 0; c < chunks; ++c) {
-        const float2 p = ml[((int64_t)sub * chunks + c) * S + qs];
-        if (p.y > 0.f) Ls += p.y * exp2_(p.x - M);
-      }
-    lse2[u] = Ls > 0.f ? M + __log2f(Ls) : -INFINITY;
-    if (wave == 0) lse[(int64_t)sub * S + qs] = lse2[u] * 0.69314718055994531f;
-  }
-  const float* rm = rowmax + (int64_t)sub * L.max_tiles * S + QPL * lane;
-  for (int j = wave; j < L.max_tiles; j += 4) {
-    float v = 0.f;
-    if (j < n_h) {
-      float x[QPL];
-      if constexpr (QPL == 2) {
-        const float2 r2 = *reinterpret_cast<const float2*>(rm + (int64_t)j * S);
-        x[0] = r2.x;
-        x[1] = r2.y;
-      } else {
-        x[0] = rm[(int64_t)j * S];
-      }
+    if (M != -INFINITY) {
 #pragma unroll
-      for (int u = 0; u < QPL; ++u)
-        if (real[u] && lse2[u] != -INFINITY) v = fmaxf(v, exp2_(x[u] - lse2[u]));
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+      for (int c = 0; c < kMaxChunks; ++c)
+        if (part[u][c].y > 0.f) Ls += part[u][c].y * exp2_(part[u][c].x - M);
     }
-    if (lane == 0) mrow[j] = v;
+    lse2[u] = Ls > 0.f ? M + __log2f(Ls) : -INFINITY;
+    if (blockIdx.x == 0 && wave == 0) lse[(int64_t)sub * S + qs] = lse2[u] * 0.69314718055994531f;
+  }
+#pragma unroll
+  for (int t = 0; t < PER_WAVE; ++t) {
+    const int j = jb + wave + 4 * t;
+    float v = 0.f;
+#pragma unroll
+    for (int u = 0; u < QPL; ++u)
+      if (j < n_h && real[u] && lse2[u] != -INFINITY) v = fmaxf(v, exp2_(x[t][u] - lse2[u]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    if (lane == 0 && j < jend) mrow[j] = v;
   }
 }
 
@@ -290,7 +306,7 @@ __global__ __launch_bounds__(256) void map_reduce_kernel(
 int64_t map_chunks(int64_t n_sub, int64_t max_tiles) {
   if (n_sub <= 0) return 1;
   int64_t c = (1536 + n_sub - 1) / n_sub;   // about 1.5 K workgroups in pass 1
-  if (c > 16) c = 16;
+  if (c > kMaxChunks) c = kMaxChunks;
   if (c > max_tiles) c = max_tiles;
   return c < 1 ? 1 : c;
 }
@@ -313,15 +329,16 @@ int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm
   const int64_t rm = ((n_sub * (int64_t)L.max_tiles * L.S * 4) + 255) / 256 * 256;
   float2* ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(workspace) + rm);
   const unsigned grid1 = (unsigned)(n_sub * chunks);
+  const dim3 grid2((unsigned)((L.max_tiles + kReduceTiles - 1) / kReduceTiles), (unsigned)n_sub);
   if (L.d == 128) {
     hipLaunchKernelGGL((map_stats_kernel<128, 128>), dim3(grid1), dim3(256), 0, s, L,
                        (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, chunks, rowmax, ml);
-    hipLaunchKernelGGL((map_reduce_kernel<128>), dim3(n_sub), dim3(256), 0, s, L, q_tiles, chunks,
+    hipLaunchKernelGGL((map_reduce_kernel<128>), grid2, dim3(256), 0, s, L, q_tiles, chunks,
                        rowmax, ml, lse, map);
   } else {
     hipLaunchKernelGGL((map_stats_kernel<64, 64>), dim3(grid1), dim3(128), 0, s, L,
                        (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, chunks, rowmax, ml);
-    hipLaunchKernelGGL((map_reduce_kernel<64>), dim3(n_sub), dim3(256), 0, s, L, q_tiles, chunks,
+    hipLaunchKernelGGL((map_reduce_kernel<64>), grid2, dim3(256), 0, s, L, q_tiles, chunks,
                        rowmax, ml, lse, map);
   }
   return launch_status();

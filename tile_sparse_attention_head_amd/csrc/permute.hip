@@ -2,16 +2,19 @@
 // head-conditioned tile geometry): regroup one head's T x H x W tokens into
 // its (pt, ph, pw) tiles and back.
 //
-// One workgroup per tile.  Every row (one token of one head) is d contiguous
-// elements in both layouts, moved as 16-byte chunks: consecutive lanes take
-// consecutive chunks, so each row is one fully coalesced 16*CPR-byte burst.
-// The kernels are pure data movement, bound by HBM bandwidth.
+// One workgroup per tile.  The row (token, head) of each of the tile's slots
+// is computed once into LDS.  Every row is d contiguous elements in both
+// layouts, moved as 16-byte chunks: consecutive lanes take consecutive
+// chunks, so each row is one fully coalesced 16*CPR-byte burst, and a lane
+// issues several loads before its stores.  The kernels are pure data
+// movement, bound by HBM bandwidth.
 #include "veda_internal.hpp"
 
 namespace veda {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBatch = 8;   // chunks a lane loads before it stores any
 
 struct Chunk { uint32_t x, y, z, w; };
 
@@ -27,25 +30,51 @@ __device__ __forceinline__ int64_t token_of_slot(const DevLayout& L, const TileE
   return (t * L.H + h) * L.W + w;
 }
 
+// Row (token * heads + head) of every slot of tile g in the token-major
+// layout, -1 for padding: computed once per workgroup into LDS.
+__device__ __forceinline__ int tile_rows(const DevLayout& L, int64_t g, int64_t* rows) {
+  const int h = head_of_tile(L, g);
+  const TileExtent e = tile_extent(L, h, (int)(g - L.tile_off[h]));
+  for (int u = threadIdx.x; u < L.S; u += kThreads) {
+    const int64_t n = token_of_slot(L, e, u);
+    rows[u] = n >= 0 ? n * L.heads + h : -1;
+  }
+  __syncthreads();
+  return h;
+}
+
 // x [N][heads][CPR chunks] -> y [tiles*S][CPR chunks]; padding slots = 0.
 __global__ __launch_bounds__(kThreads) void permute_fwd_kernel(DevLayout L, int cpr,
                                                                const Chunk* __restrict__ x,
                                                                Chunk* __restrict__ y) {
+  __shared__ int64_t rows[256];
   const int64_t g = blockIdx.x;
-  const int h = head_of_tile(L, g);
-  const TileExtent e = tile_extent(L, h, (int)(g - L.tile_off[h]));
+  tile_rows(L, g, rows);
   const int total = L.S * cpr;
   Chunk* dst = y + g * (int64_t)total;
-  for (int c = threadIdx.x; c < total; c += kThreads) {
-    const int u = c / cpr, k = c - u * cpr;
-    const int64_t n = token_of_slot(L, e, u);
-    Chunk v = {0u, 0u, 0u, 0u};
-    if (n >= 0) v = x[(n * L.heads + h) * cpr + k];
-    dst[c] = v;
+  for (int c0 = 0; c0 < total; c0 += kThreads * kBatch) {
+    Chunk v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kThreads + threadIdx.x;
+      v[i] = Chunk{0u, 0u, 0u, 0u};
+      if (c < total) {
+        const int u = c / cpr, k = c - u * cpr;
+        const int64_t r = rows[u];
+        if (r >= 0) v[i] = x[r * cpr + k];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kThreads + threadIdx.x;
+      if (c < total) dst[c] = v[i];
+    }
   }
 }
 
-// x tile order -> y [N][heads][CPR]; only real slots are read and written.
+// x tile order -> y [N][heads][CPR]; only real slots are read and written
+// (one chunk per lane per pass: batching the loads slows the scattered
+// stores down).
 __global__ __launch_bounds__(kThreads) void permute_inv_kernel(DevLayout L, int cpr,
                                                                const Chunk* __restrict__ x,
                                                                Chunk* __restrict__ y) {
@@ -61,31 +90,70 @@ __global__ __launch_bounds__(kThreads) void permute_inv_kernel(DevLayout L, int 
   }
 }
 
-// x [N][heads][d] -> y tile-transposed ([d][S] per tile).  The tile passes
+// bf16 x [N][heads][d] -> y tile-transposed ([d][S] per tile), in registers:
+// each lane moves one block of 8 slots x 8 channels -- eight 16-byte reads
+// along token rows, an 8x8 transpose of 16-bit values with byte permutes,
+// eight 16-byte writes along channel rows.  Lanes take consecutive channel
+// chunks of one slot group, so each read instruction covers whole token rows.
+__global__ __launch_bounds__(kThreads) void permute_fwd_t_bf16_kernel(DevLayout L,
+                                                                      const Chunk* __restrict__ x,
+                                                                      Chunk* __restrict__ y) {
+  __shared__ int64_t rows[256];
+  const int64_t g = blockIdx.x;
+  tile_rows(L, g, rows);
+  const int S = L.S, cpr = L.d / 8;             // channel chunks per token row
+  Chunk* dst = y + g * (int64_t)S * cpr;        // [d][S] bf16 = d rows of S/8 chunks
+  for (int b = threadIdx.x; b < (S / 8) * cpr; b += kThreads) {
+    const int k = b % cpr, tg = b / cpr;        // channels 8k..8k+7, slots 8tg..8tg+7
+    Chunk r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t row = rows[8 * tg + j];
+      r[j] = Chunk{0u, 0u, 0u, 0u};
+      if (row >= 0) r[j] = x[row * cpr + k];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      // channel 8k+q of slot j sits in word q/2 of r[j], low half for even q
+      const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t w[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const Chunk& a = r[2 * m];
+        const Chunk& c = r[2 * m + 1];
+        const uint32_t lo = (q >> 1) == 0 ? a.x : (q >> 1) == 1 ? a.y : (q >> 1) == 2 ? a.z : a.w;
+        const uint32_t hi = (q >> 1) == 0 ? c.x : (q >> 1) == 1 ? c.y : (q >> 1) == 2 ? c.z : c.w;
+        w[m] = __builtin_amdgcn_perm(hi, lo, sel);
+      }
+      dst[(int64_t)(8 * k + q) * (S / 8) + tg] = Chunk{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+// f32 x [N][heads][d] -> y tile-transposed ([d][S] per tile).  The tile passes
 // through LDS: rows are read as coalesced chunks, scattered element-wise into
 // a [d][S + pad] LDS image, and written back as coalesced chunks of S.
-template <typename E>
-__global__ __launch_bounds__(kThreads) void permute_fwd_t_kernel(DevLayout L,
-                                                                 const E* __restrict__ x,
-                                                                 E* __restrict__ y) {
-  constexpr int VEC = 16 / sizeof(E);            // elements per chunk
+__global__ __launch_bounds__(kThreads) void permute_fwd_t_f32_kernel(DevLayout L,
+                                                                     const float* __restrict__ x,
+                                                                     float* __restrict__ y) {
+  constexpr int VEC = 4;                         // elements per chunk
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  E* lds = reinterpret_cast<E*>(smem_raw);
+  float* lds = reinterpret_cast<float*>(smem_raw);
+  __shared__ int64_t rows[256];
+  const int64_t g = blockIdx.x;
+  tile_rows(L, g, rows);
   const int S = L.S, d = L.d;
   const int ld = S + VEC;                        // padded LDS row (keeps 16-B alignment)
-  const int64_t g = blockIdx.x;
-  const int h = head_of_tile(L, g);
-  const TileExtent e = tile_extent(L, h, (int)(g - L.tile_off[h]));
   const int cpr = d / VEC;                       // chunks per token row
   for (int c = threadIdx.x; c < S * cpr; c += kThreads) {
     const int u = c / cpr, k = c - u * cpr;
-    const int64_t n = token_of_slot(L, e, u);
-    E v[VEC];
-    if (n >= 0) {
-      *reinterpret_cast<Chunk*>(v) = reinterpret_cast<const Chunk*>(x + (n * L.heads + h) * (int64_t)d)[k];
+    const int64_t row = rows[u];
+    float v[VEC];
+    if (row >= 0) {
+      *reinterpret_cast<Chunk*>(v) = reinterpret_cast<const Chunk*>(x + row * (int64_t)d)[k];
     } else {
 #pragma unroll
-      for (int q = 0; q < VEC; ++q) v[q] = E(0);
+      for (int q = 0; q < VEC; ++q) v[q] = 0.f;
     }
 #pragma unroll
     for (int q = 0; q < VEC; ++q) lds[(k * VEC + q) * ld + u] = v[q];
@@ -112,14 +180,13 @@ int launch_permute(const DevLayout& L, int dtype, int dir, const void* x, void* 
   } else if (dir == VEDA_INV) {
     hipLaunchKernelGGL(permute_inv_kernel, dim3(blocks), dim3(kThreads), 0, s, L, cpr,
                        (const Chunk*)x, (Chunk*)y);
+  } else if (dtype == VEDA_F32) {
+    const size_t lds = (size_t)L.d * (L.S + 4) * 4;
+    hipLaunchKernelGGL(permute_fwd_t_f32_kernel, dim3(blocks), dim3(kThreads), lds, s, L,
+                       (const float*)x, (float*)y);
   } else {
-    const size_t lds = (size_t)L.d * (L.S + 16 / esize) * esize;
-    if (dtype == VEDA_F32)
-      hipLaunchKernelGGL(permute_fwd_t_kernel<float>, dim3(blocks), dim3(kThreads), lds, s, L,
-                         (const float*)x, (float*)y);
-    else
-      hipLaunchKernelGGL(permute_fwd_t_kernel<__bf16>, dim3(blocks), dim3(kThreads), lds, s, L,
-                         (const __bf16*)x, (__bf16*)y);
+    hipLaunchKernelGGL(permute_fwd_t_bf16_kernel, dim3(blocks), dim3(kThreads), 0, s, L,
+                       (const Chunk*)x, (Chunk*)y);
   }
   return launch_status();
 }

@@ -10,7 +10,8 @@
 //  2. project: phi = desc W^T + b, batched over (side, head).
 //  3. score:   scores = phi_q phi_k^T, batched over heads.
 // 2 and 3 share one LDS-tiled f32 "C = A B^T" kernel (64x64 tile, 4x4 outputs
-// per lane); both operands are read along their contiguous K dimension.
+// per lane, K steps of 32 fetched one step ahead); both operands are read
+// along their contiguous K dimension.
 #include "veda_internal.hpp"
 
 namespace veda {
@@ -79,44 +80,86 @@ __global__ __launch_bounds__(kPoolThreads) void tripool_pool_kernel(DevLayout L,
 }
 
 // ---- batched f32 C[m][n] = sum_k A[m][k] B[n][k] (+ bias[n]) -------------
-constexpr int BM = 64, BN = 64, BK = 16, kGemmThreads = 256;
+// 64x64 output tile per workgroup, 4x4 outputs per lane, K in steps of 32.
+// Each lane fetches 8 consecutive k of one A row and one B row per step (two
+// 16-byte loads each when VEC: K % 4 == 0 and 16-byte aligned operands), and
+// the next step's values are fetched while the current step is multiplied.
+constexpr int BN = 64, BK = 32, kGemmThreads = 256;
+
+// projection: few, deep (K = 3d) products -> smaller tiles for more workgroups
+constexpr int kProjBM = 32, kScoreBM = 64;
 
 struct GemmArgs {
   const float* A; const float* B; const float* bias; float* C;
   int M, N, K; int64_t lda, ldb, ldc;
 };
 
+template <bool VEC>
+__device__ __forceinline__ void gemm_fetch(const float* __restrict__ src, int64_t ld, int row,
+                                           int rows, int k, int K, float (&v)[8]) {
+  if (row >= rows) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = 0.f;
+    return;
+  }
+  const float* p = src + row * ld + k;
+  if (VEC && k + 8 <= K) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    const float4 y = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = k + c < K ? p[c] : 0.f;
+  }
+}
+
+// BM x 64 output tile (BM = 64: 4x4 outputs per lane; BM = 32: 2x4).
+template <int BM, bool VEC>
 __device__ __forceinline__ void gemm_abt_tile(const GemmArgs& a, int m0, int n0) {
+  constexpr int RM = BM / 16;              // output rows per lane
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
   const int t = threadIdx.x;
-  const int tm = (t / 16) * 4, tn = (t % 16) * 4;
-  float acc[4][4] = {};
+  const int tm = (t / 16) * RM, tn = (t % 16) * 4;
+  const int r = t / 4, kc = (t % 4) * 8;   // fetched row and k offset within the step
+  const bool fa = r < BM;                  // this lane also fetches an A row
+  float acc[RM][4] = {};
+  float va[8], vb[8];
+  if (fa) gemm_fetch<VEC>(a.A, a.lda, m0 + r, a.M, kc, a.K, va);
+  gemm_fetch<VEC>(a.B, a.ldb, n0 + r, a.N, kc, a.K, vb);
   for (int k0 = 0; k0 < a.K; k0 += BK) {
-    // each lane stages 4 elements of A and 4 of B (row = t/4, k = (t%4)*4 + c)
-    const int r = t / 4, kc = (t % 4) * 4;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int kk = k0 + kc + c;
-      const int am = m0 + r, bn = n0 + r;
-      As[kc + c][r] = (am < a.M && kk < a.K) ? a.A[am * a.lda + kk] : 0.f;
-      Bs[kc + c][r] = (bn < a.N && kk < a.K) ? a.B[bn * a.ldb + kk] : 0.f;
+    for (int c = 0; c < 8; ++c) {
+      if (fa) As[kc + c][r] = va[c];
+      Bs[kc + c][r] = vb[c];
     }
     __syncthreads();
+    if (k0 + BK < a.K) {   // next step's values, in flight during the products
+      if (fa) gemm_fetch<VEC>(a.A, a.lda, m0 + r, a.M, k0 + BK + kc, a.K, va);
+      gemm_fetch<VEC>(a.B, a.ldb, n0 + r, a.N, k0 + BK + kc, a.K, vb);
+    }
 #pragma unroll
     for (int kk = 0; kk < BK; ++kk) {
-      float av[4], bv[4];
+      float am[RM];
+      if constexpr (RM == 4) {
+        const float4 av = *reinterpret_cast<const float4*>(&As[kk][tm]);
+        am[0] = av.x; am[1] = av.y; am[2] = av.z; am[3] = av.w;
+      } else {
+        const float2 av = *reinterpret_cast<const float2*>(&As[kk][tm]);
+        am[0] = av.x; am[1] = av.y;
+      }
+      const float4 bv = *reinterpret_cast<const float4*>(&Bs[kk][tn]);
+      const float bn[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { av[i] = As[kk][tm + i]; bv[i] = Bs[kk][tn + i]; }
+      for (int i = 0; i < RM; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(am[i], bn[j], acc[i][j]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < RM; ++i) {
     const int m = m0 + tm + i;
     if (m >= a.M) continue;
 #pragma unroll
@@ -129,6 +172,7 @@ __device__ __forceinline__ void gemm_abt_tile(const GemmArgs& a, int m0, int n0)
 }
 
 // batch = side*heads + h: desc rows of head h -> phi rows of head h.
+template <bool VEC>
 __global__ __launch_bounds__(kGemmThreads) void project_kernel(DevLayout L, int d_e,
                                                                const float* __restrict__ desc,
                                                                const float* __restrict__ wq,
@@ -138,7 +182,7 @@ __global__ __launch_bounds__(kGemmThreads) void project_kernel(DevLayout L, int 
   const int side = blockIdx.z / L.heads, h = blockIdx.z % L.heads;
   const int64_t total = L.tile_off[L.heads];
   const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int m0 = blockIdx.y * kProjBM, n0 = blockIdx.x * BN;
   if (m0 >= n_h || n0 >= d_e) return;
   const int K = 3 * L.d;
   GemmArgs a;
@@ -148,16 +192,17 @@ __global__ __launch_bounds__(kGemmThreads) void project_kernel(DevLayout L, int 
   a.bias = b ? b + (int64_t)h * d_e : nullptr;
   a.C = phi + ((int64_t)side * total + L.tile_off[h]) * d_e;
   a.M = n_h; a.N = d_e; a.K = K; a.lda = K; a.ldb = K; a.ldc = d_e;
-  gemm_abt_tile(a, m0, n0);
+  gemm_abt_tile<kProjBM, VEC>(a, m0, n0);
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(kGemmThreads) void score_kernel(DevLayout L, int d_e,
                                                              const float* __restrict__ phi,
                                                              float* __restrict__ scores) {
   const int h = blockIdx.z;
   const int64_t total = L.tile_off[L.heads];
   const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int m0 = blockIdx.y * kScoreBM, n0 = blockIdx.x * BN;
   if (m0 >= n_h || n0 >= n_h) return;
   GemmArgs a;
   a.A = phi + L.tile_off[h] * d_e;
@@ -165,7 +210,7 @@ __global__ __launch_bounds__(kGemmThreads) void score_kernel(DevLayout L, int d_
   a.bias = nullptr;
   a.C = scores + L.score_off[h];
   a.M = n_h; a.N = n_h; a.K = d_e; a.lda = d_e; a.ldb = d_e; a.ldc = n_h;
-  gemm_abt_tile(a, m0, n0);
+  gemm_abt_tile<kScoreBM, VEC>(a, m0, n0);
 }
 
 }  // namespace
@@ -192,12 +237,26 @@ int launch_tripool_score(const DevLayout& L, int dtype, const void* q, const voi
                          (const __bf16*)q, (const __bf16*)k, desc);
   }
   if (launch_status() != VEDA_OK) return VEDA_ERR_LAUNCH;
-  const unsigned mb = (unsigned)((L.max_tiles + BM - 1) / BM);
-  hipLaunchKernelGGL(project_kernel, dim3((d_e + BN - 1) / BN, mb, 2 * L.heads),
-                     dim3(kGemmThreads), 0, s, L, d_e, desc, wq, wk, bq, bk, phi);
+  const unsigned mbp = (unsigned)((L.max_tiles + kProjBM - 1) / kProjBM);
+  const unsigned mb = (unsigned)((L.max_tiles + kScoreBM - 1) / kScoreBM);
+  // 16-byte loads need 16-byte aligned rows: K % 4 == 0 and aligned bases
+  auto al = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  const bool pvec = al(desc) && al(wq) && al(wk);   // K = 3d is a multiple of 4
+  const bool svec = d_e % 4 == 0 && al(phi);
+  const dim3 pgrid((d_e + BN - 1) / BN, mbp, 2 * L.heads);
+  if (pvec)
+    hipLaunchKernelGGL(project_kernel<true>, pgrid, dim3(kGemmThreads), 0, s, L, d_e, desc, wq, wk,
+                       bq, bk, phi);
+  else
+    hipLaunchKernelGGL(project_kernel<false>, pgrid, dim3(kGemmThreads), 0, s, L, d_e, desc, wq,
+                       wk, bq, bk, phi);
   if (launch_status() != VEDA_OK) return VEDA_ERR_LAUNCH;
-  hipLaunchKernelGGL(score_kernel, dim3(mb, mb, L.heads), dim3(kGemmThreads), 0, s, L, d_e,
-                     phi, scores);
+  if (svec)
+    hipLaunchKernelGGL(score_kernel<true>, dim3(mb, mb, L.heads), dim3(kGemmThreads), 0, s, L,
+                       d_e, phi, scores);
+  else
+    hipLaunchKernelGGL(score_kernel<false>, dim3(mb, mb, L.heads), dim3(kGemmThreads), 0, s, L,
+                       d_e, phi, scores);
   return launch_status();
 }
 
