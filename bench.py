@@ -108,14 +108,27 @@ def map_flops(n_sub_per_head, L, S, d):
     return sum(2.0 * S * S * d * n_sub_per_head[h] * L.n(h) for h in range(L.num_heads))
 
 
+def tile_real_counts(L):
+    """Real (non-padding) slots of every tile, in global tile order."""
+    out = []
+    for h in range(L.num_heads):
+        pt, ph, pw = (int(x) for x in L.tile_shape[h])
+        nT, nH, nW = (int(x) for x in L.tile_grid[h])
+        lt = np.minimum(pt, L.T - np.arange(nT) * pt)
+        lh = np.minimum(ph, L.H - np.arange(nH) * ph)
+        lw = np.minimum(pw, L.W - np.arange(nW) * pw)
+        out.append((lt[:, None, None] * lh[None, :, None] * lw[None, None, :]).reshape(-1))
+    return np.concatenate(out).astype(np.int64)
+
+
 class Bench:
-    def __init__(self, name: str, sparsity: int, seed: int = 0):
+    def __init__(self, name: str, sparsity: int, seed: int = 0, T=None, wl=None):
         import torch
 
         import tile_sparse_attention_head_amd as V
         import workloads
         self.torch, self.V = torch, V
-        self.wl = workloads.make(name, seed)
+        self.wl = workloads.make(name, seed, T) if wl is None else wl
         cfg = self.wl.config
         self.cfg = cfg
         self.sparsity = sparsity
@@ -185,7 +198,20 @@ class Bench:
             "map": ("mfma", self.flops_d, "map_stats_kernel"),
         }
 
-    def run(self, steps: int, warmup: int, with_map=True):
+    def valid_flops_c(self):
+        """4*d*sum over kept pairs of |real query slots| * |real key slots|."""
+        L, d = self.L, self.cfg.head_dim
+        cnt = tile_real_counts(L)
+        rp = self.layer.row_ptr.cpu().numpy().astype(np.int64)
+        ci = self.layer.col_idx.cpu().numpy().astype(np.int64)[: rp[-1]]
+        rows = np.repeat(np.arange(L.total_tiles), np.diff(rp))
+        base = np.repeat(np.asarray(L.tile_off[: L.num_heads], dtype=np.int64),
+                         [L.n(h) for h in range(L.num_heads)])
+        return 4.0 * d * float(np.sum(cnt[rows] * cnt[base[rows] + ci]))
+
+    def run(self, steps: int, warmup: int, with_map=True, flush=None):
+        """Time `steps` steps after `warmup` untimed ones; with `flush` (a
+        device buffer) it is overwritten before every step (cold L2/MALL)."""
         torch = self.torch
         for _ in range(warmup):
             self.step(with_map=with_map)
@@ -193,6 +219,8 @@ class Bench:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
+            if flush is not None:
+                flush.fill_(i)
             self.step(ev[i], with_map=with_map)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps * 1e3
@@ -242,6 +270,41 @@ def cpu_baseline(wl, sparsity: int, budget_s: float = 12.0):
                       f"{cfg.map_subset_pct}% query-tile subset), {dt:.1f} s, fp64 numpy"}
 
 
+def sweep():
+    """Length sweep of the attention at 95 % tile sparsity against the same
+    kernel at 0 % (dense), on the 720P layer's 24-head heterogeneous draw at
+    T = 9, 18, 36, 61 frames (32,400 .. 219,600 tokens); then the map on the
+    Waver-12B 720P 121-frame layer's 10 % query-tile subset."""
+    import torch
+    import workloads
+    out = {"sweep": [], "map": None}
+    for T in (9, 18, 36, 61):
+        wl = workloads.make("long-720p-241f", 0, T)
+        rec = {"T": T, "tokens": int(wl.q.shape[0])}
+        for sp in (95, 0):
+            b = Bench("long-720p-241f", sp, wl=wl)
+            _, sm, _ = b.run(3 if sp else 2, 1, with_map=False)
+            d = dict(zip(b.stages, [float(x) for x in sm]))
+            rec[f"s{sp}"] = {"ms_per_layer": sum(d[n] for n in b.stages if n != "map"),
+                             "attn_ms": d["sparse_attn"],
+                             "attn_tflops": b.flops_c / (d["sparse_attn"] * 1e-3) / 1e12,
+                             "kept_pairs": b.pairs}
+            del b
+            torch.cuda.empty_cache()
+        rec["density"] = rec["s95"]["kept_pairs"] / rec["s0"]["kept_pairs"]
+        rec["attn_speedup_vs_dense"] = rec["s0"]["attn_ms"] / rec["s95"]["attn_ms"]
+        out["sweep"].append(rec)
+        print(json.dumps({"progress": rec}), file=sys.stderr, flush=True)
+        del wl
+    b = Bench("waver12b-720p-121f", 90)
+    _, sm, _ = b.run(3, 1)
+    d = dict(zip(b.stages, [float(x) for x in sm]))
+    out["map"] = {"workload": "waver12b-720p-121f", "subset_tiles": int(sum(b.n_sub)),
+                  "ms": d["map"], "tflops_one_qk": b.flops_d / (d["map"] * 1e-3) / 1e12,
+                  "frac_peak": b.flops_d / (d["map"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +317,10 @@ def main():
                     help="skip the 95 %% and 0 %% (dense) context runs")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one torch copy of this many MiB (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: attention at 95%% and 0%% over the 720P "
+                         "241-frame layer at T = 9, 18, 36, 61 frames, and the map on the "
+                         "Waver-12B 720P 121-frame layer; prints one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path shards by "
@@ -265,8 +332,17 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
 
+    if args.sweep:
+        print(json.dumps(sweep()))
+        return
+
     b = Bench(args.workload, args.sparsity)
     wall_ms, stage_ms, per = b.run(args.steps, args.warmup)
+    pct = {n: [float(x) for x in np.percentile(per[:, i], [10, 50, 90])]
+           for i, n in enumerate(b.stages)}
+    layer_steps = per[:, [i for i, n in enumerate(b.stages) if n != "map"]].sum(axis=1)
+    pct["layer"] = [float(x) for x in np.percentile(layer_steps, [10, 50, 90])]
+    valid_c = b.valid_flops_c()
     names = b.stages
     st = dict(zip(names, [float(x) for x in stage_ms]))
     layer_ms = sum(st[n] for n in names if n != "map")
@@ -310,6 +386,15 @@ def main():
         if "sparsity_0" in context:
             context["attn_speedup_vs_dense"] = context["sparsity_0"]["attn_ms"] / attn_ms
             context["density"] = b.pairs / context["sparsity_0"]["kept_pairs"]
+        # cold caches: a 512 MiB buffer is overwritten before every step, which
+        # evicts L2 and MALL (256 MiB) between steps
+        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        _, smc, _ = b.run(max(3, args.steps // 2), 1, flush=flush)
+        dc = dict(zip(names, [float(x) for x in smc]))
+        context["cold_cache"] = {"ms_per_layer": sum(dc[n] for n in names if n != "map"),
+                                 "attn_ms": dc["sparse_attn"], "map_ms": dc["map"]}
+        del flush
+        torch.cuda.empty_cache()
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1024 * 1024 // 4
@@ -336,6 +421,10 @@ def main():
         "ms_per_layer": layer_ms,
         "layer_tflops_effective": b.flops_c / (layer_ms * 1e-3) / 1e12,
         "stage_ms": st,
+        "stage_ms_p10_p50_p90": pct,
+        "attn_valid_tokens": {
+            "flops": valid_c, "padding_fraction": 1.0 - valid_c / b.flops_c,
+            "tflops": valid_c / (attn_ms * 1e-3) / 1e12},
         "roofline": roofline,
         "kernels": kernels,
         "context": context,
