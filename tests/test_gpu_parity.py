@@ -306,6 +306,24 @@ def test_attention_bench_config_sampled():
     _say(f"  max-abs {worst:.3e} mean-abs {mean:.3e}")
 
 
+@pytest.mark.parametrize("name,sparsity,T", [("wan14b-720p-81f", 95, None),
+                                             ("long-720p-241f", 95, 9)])
+def test_attention_large_heterogeneous_sampled(name, sparsity, T):
+    """Full-size heterogeneous layers (per-head tile shapes drawn from the
+    seed): the Wan-14B-like 720P layer (40 heads) and the 720P 241-frame
+    layer's 24-head draw cut to 9 frames.  Every head, two seeded query
+    tiles plus its last (boundary) tile."""
+    _say(f"attention {name} T={T} {sparsity}% sampled")
+    r = Run(name, sparsity=sparsity, T=T)
+    assert len(set(r.wl.tile_shapes)) > 1
+    r.forward()
+    rng = np.random.default_rng(5)
+    sample = [np.sort(np.append(rng.choice(r.L.n(h) - 1, size=2, replace=False), r.L.n(h) - 1))
+              for h in range(r.heads)]
+    worst, mean = _check_attention(r, sample)
+    _say(f"  max-abs {worst:.3e} mean-abs {mean:.3e}")
+
+
 def test_attention_properties_full_size():
     """At full size: V = 1 gives O = 1 on every real row; outputs finite."""
     _say("attention properties")
@@ -410,6 +428,42 @@ def test_maxpool_map_bench_config_subset():
     subset = workloads.draw_subset(r.wl, [r.L.n(h) for h in range(r.heads)])
     subset = [s[:4] for s in subset]           # oracle cost: 4 query tiles per head
     _check_map(r, subset)
+
+
+def test_maxpool_map_waver12b_sampled():
+    """Waver-12B-like 720P 121-frame layer (32 heterogeneous heads): the map
+    over the whole seeded 10 % subset (the benchmark's launch shape, 3000+
+    subset tiles), checked against the oracle on one subset tile of each of
+    four heads with different tile shapes."""
+    _say("map waver12b 10% sampled")
+    import workloads
+    torch = need_gpu()
+    r = Run("waver12b-720p-121f")
+    r.layer.permute_inputs(r.q, r.k, r.v)
+    L = r.L
+    subset = workloads.draw_subset(r.wl, [L.n(h) for h in range(r.heads)])
+    flat = np.concatenate([int(L.tile_off[h]) + s for h, s in enumerate(subset)]).astype(np.int32)
+    lse, mp = r.layer.maxpool_map(torch.from_numpy(flat).cuda(), r.sm_scale)
+    torch.cuda.synchronize()
+    lse = host(lse).reshape(-1, r.S)
+    mp = host(mp).reshape(-1, L.max_tiles)
+    starts = np.concatenate([[0], np.cumsum([len(s) for s in subset])])
+    first = {}                             # the first head of each tile shape
+    for h in range(r.heads):
+        first.setdefault(r.wl.tile_shapes[h], h)
+    heads = list(first.values())[:4]
+    assert len(heads) > 1
+    for h in heads:
+        ht = r.tilings[h]
+        i = len(subset[h]) // 2
+        qp, kp, _ = r.head_perm(h)
+        rl, rm = oracle.maxpool_map(qp, kp, ht.valid, r.S, subset[h][i:i + 1], r.sm_scale)
+        row = starts[h] + i
+        got = mp[row]
+        assert np.all(got[ht.n:] == 0)
+        assert np.all(np.abs(got[:ht.n] - rm[0]) <= np.maximum(1e-3 * rm[0], 1e-7)), h
+        sel = ~np.isnan(rl)
+        assert np.abs(lse[row][sel] - rl[sel]).max() <= LSE_TOL, h
 
 
 def test_maxpool_map_edges():
