@@ -162,26 +162,28 @@ __device__ __forceinline__ int cut_of(const TileExtent& e) {
 // [cut][half][b][hf] holds the 16 accumulator elements of 32-key block b of
 // step `half` of a tile with that cut, for lanes of half hf (element i is
 // key 16(i/8) + 8hf + i%8).  Built once per workgroup.
-template <int SPT>
+// NCUT = 9 adds cut 8: every slot masked (a tile that contributes nothing).
+template <int SPT, int NCUT = 8>
 struct BiasTable {
-  f32x4 v[8][SPT][2][2][4];
+  f32x4 v[NCUT][SPT][2][2][4];
 };
 
-template <int SPT>
-__device__ __forceinline__ void build_bias_table(BiasTable<SPT>& bt, const DevLayout& L, int h,
-                                                 int tid, int nthreads) {
+template <int SPT, int NCUT>
+__device__ __forceinline__ void build_bias_table(BiasTable<SPT, NCUT>& bt, const DevLayout& L,
+                                                 int h, int tid, int nthreads) {
   const int pt = L.shape[h][0], ph = L.shape[h][1], pw = L.shape[h][2];
   const int et = L.T - (L.grid[h][0] - 1) * pt;   // extent of the last tile along t
   const int eh = L.H - (L.grid[h][1] - 1) * ph;
   const int ew = L.W - (L.grid[h][2] - 1) * pw;
   float* flat = reinterpret_cast<float*>(&bt);
-  constexpr int ENTRIES = 8 * SPT * 2 * 2 * 16;
+  constexpr int ENTRIES = NCUT * SPT * 2 * 2 * 16;
   for (int x = tid; x < ENTRIES; x += nthreads) {
     const int i = x & 15, hf = (x >> 4) & 1, b = (x >> 5) & 1, half = (x >> 6) % SPT;
     const int cut = (x >> 6) / SPT;
     const int u = half * 64 + 32 * b + 16 * (i >> 3) + 8 * hf + (i & 7);   // slot in tile
     const int dw = u % pw, r = u / pw, dh = r % ph, dt = r / ph;
-    const bool ok = (!(cut & 4) || dt < et) && (!(cut & 2) || dh < eh) && (!(cut & 1) || dw < ew);
+    const bool ok = cut < 8 && (!(cut & 4) || dt < et) && (!(cut & 2) || dh < eh) &&
+                    (!(cut & 1) || dw < ew);
     flat[x] = ok ? 0.f : -INFINITY;
   }
 }

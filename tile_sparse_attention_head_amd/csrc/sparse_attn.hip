@@ -27,7 +27,11 @@
 // bf16, f32 accumulation.  The running maximum is raised only when a new
 // logit exceeds it by more than 2^8, so the accumulator is rescaled rarely;
 // the result is the same softmax (numerator and denominator share one
-// reference).  The CSR row is read with scalar loads.
+// reference).  The CSR row sits in one register, 64 entries at a time (lane
+// l: entry l, with its tile's cut), and each step reads its entries with
+// v_readlane: no memory access and no integer division per step.  An entry
+// outside [0, n_tiles) becomes a tile whose keys are all masked, which leaves
+// the result exactly as if it were skipped.
 //
 // Workgroups are ordered XCD-aware and head-major, so the query tiles running
 // together on one XCD are spatial neighbours whose kept key tiles overlap in
@@ -55,21 +59,6 @@ struct Pipe {
   static_assert(S % SK == 0, "tile must hold whole steps");
 };
 
-// Walks the valid entries of a CSR row: one cursor per copy stream.
-struct Cursor {
-  cint32* col;
-  int pos, end, n_h, j;
-  __device__ __forceinline__ void next() {
-    ++pos;
-    while (pos < end) {
-      const int c = col[pos];
-      if (c >= 0 && c < n_h) { j = c; return; }
-      ++pos;
-    }
-    j = 0;
-  }
-};
-
 template <int D, int S>
 __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -87,7 +76,7 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char k1[KB::BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v0[VB::BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v1[VB::BYTES];
-  __shared__ BiasTable<SPT> btab;
+  __shared__ BiasTable<SPT, 9> btab;
 
   const int64_t g = xcd_remap(blockIdx.x, gridDim.x);
   const int h = head_of_tile(L, g);
@@ -102,15 +91,11 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   load_q_regs<D>(qr, q + qrow * D, hf);
 
   cint32* rp = (cint32*)row_ptr;
-  cint32* ci = (cint32*)col_idx;
   int beg = rp[g], end = rp[g + 1];
   if (end < beg) end = beg;
-  int kept = 0;
-  for (int p = beg; p < end; ++p) {
-    const int c = ci[p];
-    kept += (c >= 0 && c < n_h) ? 1 : 0;
-  }
-  const int N = kept * SPT;   // steps
+  // every CSR entry is a tile of SPT steps; an entry outside [0, n_h) is a
+  // tile whose keys are all masked, which leaves the result as if skipped
+  const int N = (end - beg) * SPT;   // steps
 
   // the head's K and V^T tiles as buffer resources (raw, bounds = the head)
   const auto krs = make_rsrc(reinterpret_cast<const unsigned char*>(k) + head_base * TILE,
@@ -121,33 +106,25 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   KB::offsets(koff, wave, lane);
   VB::offsets(voff, wave, lane);
 
-  // Three walks over the row's kept tiles, one step (SK keys) at a time:
-  // copies of K run two steps ahead of the logits, copies of V^T with them.
-  Cursor kc{ci, beg - 1, end, n_h, 0}, vc = kc, qc = kc;
-  uint32_t kg_last = 0;
-  int kstep = 0, vstep = 0, qstep = 0, qcut = 0;
-  // HBM address of the next K step / V^T step to copy (cursors advance)
-  auto next_k = [&]() {
-    if (kstep % SPT == 0) kc.next();
-    const uint32_t r = (uint32_t)(kc.j * TILE + (kstep % SPT) * P::KSTEP);
-    ++kstep;
-    return r;
+  // A window of 64 CSR entries in one register: lane l holds entry wbase + l
+  // as col | cut << 16 (cut 8 for an entry outside [0, n_h)).  Steps read
+  // their tile with v_readlane: no memory access per step.
+  int wbase = 0, win = 0;
+  auto load_window = [&](int base) {
+    const int p = beg + base + lane;
+    const int c = p < end ? col_idx[p] : -1;
+    const bool ok = c >= 0 && c < n_h;
+    const int cut = ok ? cut_of(tile_extent(L, h, c)) : 8;
+    win = (ok ? c : 0) | (cut << 16);
+    wbase = base;
   };
-  auto next_v = [&]() {
-    if (vstep % SPT == 0) vc.next();
-    const uint32_t r = (uint32_t)(vc.j * TILE + (vstep % SPT) * (P::SK * 2));
-    ++vstep;
-    return r;
+  auto entry = [&](int t) { return __builtin_amdgcn_readlane(win, t / SPT - wbase); };
+  auto k_off = [&](int e, int t) { return (uint32_t)((e & 0xffff) * TILE + (t % SPT) * P::KSTEP); };
+  auto v_off = [&](int e, int t) {
+    return (uint32_t)((e & 0xffff) * TILE + (t % SPT) * (P::SK * 2));
   };
-  // mask row of the next step whose logits are computed
-  auto next_bias = [&]() -> const f32x4* {
-    if (qstep % SPT == 0) {
-      qc.next();
-      qcut = cut_of(tile_extent(L, h, qc.j));
-    }
-    const f32x4* r = &btab.v[qcut][qstep % SPT][0][hf][0];
-    ++qstep;
-    return r;
+  auto bias_of = [&](int e, int t) -> const f32x4* {
+    return &btab.v[e >> 16][t % SPT][0][hf][0];
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -172,14 +149,17 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     const unsigned char* ksrc = PAR ? k0 : k1;
     const unsigned char* vsrc = PAR ? v0 : v1;
 
-    // mask rows first: no copy of this step is in flight yet
-    if constexpr (QK) load_bias(snext, next_bias());
     // K(s+2) over K(s) and V(s) over V(s-2), issued spread over the slots
-    // below; with no step s+2 the K rounds re-copy the last K step into the
-    // free slot
-    const uint32_t kgs = s + 2 < N ? next_k() : kg_last;
-    kg_last = kgs;
-    const uint32_t vgs = next_v();
+    // below; with no step s+2 the K rounds re-copy K(s) into its own, no
+    // longer read, slot.  The window moves on when step s+2 leaves it (no
+    // copy is in flight at this point).
+    if ((s + 2) / SPT - wbase >= 64) load_window((s + 2) / SPT - 2);
+    const int es = entry(s);
+    const uint32_t kgs = s + 2 < N ? k_off(entry(s + 2), s + 2) : k_off(es, s);
+    const uint32_t vgs = v_off(es, s);
+    // mask rows of step s+2, loaded into the logits registers of step s once
+    // its softmax has read them (the last slots below)
+    const f32x4* bias2 = bias_of(s + 2 < N ? entry(s + 2) : 0, s + 2);
     unsigned char* kdst = PAR ? k1 : k0;
     unsigned char* vdst = PAR ? v1 : v0;
     constexpr int RW = KB::PER_WAVE + VB::PER_WAVE;
@@ -267,6 +247,7 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
           asm volatile("" : "+v"(psum0), "+v"(psum1));
         }
       });
+      if constexpr (i == 5 + (15 * (NSLOT - 7)) / 16 + 1) load_bias(scur, bias2);
       __builtin_amdgcn_sched_barrier(0);
     });
 
@@ -289,17 +270,15 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   using Z = std::integral_constant<int, 0>;
   using O1 = std::integral_constant<int, 1>;
   if (N > 0) {
-    kg_last = next_k();
-    KB::copy(krs, kg_last, k0, koff, wave);
-    if (N > 1) {
-      kg_last = next_k();
-      KB::copy(krs, kg_last, k1, koff, wave);
-    }
-    build_bias_table<SPT>(btab, L, h, tid, 2 * S);
+    load_window(0);
+    KB::copy(krs, k_off(entry(0), 0), k0, koff, wave);
+    if (N > 1) KB::copy(krs, k_off(entry(1), 1), k1, koff, wave);
+    build_bias_table<SPT, 9>(btab, L, h, tid, 2 * S);
     wait_all();
     __syncthreads();
-    // logits of step 0
-    load_bias(sA, next_bias());
+    // logits of step 0; mask rows of step 1 (later ones come from the slots)
+    load_bias(sA, bias_of(entry(0), 0));
+    if (N > 1) load_bias(sB, bias_of(entry(1), 1));
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       sA[0] = mfma32(KB::read(k0, n, 2 * s + hf), qr[s], sA[0]);
