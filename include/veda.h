@@ -136,6 +136,31 @@ int veda_tripool_score(const veda_layout* L, int32_t dtype, const void* q_perm,
                        const float* b_q, const float* b_k, int32_t d_e,
                        float* desc, float* phi, float* scores, void* stream);
 
+/* The gather of Q or K fused with TripPool (Veda §2.1 TripPool descriptor,
+ * §2.2 head-aware tiling): one read of x gives both
+ *   y     tile order, exactly as veda_tile_permute FWD writes it
+ *   desc  f32 [tile_off[num_heads]][3*head_dim] (output): per tile
+ *         [mean | max | min] of each channel over the tile's real slots,
+ *         bit-identical to the desc rows veda_tripool_score writes
+ * For a layer, call it for Q with desc = D and for K with
+ * desc = D + tile_off[num_heads]*3*head_dim, where D is the [2][tiles][3d]
+ * buffer veda_tile_score reads.  dtype VEDA_BF16 or VEDA_F32.  Supported:
+ * head_dim in {64, 128}, tile_size <= 256, x and y 16-byte aligned
+ * (VEDA_ERR_UNSUPPORTED otherwise).  x, y and desc must not overlap. */
+int veda_tile_permute_pool(const veda_layout* L, int32_t dtype, const void* x, void* y,
+                           float* desc, void* stream);
+
+/* The projection and score half of veda_tripool_score (Veda §2.1), from
+ * descriptors already computed (by veda_tile_permute_pool or
+ * veda_tripool_score):
+ *  desc    f32 [2][tile_off[num_heads]][3*head_dim]: side 0 Q, side 1 K
+ *  w_q, w_k, b_q, b_k, d_e, phi, scores  as in veda_tripool_score
+ * Same kernels and results as veda_tripool_score.  Supported: head_dim in
+ * {64, 128}, 1 <= d_e <= 256. */
+int veda_tile_score(const veda_layout* L, const float* desc, const float* w_q,
+                    const float* w_k, const float* b_q, const float* b_k, int32_t d_e,
+                    float* phi, float* scores, void* stream);
+
 /* Tile selection (Veda lay summary and §5; Veda news: 95 % sparsity): per
  * query tile row, keep the k_per_head[hd] largest scores; equal scores prefer
  * the lower tile index, -0.0 equals +0.0, NaN ranks below every number.
@@ -169,6 +194,19 @@ int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k
                          const void* vt_perm, const int32_t* row_ptr,
                          const int32_t* col_idx, float sm_scale, void* o_perm,
                          float* lse, void* stream);
+
+/* veda_sparse_attn_fwd with the inverse permutation folded into its
+ * epilogue (Veda §2.3 tile-skipping kernel, §2.2 tiles): the same O values,
+ * written straight to token order.
+ *  o       bf16 [N][num_heads][head_dim] (output): every element is written
+ *          (each token is a real slot of exactly one tile per head); must not
+ *          overlap the inputs
+ *  lse     as in veda_sparse_attn_fwd (tile-slot order), or NULL
+ * Every other argument, result and limit as veda_sparse_attn_fwd. */
+int veda_sparse_attn_fwd_tokens(const veda_layout* L, const void* q_perm, const void* k_perm,
+                                const void* vt_perm, const int32_t* row_ptr,
+                                const int32_t* col_idx, float sm_scale, void* o,
+                                float* lse, void* stream);
 
 /* Max-pooled attention map, the distillation target (Veda §2.1 target
  * construction; Veda §2.3: two passes over a random subset of query tiles).

@@ -68,8 +68,16 @@ class Run:
         self.tilings = [oracle.HeadTiling(self.T, self.H, self.W, s) for s in self.wl.tile_shapes]
 
     def forward(self):
-        out = self.layer.forward(self.q, self.k, self.v, self.w, self.w, self.sm_scale)
-        self.V.lib()
+        """The layer one method step per call: tile-order O stays in
+        layer.o_perm, and the inverse permutation gives the returned O."""
+        out = self.layer.forward_unfused(self.q, self.k, self.v, self.w, self.w, self.sm_scale)
+        need_gpu().cuda.synchronize()
+        return out
+
+    def forward_fused(self, out=None):
+        """The fused layer (gather + TripPool, score, select, attention writing
+        token-order O); layer.o_perm is not written."""
+        out = self.layer.forward(self.q, self.k, self.v, self.w, self.w, self.sm_scale, out=out)
         need_gpu().cuda.synchronize()
         return out
 

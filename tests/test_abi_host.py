@@ -144,6 +144,33 @@ def test_device_calls_reject_before_launch(lib):
         assert lib.veda_sparse_attn_fwd(Lp, fake, fake, fake, fake, fake, bad, fake, None, None) == -1
     L3 = V.veda_layout_init(5, 9, 20, 96, 128, [(8, 4, 4)])
     assert lib.veda_sparse_attn_fwd(ctypes.byref(L3), fake, fake, fake, fake, fake, 0.1, fake, None, None) == -2
+    # token-order attention: same checks, plus an output overlapping an input
+    A = lib.veda_sparse_attn_fwd_tokens
+    assert A(Lp, fake, fake, None, fake, fake, 0.1, fake * 64, None, None) == -1
+    for bad in (float("nan"), 0.0, -0.1, float("inf")):
+        assert A(Lp, fake, fake * 16, fake * 32, fake, fake, bad, fake * 64, None, None) == -1
+    assert A(ctypes.byref(L3), fake, fake * 16, fake * 32, fake, fake, 0.1, fake * 64, None,
+             None) == -2
+    assert A(Lp, fake, fake * 16, fake * 32, fake, fake, 0.1, fake * 64 + 8, None, None) == -2
+    assert A(Lp, fake, fake * 16, fake * 32, fake, fake, 0.1, fake + 4096, None, None) == -1
+    # fused gather + TripPool: nulls, bad dtype, head_dim outside {64, 128},
+    # misalignment, overlaps
+    P = lib.veda_tile_permute_pool
+    assert P(Lp, 0, None, fake * 16, fake * 32, None) == -1
+    assert P(Lp, 0, fake, fake * 16, None, None) == -1
+    assert P(Lp, 5, fake, fake * 16, fake * 32, None) == -1
+    assert P(ctypes.byref(L3), 0, fake, fake * 16, fake * 32, None) == -2
+    assert P(Lp, 0, fake + 8, fake * 16, fake * 32, None) == -2
+    assert P(Lp, 0, fake, fake + 4096, fake * 32, None) == -1
+    assert P(Lp, 0, fake, fake * 16, fake * 16 + 64, None) == -1
+    assert P(ctypes.byref(L4), 0, fake, fake * 64, fake * 128, None) == -2
+    # projection + score from descriptors: null weights, bad d_e
+    TS = lib.veda_tile_score
+    assert TS(Lp, fake, None, fake, None, None, 128, fake, fake, None) == -1
+    assert TS(Lp, None, fake, fake, None, None, 128, fake, fake, None) == -1
+    assert TS(Lp, fake, fake, fake, None, None, 0, fake, fake, None) == -1
+    assert TS(Lp, fake, fake, fake, None, None, 999, fake, fake, None) == -2
+    assert TS(ctypes.byref(L3), fake, fake, fake, None, None, 96, fake, fake, None) == -2
     # map: negative count, nulls, bad scale, missing / short / misaligned workspace
     ws = ctypes.c_int64(0)
     assert lib.veda_oracle_maxpool_map_workspace(Lp, 3, ctypes.byref(ws)) == 0

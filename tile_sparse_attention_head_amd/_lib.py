@@ -85,9 +85,13 @@ def lib() -> ctypes.CDLL:
         "veda_tile_permute": (c_i32, [P, c_i32, c_i32, c_vp, c_vp, c_vp]),
         "veda_tripool_score": (c_i32, [P, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                        c_vp, c_vp, c_vp, c_vp]),
+        "veda_tile_permute_pool": (c_i32, [P, c_i32, c_vp, c_vp, c_vp, c_vp]),
+        "veda_tile_score": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
         "veda_select_tiles": (c_i32, [P, c_vp, ctypes.POINTER(c_i32), c_vp, c_vp, c_vp]),
         "veda_sparse_attn_fwd": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_vp, c_vp,
                                          c_vp]),
+        "veda_sparse_attn_fwd_tokens": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_vp,
+                                                c_vp, c_vp]),
         "veda_oracle_maxpool_map": (c_i32, [P, c_vp, c_vp, c_f32, c_vp, c_i32, c_vp, c_i64,
                                             c_vp, c_vp, c_vp]),
         "veda_oracle_maxpool_map_workspace": (c_i32, [P, c_i32, ctypes.POINTER(c_i64)]),
@@ -216,6 +220,36 @@ def veda_tripool_score(L: veda_layout, q_perm, k_perm, w_q, w_k, desc, phi, scor
            "veda_tripool_score")
 
 
+def veda_tile_permute_pool(L: veda_layout, x, y, desc, stream=None) -> None:
+    """Gather x (token order) into y (tile order) and write the tiles'
+    TripPool descriptors to desc ([tiles][3*head_dim] f32)."""
+    torch = _torch()
+    dt = _code(x)
+    px = _dev(x, "x", (torch.bfloat16, torch.float32), tokens_numel(L))
+    py = _dev(y, "y", x.dtype, tiles_numel(L))
+    pd = _dev(desc, "desc", torch.float32, L.total_tiles * 3 * L.head_dim)
+    _check(lib().veda_tile_permute_pool(ctypes.byref(L), dt, px, py, pd, _stream(stream)),
+           "veda_tile_permute_pool")
+
+
+def veda_tile_score(L: veda_layout, desc, w_q, w_k, phi, scores, b_q=None, b_k=None,
+                    stream=None) -> None:
+    """Projection and tile scores from descriptors desc [2][tiles][3*head_dim]."""
+    torch = _torch()
+    f32 = torch.float32
+    H, d = L.num_heads, L.head_dim
+    d_e = int(w_q.shape[1])
+    if tuple(w_q.shape) != (H, d_e, 3 * d) or tuple(w_k.shape) != (H, d_e, 3 * d):
+        raise ValueError("w_q/w_k must be [heads][d_e][3*head_dim]")
+    args = [_dev(desc, "desc", f32, 2 * L.total_tiles * 3 * d),
+            _dev(w_q, "w_q", f32, H * d_e * 3 * d), _dev(w_k, "w_k", f32, H * d_e * 3 * d),
+            _dev(b_q, "b_q", f32, H * d_e, True), _dev(b_k, "b_k", f32, H * d_e, True)]
+    outs = [_dev(phi, "phi", f32, 2 * L.total_tiles * d_e),
+            _dev(scores, "scores", f32, L.total_scores)]
+    _check(lib().veda_tile_score(ctypes.byref(L), *args, d_e, *outs, _stream(stream)),
+           "veda_tile_score")
+
+
 def csr_nnz(L: veda_layout, k_per_head: Sequence[int]) -> int:
     return sum(L.n(h) * int(k_per_head[h]) for h in range(L.num_heads))
 
@@ -247,6 +281,23 @@ def veda_sparse_attn_fwd(L: veda_layout, q_perm, k_perm, vt_perm, row_ptr, col_i
     _check(lib().veda_sparse_attn_fwd(ctypes.byref(L), *args, float(sm_scale), po, pl,
                                       _stream(stream)),
            "veda_sparse_attn_fwd")
+
+
+def veda_sparse_attn_fwd_tokens(L: veda_layout, q_perm, k_perm, vt_perm, row_ptr, col_idx,
+                                sm_scale: float, o, lse=None, stream=None) -> None:
+    """As veda_sparse_attn_fwd, with O written in token order [N][heads][d]."""
+    torch = _torch()
+    bf = torch.bfloat16
+    n = tiles_numel(L)
+    args = [_dev(q_perm, "q_perm", bf, n), _dev(k_perm, "k_perm", bf, n),
+            _dev(vt_perm, "vt_perm", bf, n),
+            _dev(row_ptr, "row_ptr", torch.int32, L.total_tiles + 1),
+            _dev(col_idx, "col_idx", torch.int32, 0)]
+    po = _dev(o, "o", bf, tokens_numel(L))
+    pl = _dev(lse, "lse", torch.float32, L.total_tiles * L.tile_size, True)
+    _check(lib().veda_sparse_attn_fwd_tokens(ctypes.byref(L), *args, float(sm_scale), po, pl,
+                                             _stream(stream)),
+           "veda_sparse_attn_fwd_tokens")
 
 
 def veda_oracle_maxpool_map_workspace(L: veda_layout, n_sub: int) -> int:

@@ -114,6 +114,40 @@ bool attn_shape_ok(const veda_layout* L) {
   return (L->head_dim == 128 && L->tile_size == 128) || (L->head_dim == 64 && L->tile_size == 64);
 }
 
+// Checks shared by the two attention entry points, plus the debug-mode CSR
+// validation (synchronous).
+int attn_args(const veda_layout* L, const void* q_perm, const void* k_perm, const void* vt_perm,
+              const int32_t* row_ptr, const int32_t* col_idx, float sm_scale, const void* o,
+              void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (q_perm == nullptr || k_perm == nullptr || vt_perm == nullptr || row_ptr == nullptr ||
+      col_idx == nullptr || o == nullptr)
+    return VEDA_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.f) || sm_scale == INFINITY) return VEDA_ERR_INVALID_ARG;
+  if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
+  if (!aligned16(q_perm) || !aligned16(k_perm) || !aligned16(vt_perm) || !aligned16(o))
+    return VEDA_ERR_UNSUPPORTED;
+  if (debug_sync()) {
+    const int64_t rows = L->tile_off[L->num_heads];
+    std::vector<int32_t> rp(rows + 1);
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return VEDA_ERR_LAUNCH;
+    if (hipMemcpy(rp.data(), row_ptr, (rows + 1) * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+      return VEDA_ERR_LAUNCH;
+    if (rp[0] < 0) return VEDA_ERR_BAD_CSR;
+    for (int64_t r = 0; r < rows; ++r)
+      if (rp[r + 1] < rp[r]) return VEDA_ERR_BAD_CSR;
+    std::vector<int32_t> ci(rp[rows]);
+    if (!ci.empty() && hipMemcpy(ci.data(), col_idx, ci.size() * sizeof(int32_t),
+                                 hipMemcpyDeviceToHost) != hipSuccess)
+      return VEDA_ERR_LAUNCH;
+    for (int h = 0; h < L->num_heads; ++h)
+      for (int64_t r = L->tile_off[h]; r < L->tile_off[h + 1]; ++r)
+        for (int32_t p = rp[r]; p < rp[r + 1]; ++p)
+          if (ci[p] < 0 || ci[p] >= L->n_tiles[h]) return VEDA_ERR_BAD_CSR;
+  }
+  return VEDA_OK;
+}
+
 }  // namespace
 }  // namespace veda
 
@@ -178,6 +212,39 @@ int veda_tripool_score(const veda_layout* L, int32_t dtype, const void* q_perm,
                 stream);
 }
 
+int veda_tile_permute_pool(const veda_layout* L, int32_t dtype, const void* x, void* y,
+                           float* desc, void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (dtype != VEDA_BF16 && dtype != VEDA_F32) return VEDA_ERR_INVALID_ARG;
+  if (x == nullptr || y == nullptr || desc == nullptr) return VEDA_ERR_INVALID_ARG;
+  if (L->head_dim != 64 && L->head_dim != 128) return VEDA_ERR_UNSUPPORTED;
+  if (L->tile_size > 256) return VEDA_ERR_UNSUPPORTED;   // per-tile row table in LDS
+  if (!aligned16(x) || !aligned16(y)) return VEDA_ERR_UNSUPPORTED;
+  const int esize = dtype == VEDA_F32 ? 4 : 2;
+  const size_t tok = (size_t)L->T * L->H * L->W * L->num_heads * L->head_dim * esize;
+  const size_t til = (size_t)L->tile_off[L->num_heads] * L->tile_size * L->head_dim * esize;
+  const size_t dsc = (size_t)L->tile_off[L->num_heads] * 3 * L->head_dim * 4;
+  if (!disjoint(x, tok, y, til) || !disjoint(x, tok, desc, dsc) || !disjoint(y, til, desc, dsc))
+    return VEDA_ERR_INVALID_ARG;
+  const DevLayout dl = make_dev_layout(L);
+  return finish(launch_permute_pool(dl, dtype, x, y, desc, (hipStream_t)stream), stream);
+}
+
+int veda_tile_score(const veda_layout* L, const float* desc, const float* w_q, const float* w_k,
+                    const float* b_q, const float* b_k, int32_t d_e, float* phi, float* scores,
+                    void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (desc == nullptr || w_q == nullptr || w_k == nullptr || phi == nullptr || scores == nullptr)
+    return VEDA_ERR_INVALID_ARG;
+  if (d_e < 1) return VEDA_ERR_INVALID_ARG;
+  if (d_e > 256) return VEDA_ERR_UNSUPPORTED;
+  if (L->head_dim != 64 && L->head_dim != 128) return VEDA_ERR_UNSUPPORTED;
+  const DevLayout dl = make_dev_layout(L);
+  return finish(launch_project_score(dl, desc, w_q, w_k, b_q, b_k, d_e, phi, scores,
+                                     (hipStream_t)stream),
+                stream);
+}
+
 int veda_select_tiles(const veda_layout* L, const float* scores, const int32_t* k_per_head,
                       int32_t* row_ptr, int32_t* col_idx, void* stream) {
   if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
@@ -198,35 +265,28 @@ int veda_select_tiles(const veda_layout* L, const float* scores, const int32_t* 
 int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k_perm,
                          const void* vt_perm, const int32_t* row_ptr, const int32_t* col_idx,
                          float sm_scale, void* o_perm, float* lse, void* stream) {
-  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
-  if (q_perm == nullptr || k_perm == nullptr || vt_perm == nullptr || row_ptr == nullptr ||
-      col_idx == nullptr || o_perm == nullptr)
-    return VEDA_ERR_INVALID_ARG;
-  if (!(sm_scale > 0.f) || sm_scale == INFINITY) return VEDA_ERR_INVALID_ARG;
-  if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
-  if (!aligned16(q_perm) || !aligned16(k_perm) || !aligned16(vt_perm) || !aligned16(o_perm))
-    return VEDA_ERR_UNSUPPORTED;
-  if (debug_sync()) {   // host-side CSR validation (synchronous, debug only)
-    const int64_t rows = L->tile_off[L->num_heads];
-    std::vector<int32_t> rp(rows + 1);
-    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return VEDA_ERR_LAUNCH;
-    if (hipMemcpy(rp.data(), row_ptr, (rows + 1) * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
-      return VEDA_ERR_LAUNCH;
-    if (rp[0] < 0) return VEDA_ERR_BAD_CSR;
-    for (int64_t r = 0; r < rows; ++r)
-      if (rp[r + 1] < rp[r]) return VEDA_ERR_BAD_CSR;
-    std::vector<int32_t> ci(rp[rows]);
-    if (!ci.empty() && hipMemcpy(ci.data(), col_idx, ci.size() * sizeof(int32_t),
-                                 hipMemcpyDeviceToHost) != hipSuccess)
-      return VEDA_ERR_LAUNCH;
-    for (int h = 0; h < L->num_heads; ++h)
-      for (int64_t r = L->tile_off[h]; r < L->tile_off[h + 1]; ++r)
-        for (int32_t p = rp[r]; p < rp[r + 1]; ++p)
-          if (ci[p] < 0 || ci[p] >= L->n_tiles[h]) return VEDA_ERR_BAD_CSR;
-  }
+  const int st = attn_args(L, q_perm, k_perm, vt_perm, row_ptr, col_idx, sm_scale, o_perm, stream);
+  if (st != VEDA_OK) return st;
   const DevLayout dl = make_dev_layout(L);
   return finish(launch_sparse_attn(dl, q_perm, k_perm, vt_perm, row_ptr, col_idx, sm_scale, o_perm,
-                                   lse, (hipStream_t)stream),
+                                   lse, false, (hipStream_t)stream),
+                stream);
+}
+
+int veda_sparse_attn_fwd_tokens(const veda_layout* L, const void* q_perm, const void* k_perm,
+                                const void* vt_perm, const int32_t* row_ptr,
+                                const int32_t* col_idx, float sm_scale, void* o, float* lse,
+                                void* stream) {
+  const int st = attn_args(L, q_perm, k_perm, vt_perm, row_ptr, col_idx, sm_scale, o, stream);
+  if (st != VEDA_OK) return st;
+  const size_t tok = (size_t)L->T * L->H * L->W * L->num_heads * L->head_dim * 2;
+  const size_t til = (size_t)L->tile_off[L->num_heads] * L->tile_size * L->head_dim * 2;
+  if (!disjoint(o, tok, q_perm, til) || !disjoint(o, tok, k_perm, til) ||
+      !disjoint(o, tok, vt_perm, til))
+    return VEDA_ERR_INVALID_ARG;
+  const DevLayout dl = make_dev_layout(L);
+  return finish(launch_sparse_attn(dl, q_perm, k_perm, vt_perm, row_ptr, col_idx, sm_scale, o, lse,
+                                   true, (hipStream_t)stream),
                 stream);
 }
 

@@ -72,6 +72,91 @@ __global__ __launch_bounds__(kThreads) void permute_fwd_kernel(DevLayout L, int 
   }
 }
 
+// The gather of Q or K fused with TripPool (Veda §2.1): as permute_fwd_kernel,
+// and for each channel the mean, max and min over the tile's real slots,
+// written as desc[g] = [mean | max | min] (3 D floats).  Lane t always moves
+// channel chunk t % CPR, and walks the slots t / CPR, + RG, + 2 RG, ..., so it
+// keeps running statistics of its VEC channels in registers (in the order
+// tripool_pool_kernel uses, which makes the two bit-identical); the RG row
+// groups are combined through LDS.
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void permute_fwd_pool_kernel(DevLayout L,
+                                                                    const Chunk* __restrict__ x,
+                                                                    Chunk* __restrict__ y,
+                                                                    float* __restrict__ desc) {
+  constexpr int VEC = 16 / (int)sizeof(E);
+  constexpr int CPR = D / VEC;                 // chunks per row
+  constexpr int RG = kThreads / CPR;           // row groups
+  static_assert(kThreads % CPR == 0, "every lane keeps one chunk column");
+  __shared__ int64_t rows[256];
+  __shared__ float red[3][RG][D];
+  const int64_t g = blockIdx.x;
+  const int h = tile_rows(L, g, rows);
+  const int total = L.S * CPR;
+  const int ch = threadIdx.x % CPR, rg = threadIdx.x / CPR;
+  float sum[VEC], mx[VEC], mn[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) { sum[c] = 0.f; mx[c] = -INFINITY; mn[c] = INFINITY; }
+  Chunk* dst = y + g * (int64_t)total;
+  for (int c0 = 0; c0 < total; c0 += kThreads * kBatch) {
+    Chunk v[kBatch];
+    bool real[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kThreads + threadIdx.x;
+      v[i] = Chunk{0u, 0u, 0u, 0u};
+      real[i] = false;
+      if (c < total) {
+        const int64_t r = rows[c / CPR];
+        if (r >= 0) {
+          v[i] = x[r * CPR + ch];
+          real[i] = true;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kThreads + threadIdx.x;
+      if (c < total) dst[c] = v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (!real[i]) continue;
+      E e[VEC];
+      __builtin_memcpy(e, &v[i], 16);
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) {
+        const float f = (float)e[c];
+        sum[c] += f;
+        mx[c] = fmaxf(mx[c], f);
+        mn[c] = fminf(mn[c], f);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) {
+    red[0][rg][ch * VEC + c] = sum[c];
+    red[1][rg][ch * VEC + c] = mx[c];
+    red[2][rg][ch * VEC + c] = mn[c];
+  }
+  __syncthreads();
+  const TileExtent e = tile_extent(L, h, (int)(g - L.tile_off[h]));
+  const float inv_cnt = 1.0f / (float)e.count();
+  float* out = desc + g * 3 * D;
+  for (int c = threadIdx.x; c < D; c += kThreads) {
+    float sm = 0.f, a = -INFINITY, b = INFINITY;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      sm += red[0][r][c];
+      a = fmaxf(a, red[1][r][c]);
+      b = fminf(b, red[2][r][c]);
+    }
+    out[c] = sm * inv_cnt;
+    out[D + c] = a;
+    out[2 * D + c] = b;
+  }
+}
+
 // x tile order -> y [N][heads][CPR]; only real slots are read and written
 // (one chunk per lane per pass: batching the loads slows the scattered
 // stores down).
@@ -168,6 +253,30 @@ __global__ __launch_bounds__(kThreads) void permute_fwd_t_f32_kernel(DevLayout L
 }
 
 }  // namespace
+
+int launch_permute_pool(const DevLayout& L, int dtype, const void* x, void* y, float* desc,
+                        hipStream_t s) {
+  const unsigned blocks = (unsigned)L.tile_off[L.heads];
+  if (blocks == 0) return VEDA_OK;
+  const Chunk* cx = (const Chunk*)x;
+  Chunk* cy = (Chunk*)y;
+  if (dtype == VEDA_F32) {
+    if (L.d == 128)
+      hipLaunchKernelGGL((permute_fwd_pool_kernel<float, 128>), dim3(blocks), dim3(kThreads), 0, s,
+                         L, cx, cy, desc);
+    else
+      hipLaunchKernelGGL((permute_fwd_pool_kernel<float, 64>), dim3(blocks), dim3(kThreads), 0, s,
+                         L, cx, cy, desc);
+  } else {
+    if (L.d == 128)
+      hipLaunchKernelGGL((permute_fwd_pool_kernel<__bf16, 128>), dim3(blocks), dim3(kThreads), 0,
+                         s, L, cx, cy, desc);
+    else
+      hipLaunchKernelGGL((permute_fwd_pool_kernel<__bf16, 64>), dim3(blocks), dim3(kThreads), 0,
+                         s, L, cx, cy, desc);
+  }
+  return launch_status();
+}
 
 int launch_permute(const DevLayout& L, int dtype, int dir, const void* x, void* y, hipStream_t s) {
   const int esize = dtype == VEDA_F32 ? 4 : 2;

@@ -59,7 +59,9 @@ struct Pipe {
   static_assert(S % SK == 0, "tile must hold whole steps");
 };
 
-template <int D, int S>
+// TOK: O is written in token order ([N][heads][D], real slots only) instead
+// of tile order, which folds the inverse permutation into the epilogue.
+template <int D, int S, bool TOK>
 __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ vt, const int32_t* __restrict__ row_ptr,
@@ -315,37 +317,62 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
 
   const float l_tot = swap32_sum(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  __bf16* orow = o + qrow * D;
+  // output row of this lane's query: its slot, or (TOK) its token's row of
+  // head h, none for a padding slot
+  int64_t orow_i = qrow;
+  if constexpr (TOK) {
+    const TileExtent e = tile_extent(L, h, (int)(g - head_base));
+    const int u = wave * 32 + n;   // slot = (dt*ph + dh)*pw + dw
+    const int dw = u % e.pw, r = u / e.pw, dh = r % e.ph, dt = r / e.ph;
+    const int64_t tok =
+        ((int64_t)(e.it * e.pt + dt) * L.H + (e.ih * e.ph + dh)) * L.W + (e.iw * e.pw + dw);
+    orow_i = dt < e.lt && dh < e.lh && dw < e.lw ? tok * L.heads + h : -1;
+  }
+  if (orow_i >= 0) {
+    __bf16* orow = o + orow_i * D;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      bf16x4 wv;
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 wv;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) wv[b] = (__bf16)(oacc[db][4 * a + b] * inv);
-      *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * a + 4 * hf) = wv;
-    }
+        for (int b = 0; b < 4; ++b) wv[b] = (__bf16)(oacc[db][4 * a + b] * inv);
+        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * a + 4 * hf) = wv;
+      }
+  }
   if (lse != nullptr && hf == 0)
     lse[qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
 }
 
 }  // namespace
 
-int launch_sparse_attn(const DevLayout& L, const void* q, const void* k, const void* vt,
-                       const int32_t* row_ptr, const int32_t* col_idx, float sm_scale, void* o,
-                       float* lse, hipStream_t s) {
+namespace {
+template <bool TOK>
+void launch_attn(const DevLayout& L, const void* q, const void* k, const void* vt,
+                 const int32_t* row_ptr, const int32_t* col_idx, float scale_log2, void* o,
+                 float* lse, hipStream_t s) {
   const unsigned G = (unsigned)L.tile_off[L.heads];
-  if (G == 0) return VEDA_OK;
-  const float scale_log2 = sm_scale * 1.4426950408889634f;
   if (L.d == 128) {
-    hipLaunchKernelGGL((sparse_attn_fwd_kernel<128, 128>), dim3(G), dim3(256), 0, s,
+    hipLaunchKernelGGL((sparse_attn_fwd_kernel<128, 128, TOK>), dim3(G), dim3(256), 0, s,
                        L, (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, row_ptr, col_idx,
                        scale_log2, (__bf16*)o, lse);
   } else {
-    hipLaunchKernelGGL((sparse_attn_fwd_kernel<64, 64>), dim3(G), dim3(128), 0, s, L,
+    hipLaunchKernelGGL((sparse_attn_fwd_kernel<64, 64, TOK>), dim3(G), dim3(128), 0, s, L,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, row_ptr, col_idx,
                        scale_log2, (__bf16*)o, lse);
   }
+}
+}  // namespace
+
+int launch_sparse_attn(const DevLayout& L, const void* q, const void* k, const void* vt,
+                       const int32_t* row_ptr, const int32_t* col_idx, float sm_scale, void* o,
+                       float* lse, bool tokens, hipStream_t s) {
+  if (L.tile_off[L.heads] == 0) return VEDA_OK;
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  if (tokens)
+    launch_attn<true>(L, q, k, vt, row_ptr, col_idx, scale_log2, o, lse, s);
+  else
+    launch_attn<false>(L, q, k, vt, row_ptr, col_idx, scale_log2, o, lse, s);
   return launch_status();
 }
 

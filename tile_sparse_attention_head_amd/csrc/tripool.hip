@@ -237,6 +237,13 @@ int launch_tripool_score(const DevLayout& L, int dtype, const void* q, const voi
                          (const __bf16*)q, (const __bf16*)k, desc);
   }
   if (launch_status() != VEDA_OK) return VEDA_ERR_LAUNCH;
+  return launch_project_score(L, desc, wq, wk, bq, bk, d_e, phi, scores, s);
+}
+
+int launch_project_score(const DevLayout& L, const float* desc, const float* wq, const float* wk,
+                         const float* bq, const float* bk, int d_e, float* phi, float* scores,
+                         hipStream_t s) {
+  if (L.tile_off[L.heads] == 0) return VEDA_OK;
   const unsigned mbp = (unsigned)((L.max_tiles + kProjBM - 1) / kProjBM);
   const unsigned mb = (unsigned)((L.max_tiles + kScoreBM - 1) / kScoreBM);
   // 16-byte loads need 16-byte aligned rows: K % 4 == 0 and aligned bases

@@ -70,11 +70,16 @@ int launch_tripool_score(const DevLayout& L, int dtype, const void* q, const voi
                          const float* wq, const float* wk, const float* bq,
                          const float* bk, int d_e, float* desc, float* phi,
                          float* scores, hipStream_t s);
+int launch_permute_pool(const DevLayout& L, int dtype, const void* x, void* y, float* desc,
+                        hipStream_t s);
+int launch_project_score(const DevLayout& L, const float* desc, const float* wq,
+                         const float* wk, const float* bq, const float* bk, int d_e,
+                         float* phi, float* scores, hipStream_t s);
 int launch_select(const DevLayout& L, const float* scores, const int32_t* k_host,
                   int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
 int launch_sparse_attn(const DevLayout& L, const void* q, const void* k, const void* vt,
                        const int32_t* row_ptr, const int32_t* col_idx, float sm_scale,
-                       void* o, float* lse, hipStream_t s);
+                       void* o, float* lse, bool tokens, hipStream_t s);
 int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm_scale,
                       const int32_t* q_tiles, int n_sub, void* workspace, float* lse,
                       float* map, hipStream_t s);

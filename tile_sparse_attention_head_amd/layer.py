@@ -2,16 +2,21 @@
 
 ``TileSparseAttention`` owns the device buffers one layer needs (allocated
 once with torch; the library itself never allocates) and enqueues the
-library's calls in the order of the method (Veda §2.1-§2.3):
+library's calls in the order of the method (Veda §2.1-§2.3).  ``forward``
+runs the fused sequence:
 
-  1. veda_tile_permute   Q, K -> tile order; V -> tile-transposed order
-  2. veda_tripool_score  TripPool + per-head projection + tile scores
-  3. veda_select_tiles   top-k key tiles per query tile -> CSR
-  4. veda_sparse_attn_fwd
-  5. veda_tile_permute   O -> token order
+  1. veda_tile_permute_pool  Q, K -> tile order, with their TripPool
+                             descriptors; veda_tile_permute V -> tile-
+                             transposed order
+  2. veda_tile_score         per-head projection + tile scores
+  3. veda_select_tiles       top-k key tiles per query tile -> CSR
+  4. veda_sparse_attn_fwd_tokens   attention, O written in token order
 
-and, on request, veda_oracle_maxpool_map for a subset of query tiles.  All
-calls go on the current torch stream without synchronising.
+``forward_unfused`` runs the same method one step per call (permute,
+veda_tripool_score, select, veda_sparse_attn_fwd, inverse permute); both give
+identical results.  ``maxpool_map`` runs veda_oracle_maxpool_map for a subset
+of query tiles.  All calls go on the current torch stream without
+synchronising.
 """
 from __future__ import annotations
 
@@ -73,10 +78,39 @@ class TileSparseAttention:
     def unpermute(self, out, stream=None):
         V.veda_tile_permute(self.L, self.o_perm, out, V.VEDA_INV, stream)
 
+    # fused stages ------------------------------------------------------------
+    def permute_pool_inputs(self, q, k, v, stream=None):
+        """Q, K -> tile order with their TripPool descriptors (desc[0], desc[1]);
+        V -> tile-transposed order."""
+        n = self.L.total_tiles * 3 * self.L.head_dim
+        V.veda_tile_permute_pool(self.L, q, self.q_perm, self.desc[:n], stream)
+        V.veda_tile_permute_pool(self.L, k, self.k_perm, self.desc[n:2 * n], stream)
+        V.veda_tile_permute(self.L, v, self.vt_perm, V.VEDA_FWD_T, stream)
+
+    def score_from_desc(self, w_q, w_k, b_q=None, b_k=None, stream=None):
+        V.veda_tile_score(self.L, self.desc, w_q, w_k, self.phi, self.scores, b_q, b_k, stream)
+
+    def attend_tokens(self, sm_scale: float, out, with_lse: bool = True, stream=None):
+        V.veda_sparse_attn_fwd_tokens(self.L, self.q_perm, self.k_perm, self.vt_perm,
+                                      self.row_ptr, self.col_idx, sm_scale, out,
+                                      self.lse if with_lse else None, stream)
+
     # whole layer -----------------------------------------------------------
     def forward(self, q, k, v, w_q, w_k, sm_scale: float, out=None, b_q=None, b_k=None,
                 stream=None):
         """q, k, v: bf16 [N][heads][d] (token order).  Returns O, same shape."""
+        if out is None:
+            out = self.torch.empty_like(q)
+        self.permute_pool_inputs(q, k, v, stream)
+        self.score_from_desc(w_q, w_k, b_q, b_k, stream)
+        self.select(stream)
+        self.attend_tokens(sm_scale, out, True, stream)
+        return out
+
+    def forward_unfused(self, q, k, v, w_q, w_k, sm_scale: float, out=None, b_q=None, b_k=None,
+                        stream=None):
+        """forward, one method step per call (tile-order O, then the inverse
+        permutation)."""
         if out is None:
             out = self.torch.empty_like(q)
         self.permute_inputs(q, k, v, stream)
