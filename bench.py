@@ -4,12 +4,17 @@
                     [--sparsity S] [--no-cpu-baseline] [--no-context]
 
 One step is one pass of every stage of the path over one synthetic layer
-whose inputs are already resident in HBM:
+whose inputs are already resident in HBM, through the layer's fused calls:
 
-  veda_tile_permute (Q, K forward; V forward-transposed) -> veda_tripool_score
-  -> veda_select_tiles -> veda_sparse_attn_fwd -> veda_tile_permute (O inverse)
-  -> veda_oracle_maxpool_map (the distillation target on the workload's seeded
-     query-tile subset)
+  veda_tile_permute_pool (Q, K: gather + TripPool) -> veda_tile_permute (V
+  forward-transposed) -> veda_tile_score -> veda_select_tiles ->
+  veda_sparse_attn_fwd_tokens (O written in token order) ->
+  veda_oracle_maxpool_map (the distillation target on the workload's seeded
+  query-tile subset)
+
+The context runs also time the same layer one method step per call
+(veda_tile_permute, veda_tripool_score, veda_select_tiles,
+veda_sparse_attn_fwd, inverse veda_tile_permute).
 
 W untimed steps run first, then exactly K steps are timed between two device
 synchronisations.  Every stage is also bracketed by HIP events on the stream
@@ -54,6 +59,9 @@ KERNEL_SOURCES = {
     "map_stats_kernel": ("oracle_map.hip", "attn_common.hpp", "veda_internal.hpp"),
     "map_reduce_kernel": ("oracle_map.hip", "attn_common.hpp", "veda_internal.hpp"),
     "permute_fwd_kernel": ("permute.hip", "veda_internal.hpp"),
+    "permute_fwd_pool_kernel": ("permute.hip", "veda_internal.hpp"),
+    "project_kernel": ("tripool.hip", "veda_internal.hpp"),
+    "score_kernel": ("tripool.hip", "veda_internal.hpp"),
     "permute_fwd_t_kernel": ("permute.hip", "veda_internal.hpp"),
     "permute_inv_kernel": ("permute.hip", "veda_internal.hpp"),
     "tripool_pool_kernel": ("tripool.hip", "veda_internal.hpp"),
@@ -121,8 +129,14 @@ def tile_real_counts(L):
     return np.concatenate(out).astype(np.int64)
 
 
+FUSED_STAGES = ["permute_pool_q", "permute_pool_k", "permute_vt", "tile_score", "select",
+                "sparse_attn", "map"]
+UNFUSED_STAGES = ["permute_q", "permute_k", "permute_vt", "tripool_score", "select",
+                  "sparse_attn", "permute_o", "map"]
+
+
 class Bench:
-    def __init__(self, name: str, sparsity: int, seed: int = 0, T=None, wl=None):
+    def __init__(self, name: str, sparsity: int, seed: int = 0, T=None, wl=None, fused=True):
         import torch
 
         import tile_sparse_attention_head_amd as V
@@ -149,8 +163,8 @@ class Bench:
         self.out = torch.empty_like(self.q)
         self.flops_c, self.pairs = attn_flops(L, self.layer.k_per_head, cfg.tile_size, cfg.head_dim)
         self.flops_d = map_flops(self.n_sub, L, cfg.tile_size, cfg.head_dim)
-        self.stages = ["permute_q", "permute_k", "permute_vt", "tripool_score", "select",
-                       "sparse_attn", "permute_o", "map"]
+        self.fused = fused
+        self.stages = FUSED_STAGES if fused else UNFUSED_STAGES
         self.ev = None
 
     def _events(self, reps):
@@ -161,6 +175,25 @@ class Bench:
         import tile_sparse_attention_head_amd as V
         ly, sm, L = self.layer, self.cfg.sm_scale, self.L
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        if self.fused:
+            n = L.total_tiles * 3 * L.head_dim
+            rec(0)
+            V.veda_tile_permute_pool(L, self.q, ly.q_perm, ly.desc[:n])
+            rec(1)
+            V.veda_tile_permute_pool(L, self.k, ly.k_perm, ly.desc[n:2 * n])
+            rec(2)
+            V.veda_tile_permute(L, self.v, ly.vt_perm, V.VEDA_FWD_T)
+            rec(3)
+            ly.score_from_desc(self.w, self.w)
+            rec(4)
+            ly.select()
+            rec(5)
+            ly.attend_tokens(sm, self.out, with_lse=True)
+            rec(6)
+            if with_map:
+                ly.maxpool_map(self.q_tiles, sm, self.map_lse, self.map_out)
+            rec(7)
+            return
         rec(0)
         V.veda_tile_permute(L, self.q, ly.q_perm, V.VEDA_FWD)
         rec(1)
@@ -186,6 +219,23 @@ class Bench:
         tok = L.tokens * L.num_heads * d * 2            # real rows, bf16
         til = L.total_tiles * S * d * 2                 # tile order incl. padding
         nnz = sum(L.n(h) * self.layer.k_per_head[h] for h in range(L.num_heads))
+        desc = L.total_tiles * 3 * d * 4                # one side's descriptors, f32
+        d_e = self.layer.d_e
+        proj = 2 * desc + 2 * L.num_heads * d_e * 3 * d * 4 + 2 * L.total_tiles * d_e * 4
+        if self.fused:
+            return {
+                "permute_pool_q": ("hbm", tok + til + desc, "permute_fwd_pool_kernel"),
+                "permute_pool_k": ("hbm", tok + til + desc, "permute_fwd_pool_kernel"),
+                "permute_vt": ("hbm", tok + til, "permute_fwd_t_kernel"),
+                # projection (descriptors + weights in, phi out) and score
+                # (phi in, score matrix out)
+                "tile_score": ("hbm", proj + 2 * L.total_tiles * d_e * 4 + 4 * L.total_scores,
+                               "project_kernel"),
+                "select": ("hbm", 4 * L.total_scores + 4 * nnz + 4 * (L.total_tiles + 1),
+                           "select_kernel"),
+                "sparse_attn": ("mfma", self.flops_c, "sparse_attn_fwd_kernel"),
+                "map": ("mfma", self.flops_d, "map_stats_kernel"),
+            }
         return {
             "permute_q": ("hbm", tok + til, "permute_fwd_kernel"),
             "permute_k": ("hbm", tok + til, "permute_fwd_kernel"),
@@ -386,6 +436,15 @@ def main():
         if "sparsity_0" in context:
             context["attn_speedup_vs_dense"] = context["sparsity_0"]["attn_ms"] / attn_ms
             context["density"] = b.pairs / context["sparsity_0"]["kept_pairs"]
+        # the same layer one method step per call (tile-order O, then the
+        # inverse permutation): what the fused calls save
+        u = Bench(args.workload, args.sparsity, fused=False)
+        _, smu, _ = u.run(max(3, args.steps // 2), 2, with_map=False)
+        du = dict(zip(u.stages, [float(x) for x in smu]))
+        context["unfused"] = {"ms_per_layer": sum(du[n] for n in u.stages if n != "map"),
+                              "stage_ms": {n: du[n] for n in u.stages if n != "map"}}
+        del u
+        torch.cuda.empty_cache()
         # cold caches: a 512 MiB buffer is overwritten before every step, which
         # evicts L2 and MALL (256 MiB) between steps
         flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
