@@ -10,7 +10,7 @@ Citations: "Veda §x" is the technical summary of "Veda: Scalable Video
 Diffusion via Distilled Sparse Attention" on gist.science (the zh, fr and es
 editions share its section numbering); "Veda news" is the aikraft.ru item on
 Veda (ByteDance, HKU, USTC).  Where the pages leave a step open, the reading
-taken is stated at the function that makes it (readings R1-R16).
+taken is stated at the function that makes it (readings R1-R20).
 
 Every function works per attention head on numpy arrays and computes in
 float64.  Inputs that are bf16 are widened exactly before they get here.
@@ -24,10 +24,11 @@ from .estimator import tripool, project, tile_scores
 from .select import keep_count, select_topk
 from .attention import sparse_attention, dense_attention, csr_to_block_mask
 from .oracle_map import maxpool_map, maxpool_map_bruteforce
+from .distill import kl_rows, distill_head
 
 __all__ = [
     "tile_grid", "slot_tokens", "valid_slots", "gather", "scatter", "HeadTiling",
     "tripool", "project", "tile_scores", "keep_count", "select_topk",
     "sparse_attention", "dense_attention", "csr_to_block_mask",
-    "maxpool_map", "maxpool_map_bruteforce",
+    "maxpool_map", "maxpool_map_bruteforce", "kl_rows", "distill_head",
 ]

@@ -31,6 +31,12 @@ MUTS = [
  ("attention.py", "q_slots = q_slots[valid[q_slots]]", "q_slots = q_slots"),
  ("attention.py", "mask = np.repeat(np.repeat(tile_keep, S, axis=0), S, axis=1)", "mask = np.repeat(np.repeat(tile_keep.T, S, axis=0), S, axis=1)"),
  ("tiling.py", "x[n] = y[s]", "x[n] = y[s] if s % 2 == 0 else 0"),
+ ("distill.py", "t * (np.log(safe_t) - log_p)", "np.exp(log_p) * (log_p - np.log(safe_t))"),
+ ("distill.py", "g = (p - t) / R", "g = (t - p) / R"),
+ ("distill.py", "np.add.at(dphi_q, rows, g @ phi_k)", "dphi_q[rows] = g @ phi_k"),
+ ("distill.py", "dphi_k = g.T @ phi_q[rows]", "dphi_k = g.T @ phi_k[rows]"),
+ ("distill.py", "dphi_q.sum(axis=0), dphi_k.sum(axis=0)", "dphi_q.sum(axis=0), dphi_q.sum(axis=0)"),
+ ("distill.py", "loss = kl_rows(s[rows], map_rows).sum() / R", "loss = kl_rows(s[rows], map_rows).mean()"),
 ]
 env = dict(os.environ)
 survivors = []
