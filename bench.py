@@ -248,6 +248,21 @@ class Bench:
             "map": ("mfma", self.flops_d, "map_stats_kernel"),
         }
 
+    def time_distill(self, reps: int = 10):
+        """The estimator's distillation step (veda_distill_grad) on the map and
+        scores of the last step: mean ms over ``reps`` event-timed calls."""
+        torch = self.torch
+        ly = self.layer
+        ly.distill_grad(self.q_tiles, self.map_out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            ly.distill_grad(self.q_tiles, self.map_out)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
     def valid_flops_c(self):
         """4*d*sum over kept pairs of |real query slots| * |real key slots|."""
         L, d = self.L, self.cfg.head_dim
@@ -419,6 +434,16 @@ def main():
 
     context = {}
     if not args.no_context:
+        # the distillation step on this step's map and scores: KL rows, then
+        # the projection gradients (2 S = phi phi^T backward products and the
+        # 3d x d_e weight gradients per head)
+        dms = b.time_distill()
+        n_sub = int(sum(b.n_sub))
+        de = b.layer.d_e
+        flops = (2.0 * 2 * de * sum(b.n_sub[h] * L.n(h) for h in range(L.num_heads))
+                 + 2.0 * 3 * cfg.head_dim * de * (n_sub + L.total_tiles))
+        context["distill"] = {"ms": dms, "subset_tiles": n_sub, "gflop": flops / 1e9,
+                              "tflops": flops / (dms * 1e-3) / 1e12}
         for s in (95, 0):
             if s == args.sparsity:
                 continue

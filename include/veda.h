@@ -243,6 +243,42 @@ int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void
  *  bytes  (host) output */
 int veda_oracle_maxpool_map_workspace(const veda_layout* L, int32_t n_sub, int64_t* bytes);
 
+/* Distillation step of the estimator (Veda §2.1, optimisation: row-wise KL
+ * objective, stop-gradient on the backbone features).  For every subset entry
+ * s with query tile g = q_tiles[s] (local index i in head hd):
+ *   p = softmax over j < n_tiles[hd] of scores[score_off[hd] + i*n + j]
+ *   t = map[s][j] / sum_j map[s][j]
+ *   loss = (1/R) sum_s KL(t || p)         R = entries with 0 <= g < tiles
+ * and the gradients of loss with respect to the projections of
+ * veda_tile_score, the TripPool descriptors being constants:
+ *   grad_w_q, grad_w_k  f32 [num_heads][d_e][3*head_dim] (output)
+ *   grad_b_q, grad_b_k  f32 [num_heads][d_e] (output), or NULL
+ * When one weight set serves both sides, its gradient is the sum of the two.
+ *  scores    f32 [score_off[num_heads]] as written by veda_tile_score
+ *  map       f32 [n_sub][max_tiles]: veda_oracle_maxpool_map over the same
+ *            q_tiles (a row whose map sums to 0 contributes nothing)
+ *  q_tiles   int32 [n_sub] global query-tile indices; entries outside
+ *            [0, tile_off[num_heads]) are ignored (and not counted in R)
+ *  desc      f32 [2][tile_off[num_heads]][3*head_dim] TripPool descriptors
+ *  phi       f32 [2][tile_off[num_heads]][d_e] projections
+ *  workspace device scratch of at least veda_distill_grad_workspace(L, n_sub,
+ *            d_e) bytes, 16-byte aligned (smaller: VEDA_ERR_INVALID_ARG);
+ *            owned by the caller, contents unspecified on entry and exit
+ *  loss      f32 [1] (output)
+ * Every output element is written; with R = 0 the loss and gradients are 0.
+ * f32 arithmetic, sums in a fixed order (deterministic).  Supported:
+ * 1 <= d_e <= 256, head_dim in {64, 128}. */
+int veda_distill_grad(const veda_layout* L, const float* scores, const float* map,
+                      const int32_t* q_tiles, int32_t n_sub, const float* desc,
+                      const float* phi, int32_t d_e, void* workspace, int64_t workspace_bytes,
+                      float* loss, float* grad_w_q, float* grad_w_k, float* grad_b_q,
+                      float* grad_b_k, void* stream);
+
+/* Workspace bytes veda_distill_grad needs.  Host-only.
+ *  bytes  (host) output */
+int veda_distill_grad_workspace(const veda_layout* L, int32_t n_sub, int32_t d_e,
+                                int64_t* bytes);
+
 /* Static text for a veda_status value. */
 const char* veda_status_string(int status);
 

@@ -10,7 +10,7 @@ Citations: "Veda §x" is the technical summary of "Veda: Scalable Video
 Diffusion via Distilled Sparse Attention" on gist.science (the zh, fr and es
 editions share its section numbering); "Veda news" is the aikraft.ru item on
 Veda (ByteDance, HKU, USTC).  Where the pages leave a step open, the reading
-taken is stated at the function that makes it (readings R1-R20).
+taken is stated at the function that makes it (readings R1-R16 and R21-R24).
 
 Every function works per attention head on numpy arrays and computes in
 float64.  Inputs that are bf16 are widened exactly before they get here.

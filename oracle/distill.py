@@ -9,14 +9,14 @@ on the backbone features that feed the estimator, so only the estimator's own
 parameters learn.
 
 Readings (the pages leave these open):
-  R17 the predicted distribution of query tile i is the softmax over the
+  R21 the predicted distribution of query tile i is the softmax over the
       head's key tiles j of the estimator score S[i][j] (no temperature);
-  R18 the reference distribution is the max-pooled map row M[i][:] (Veda
+  R22 the reference distribution is the max-pooled map row M[i][:] (Veda
       §2.1 target construction; ``maxpool_map``) divided by its sum;
-  R19 the divergence is KL(reference || predicted) = sum_j t_j log(t_j/p_j),
+  R23 the divergence is KL(reference || predicted) = sum_j t_j log(t_j/p_j),
       with t_j log t_j = 0 for t_j = 0, averaged over the subset's query-tile
       rows of every head (R = number of rows);
-  R20 stop-gradient on the features means the TripPool descriptors are
+  R24 stop-gradient on the features means the TripPool descriptors are
       constants: gradients flow to the projection weights and biases only;
       the query-side and key-side projections get gradients of their own
       (equal weight sets are one parameter whose gradient is the sum).
@@ -31,7 +31,7 @@ from .estimator import project, tile_scores
 
 
 def kl_rows(scores_rows: np.ndarray, map_rows: np.ndarray) -> np.ndarray:
-    """KL(t || p) of every row (R17-R19): ``scores_rows`` [R][n] estimator
+    """KL(t || p) of every row (R21-R23): ``scores_rows`` [R][n] estimator
     scores, ``map_rows`` [R][n] max-pooled map, each row with a positive sum."""
     s = np.asarray(scores_rows, np.float64)
     m = np.asarray(map_rows, np.float64)
@@ -47,7 +47,7 @@ def distill_head(desc_q: np.ndarray, desc_k: np.ndarray, w_q: np.ndarray, w_k: n
                  map_rows: np.ndarray, n_rows_total: int):
     """One head's share of the objective and of its gradients.
 
-    ``desc_q``/``desc_k`` [n][3d] TripPool descriptors (constants, R20);
+    ``desc_q``/``desc_k`` [n][3d] TripPool descriptors (constants, R24);
     ``w_*`` [d_e][3d], ``b_*`` [d_e] or None; ``rows`` the head-local query
     tiles of the subset (repeats allowed), ``map_rows`` [len(rows)][n] their
     max-pooled map rows; ``n_rows_total`` = R over all heads.

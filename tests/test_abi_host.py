@@ -185,6 +185,41 @@ def test_device_calls_reject_before_launch(lib):
     assert M(Lp, fake, fake, 0.1, fake, 3, fake + 8, big, fake, fake, None) == -2
 
 
+def test_distill_rejections_and_workspace(lib):
+    L = _layout()
+    Lp = ctypes.byref(L)
+    fake = 1 << 20
+    ws = ctypes.c_int64(0)
+    assert lib.veda_distill_grad_workspace(Lp, 5, 128, ctypes.byref(ws)) == 0
+    need = ws.value
+    assert need >= 4 * 5 * L.max_tiles + 4 * L.total_tiles * 128
+    assert lib.veda_distill_grad_workspace(Lp, -1, 128, ctypes.byref(ws)) == -1
+    assert lib.veda_distill_grad_workspace(Lp, 5, 0, ctypes.byref(ws)) == -1
+    assert lib.veda_distill_grad_workspace(Lp, 5, 128, None) == -1
+    D = lib.veda_distill_grad
+    ok = dict(sc=fake, mp=fake, qt=fake, n=5, desc=fake, phi=fake, de=128, ws=fake, wsb=need,
+              loss=fake, gq=fake, gk=fake)
+    def call(**kw):
+        a = dict(ok, **kw)
+        return D(Lp, a["sc"], a["mp"], a["qt"], a["n"], a["desc"], a["phi"], a["de"], a["ws"],
+                 a["wsb"], a["loss"], a["gq"], a["gk"], None, None, None)
+    assert call(n=-1) == -1
+    assert call(de=0) == -1
+    assert call(de=300) == -2
+    assert call(desc=None) == -1
+    assert call(loss=None) == -1
+    assert call(gk=None) == -1
+    assert call(mp=None) == -1
+    assert call(ws=None) == -1
+    assert call(wsb=need - 1) == -1
+    assert call(ws=fake + 8) == -2
+    L3 = V.veda_layout_init(5, 9, 20, 96, 128, [(8, 4, 4)])
+    ws3 = ctypes.c_int64(0)
+    assert lib.veda_distill_grad_workspace(ctypes.byref(L3), 5, 128, ctypes.byref(ws3)) == 0
+    assert D(ctypes.byref(L3), fake, fake, fake, 5, fake, fake, 128, fake, ws3.value, fake, fake,
+             fake, None, None, None) == -2
+
+
 def test_map_workspace_size(lib):
     # row maxima (n_sub x max_tiles x S f32, rounded up to 256 bytes) followed by
     # the per-chunk (m, l) pairs (n_sub x chunks x S x 2 f32)

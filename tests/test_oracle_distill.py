@@ -70,7 +70,7 @@ def _problem(seed=2, n=6, d3=12, de=5):
 
 
 def _loss(desc_q, desc_k, w_q, w_k, b_q, b_k, rows, m, R):
-    # the objective written out from its definition (R17-R19): estimator
+    # the objective written out from its definition (R21-R23): estimator
     # forward, then the mean row KL against the normalised map rows
     s = oracle.tile_scores(oracle.project(desc_q, w_q, b_q), oracle.project(desc_k, w_k, b_k))
     return sum(rel_entr(mr / mr.sum(), np.exp(s[r]) / np.exp(s[r]).sum()).sum()

@@ -95,6 +95,9 @@ def lib() -> ctypes.CDLL:
         "veda_oracle_maxpool_map": (c_i32, [P, c_vp, c_vp, c_f32, c_vp, c_i32, c_vp, c_i64,
                                             c_vp, c_vp, c_vp]),
         "veda_oracle_maxpool_map_workspace": (c_i32, [P, c_i32, ctypes.POINTER(c_i64)]),
+        "veda_distill_grad": (c_i32, [P, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_i64,
+                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+        "veda_distill_grad_workspace": (c_i32, [P, c_i32, c_i32, ctypes.POINTER(c_i64)]),
         "veda_status_string": (ctypes.c_char_p, [c_i32]),
         "veda_layout_sizeof": (c_i64, []),
     }
@@ -328,3 +331,42 @@ def veda_oracle_maxpool_map(L: veda_layout, q_perm, k_perm, sm_scale: float, q_t
     _check(lib().veda_oracle_maxpool_map(ctypes.byref(L), args[0], args[1], float(sm_scale), pq,
                                          n_sub, pw, have, pl, pm, _stream(stream)),
            "veda_oracle_maxpool_map")
+
+
+def veda_distill_grad_workspace(L: veda_layout, n_sub: int, d_e: int) -> int:
+    """Bytes of device workspace veda_distill_grad needs."""
+    out = c_i64(0)
+    _check(lib().veda_distill_grad_workspace(ctypes.byref(L), int(n_sub), int(d_e),
+                                             ctypes.byref(out)),
+           "veda_distill_grad_workspace")
+    return int(out.value)
+
+
+def veda_distill_grad(L: veda_layout, scores, out_map, q_tiles, desc, phi, d_e: int, workspace,
+                      loss, grad_w_q, grad_w_k, grad_b_q=None, grad_b_k=None,
+                      stream=None) -> None:
+    """Row-wise KL distillation loss and its projection gradients; workspace
+    of at least veda_distill_grad_workspace(L, n_sub, d_e) bytes."""
+    torch = _torch()
+    f32 = torch.float32
+    n_sub = int(q_tiles.numel())
+    d = L.head_dim
+    H = L.num_heads
+    ps = _dev(scores, "scores", f32, L.total_scores)
+    pm = _dev(out_map, "map", f32, n_sub * L.max_tiles)
+    pq = _dev(q_tiles, "q_tiles", torch.int32, n_sub)
+    pd = _dev(desc, "desc", f32, 2 * L.total_tiles * 3 * d)
+    pp = _dev(phi, "phi", f32, 2 * L.total_tiles * int(d_e))
+    need = veda_distill_grad_workspace(L, n_sub, d_e)
+    pw = _dev(workspace, "workspace", None, 0)
+    have = workspace.numel() * workspace.element_size()
+    if have < need:
+        raise ValueError(f"workspace holds {have} bytes, needs {need}")
+    pl = _dev(loss, "loss", f32, 1)
+    gq = _dev(grad_w_q, "grad_w_q", f32, H * int(d_e) * 3 * d)
+    gk = _dev(grad_w_k, "grad_w_k", f32, H * int(d_e) * 3 * d)
+    bq = _dev(grad_b_q, "grad_b_q", f32, H * int(d_e), True)
+    bk = _dev(grad_b_k, "grad_b_k", f32, H * int(d_e), True)
+    _check(lib().veda_distill_grad(ctypes.byref(L), ps, pm, pq, n_sub, pd, pp, int(d_e), pw, have,
+                                   pl, gq, gk, bq, bk, _stream(stream)),
+           "veda_distill_grad")

@@ -316,6 +316,36 @@ int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void
                 stream);
 }
 
+int veda_distill_grad_workspace(const veda_layout* L, int32_t n_sub, int32_t d_e,
+                                int64_t* bytes) {
+  if (L == nullptr || bytes == nullptr || !layout_ok(L) || n_sub < 0 || d_e < 1)
+    return VEDA_ERR_INVALID_ARG;
+  *bytes = distill_workspace_bytes(make_dev_layout(L), n_sub, d_e);
+  return VEDA_OK;
+}
+
+int veda_distill_grad(const veda_layout* L, const float* scores, const float* map,
+                      const int32_t* q_tiles, int32_t n_sub, const float* desc, const float* phi,
+                      int32_t d_e, void* workspace, int64_t workspace_bytes, float* loss,
+                      float* grad_w_q, float* grad_w_k, float* grad_b_q, float* grad_b_k,
+                      void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (n_sub < 0 || d_e < 1) return VEDA_ERR_INVALID_ARG;
+  if (desc == nullptr || phi == nullptr || workspace == nullptr || loss == nullptr ||
+      grad_w_q == nullptr || grad_w_k == nullptr)
+    return VEDA_ERR_INVALID_ARG;
+  if (n_sub > 0 && (scores == nullptr || map == nullptr || q_tiles == nullptr))
+    return VEDA_ERR_INVALID_ARG;
+  if (d_e > 256) return VEDA_ERR_UNSUPPORTED;
+  if (L->head_dim != 64 && L->head_dim != 128) return VEDA_ERR_UNSUPPORTED;
+  const DevLayout dl = make_dev_layout(L);
+  if (workspace_bytes < distill_workspace_bytes(dl, n_sub, d_e)) return VEDA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return VEDA_ERR_UNSUPPORTED;
+  return finish(launch_distill(dl, scores, map, q_tiles, n_sub, desc, phi, d_e, workspace, loss,
+                               grad_w_q, grad_w_k, grad_b_q, grad_b_k, (hipStream_t)stream),
+                stream);
+}
+
 int64_t veda_layout_sizeof(void) { return (int64_t)sizeof(veda_layout); }
 
 const char* veda_status_string(int status) {

@@ -88,6 +88,13 @@ int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm
 int64_t map_chunks(int64_t n_sub, int64_t max_tiles);
 int64_t map_workspace_bytes(const DevLayout& L, int64_t n_sub);
 
+// Distillation step: workspace bytes, and the launch.
+int64_t distill_workspace_bytes(const DevLayout& L, int64_t n_sub, int d_e);
+int launch_distill(const DevLayout& L, const float* scores, const float* map,
+                   const int32_t* q_tiles, int n_sub, const float* desc, const float* phi,
+                   int d_e, void* workspace, float* loss, float* dwq, float* dwk, float* dbq,
+                   float* dbk, hipStream_t s);
+
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? VEDA_OK : VEDA_ERR_LAUNCH;
 }

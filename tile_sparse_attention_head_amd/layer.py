@@ -15,7 +15,8 @@ runs the fused sequence:
 ``forward_unfused`` runs the same method one step per call (permute,
 veda_tripool_score, select, veda_sparse_attn_fwd, inverse permute); both give
 identical results.  ``maxpool_map`` runs veda_oracle_maxpool_map for a subset
-of query tiles.  All calls go on the current torch stream without
+of query tiles, and ``distill_grad`` the estimator's distillation step
+(veda_distill_grad) against that map.  All calls go on the current torch stream without
 synchronising.
 """
 from __future__ import annotations
@@ -50,6 +51,7 @@ class TileSparseAttention:
         self.o_perm = torch.empty(nt, dtype=bf, device=dev)
         self.lse = torch.empty(L.total_tiles * tile_size, dtype=f32, device=dev)
         self._map_ws = None   # veda_oracle_maxpool_map workspace, sized on first use
+        self._distill_ws = None   # veda_distill_grad workspace, sized on first use
         self.desc = torch.empty(2 * L.total_tiles * 3 * head_dim, dtype=f32, device=dev)
         self.phi = torch.empty(2 * L.total_tiles * self.d_e, dtype=f32, device=dev)
         self.scores = torch.empty(L.total_scores, dtype=f32, device=dev)
@@ -138,3 +140,26 @@ class TileSparseAttention:
         V.veda_oracle_maxpool_map(self.L, self.q_perm, self.k_perm, sm_scale, q_tiles,
                                   self._map_ws, lse, out_map, stream)
         return lse, out_map
+
+    def distill_grad(self, q_tiles, out_map, loss=None, grads=None, with_bias=True, stream=None):
+        """Row-wise KL distillation loss of the scores this layer last computed
+        against the max-pooled map ``out_map`` of ``q_tiles``, and the
+        gradients of the projections (Veda §2.1 optimisation).  Returns
+        (loss [1], (grad_w_q, grad_w_k, grad_b_q, grad_b_k))."""
+        torch = self.torch
+        L, dev = self.L, self.q_perm.device
+        n_sub = int(q_tiles.numel())
+        H, de, d3 = L.num_heads, self.d_e, 3 * L.head_dim
+        if loss is None:
+            loss = torch.empty(1, dtype=torch.float32, device=dev)
+        if grads is None:
+            grads = (torch.empty(H, de, d3, dtype=torch.float32, device=dev),
+                     torch.empty(H, de, d3, dtype=torch.float32, device=dev),
+                     torch.empty(H, de, dtype=torch.float32, device=dev) if with_bias else None,
+                     torch.empty(H, de, dtype=torch.float32, device=dev) if with_bias else None)
+        need = V.veda_distill_grad_workspace(L, n_sub, de)
+        if getattr(self, "_distill_ws", None) is None or self._distill_ws.numel() < need:
+            self._distill_ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+        V.veda_distill_grad(L, self.scores, out_map, q_tiles, self.desc, self.phi, de,
+                            self._distill_ws, loss, *grads, stream=stream)
+        return loss, grads
