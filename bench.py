@@ -444,6 +444,23 @@ def main():
                  + 2.0 * 3 * cfg.head_dim * de * (n_sub + L.total_tiles))
         context["distill"] = {"ms": dms, "subset_tiles": n_sub, "gflop": flops / 1e9,
                               "tflops": flops / (dms * 1e-3) / 1e12}
+        # head-aware tiling search over the four 128-slot shapes on this layer:
+        # full attention once, then the fused layer and the per-head error for
+        # each shape (wall time, buffers allocated per candidate included)
+        import tile_sparse_attention_head_amd as V
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        chosen, errs, ref = V.search_tile_shapes(b.wl.T, cfg.H, cfg.W, cfg.head_dim,
+                                                 cfg.tile_size, b.q, b.k, b.v, b.w, b.w,
+                                                 cfg.sm_scale, args.sparsity)
+        torch.cuda.synchronize()
+        rel = (errs / ref).sqrt().cpu().numpy()
+        context["tiling_search"] = {
+            "ms": (time.perf_counter() - t0) * 1e3,
+            "candidates": [list(c) for c in V.tiling_search.SHAPES_128],
+            "chosen": [list(c) for c in chosen],
+            "rel_error_per_candidate_median_over_heads": [float(np.median(r)) for r in rel]}
+        torch.cuda.empty_cache()
         for s in (95, 0):
             if s == args.sparsity:
                 continue

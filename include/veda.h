@@ -279,6 +279,23 @@ int veda_distill_grad(const veda_layout* L, const float* scores, const float* ma
 int veda_distill_grad_workspace(const veda_layout* L, int32_t n_sub, int32_t d_e,
                                 int64_t* bytes);
 
+/* Per-head squared error between two attention outputs, the measure of the
+ * head-aware tiling search (Veda §2.2: each head's tile shape is chosen
+ * offline by the approximation error between the full-attention output and
+ * the sparse-attention output).  a, b: bf16 [N][num_heads][head_dim] in
+ * token order (e.g. full attention and veda_sparse_attn_fwd_tokens output).
+ *  err   f64 [num_heads] (output): sum over tokens and channels of (a - b)^2
+ *  ref   f64 [num_heads] (output): sum of a^2, or NULL
+ *  workspace  at least veda_head_sq_error_workspace(L) bytes, 8-byte aligned
+ * f64 accumulation in a fixed order (deterministic).  Supported: head_dim a
+ * multiple of 8 with head_dim/8 dividing 256, a and b 16-byte aligned. */
+int veda_head_sq_error(const veda_layout* L, const void* a, const void* b, double* err,
+                       double* ref, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes veda_head_sq_error needs.  Host-only.
+ *  bytes  (host) output */
+int veda_head_sq_error_workspace(const veda_layout* L, int64_t* bytes);
+
 /* Static text for a veda_status value. */
 const char* veda_status_string(int status);
 

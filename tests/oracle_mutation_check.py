@@ -37,6 +37,10 @@ MUTS = [
  ("distill.py", "dphi_k = g.T @ phi_q[rows]", "dphi_k = g.T @ phi_k[rows]"),
  ("distill.py", "dphi_q.sum(axis=0), dphi_k.sum(axis=0)", "dphi_q.sum(axis=0), dphi_q.sum(axis=0)"),
  ("distill.py", "loss = kl_rows(s[rows], map_rows).sum() / R", "loss = kl_rows(s[rows], map_rows).mean()"),
+ ("tiling_search.py", "int(np.argmin(errs))", "int(np.argmax(errs))"),
+ ("tiling_search.py", "rp, ci = select_topk(s, keep_count(ht.n, sparsity_pct))", "rp, ci = select_topk(s.T, keep_count(ht.n, sparsity_pct))"),
+ ("tiling_search.py", "return scatter(np.nan_to_num(o), T, H, W, shape)", "return np.nan_to_num(o)[:T * H * W]"),
+ ("tiling_search.py", "full, _ = dense_attention(q, k, v, sm_scale)", "full, _ = dense_attention(q, k, v, 1.0)"),
 ]
 env = dict(os.environ)
 survivors = []

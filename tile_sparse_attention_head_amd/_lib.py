@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
         "veda_distill_grad": (c_i32, [P, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_i64,
                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
         "veda_distill_grad_workspace": (c_i32, [P, c_i32, c_i32, ctypes.POINTER(c_i64)]),
+        "veda_head_sq_error": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp]),
+        "veda_head_sq_error_workspace": (c_i32, [P, ctypes.POINTER(c_i64)]),
         "veda_status_string": (ctypes.c_char_p, [c_i32]),
         "veda_layout_sizeof": (c_i64, []),
     }
@@ -370,3 +372,25 @@ def veda_distill_grad(L: veda_layout, scores, out_map, q_tiles, desc, phi, d_e: 
     _check(lib().veda_distill_grad(ctypes.byref(L), ps, pm, pq, n_sub, pd, pp, int(d_e), pw, have,
                                    pl, gq, gk, bq, bk, _stream(stream)),
            "veda_distill_grad")
+
+
+def veda_head_sq_error_workspace(L: veda_layout) -> int:
+    out = c_i64(0)
+    _check(lib().veda_head_sq_error_workspace(ctypes.byref(L), ctypes.byref(out)),
+           "veda_head_sq_error_workspace")
+    return int(out.value)
+
+
+def veda_head_sq_error(L: veda_layout, a, b, err, workspace, ref=None, stream=None) -> None:
+    """err[h] = sum (a - b)^2 over head h of two bf16 token-order outputs
+    (and ref[h] = sum a^2); err/ref f64 [num_heads]."""
+    torch = _torch()
+    n = tokens_numel(L)
+    pa = _dev(a, "a", torch.bfloat16, n)
+    pb = _dev(b, "b", torch.bfloat16, n)
+    pe = _dev(err, "err", torch.float64, L.num_heads)
+    pr = _dev(ref, "ref", torch.float64, L.num_heads, True)
+    pw = _dev(workspace, "workspace", None, 0)
+    have = workspace.numel() * workspace.element_size()
+    _check(lib().veda_head_sq_error(ctypes.byref(L), pa, pb, pe, pr, pw, have, _stream(stream)),
+           "veda_head_sq_error")

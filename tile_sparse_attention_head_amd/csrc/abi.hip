@@ -346,6 +346,25 @@ int veda_distill_grad(const veda_layout* L, const float* scores, const float* ma
                 stream);
 }
 
+int veda_head_sq_error_workspace(const veda_layout* L, int64_t* bytes) {
+  if (L == nullptr || bytes == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  *bytes = head_error_workspace_bytes(make_dev_layout(L));
+  return VEDA_OK;
+}
+
+int veda_head_sq_error(const veda_layout* L, const void* a, const void* b, double* err,
+                       double* ref, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (a == nullptr || b == nullptr || err == nullptr || workspace == nullptr)
+    return VEDA_ERR_INVALID_ARG;
+  if (L->head_dim % 8 != 0 || 256 % (L->head_dim / 8) != 0) return VEDA_ERR_UNSUPPORTED;
+  if (!aligned16(a) || !aligned16(b) || ((uintptr_t)workspace & 7u) != 0)
+    return VEDA_ERR_UNSUPPORTED;
+  const DevLayout dl = make_dev_layout(L);
+  if (workspace_bytes < head_error_workspace_bytes(dl)) return VEDA_ERR_INVALID_ARG;
+  return finish(launch_head_error(dl, a, b, err, ref, workspace, (hipStream_t)stream), stream);
+}
+
 int64_t veda_layout_sizeof(void) { return (int64_t)sizeof(veda_layout); }
 
 const char* veda_status_string(int status) {

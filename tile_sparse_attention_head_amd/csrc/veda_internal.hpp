@@ -95,6 +95,11 @@ int launch_distill(const DevLayout& L, const float* scores, const float* map,
                    int d_e, void* workspace, float* loss, float* dwq, float* dwk, float* dbq,
                    float* dbk, hipStream_t s);
 
+// Per-head squared error of two token-order outputs (tiling search).
+int64_t head_error_workspace_bytes(const DevLayout& L);
+int launch_head_error(const DevLayout& L, const void* a, const void* b, double* err, double* ref,
+                      void* workspace, hipStream_t s);
+
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? VEDA_OK : VEDA_ERR_LAUNCH;
 }
