@@ -10,7 +10,7 @@ Citations: "Veda §x" is the technical summary of "Veda: Scalable Video
 Diffusion via Distilled Sparse Attention" on gist.science (the zh, fr and es
 editions share its section numbering); "Veda news" is the aikraft.ru item on
 Veda (ByteDance, HKU, USTC).  Where the pages leave a step open, the reading
-taken is stated at the function that makes it (readings R1-R16 and R21-R27).
+taken is stated at the function that makes it (readings R1-R16 and R21-R28).
 
 Every function works per attention head on numpy arrays and computes in
 float64.  Inputs that are bf16 are widened exactly before they get here.
@@ -26,11 +26,12 @@ from .attention import sparse_attention, dense_attention, csr_to_block_mask
 from .oracle_map import maxpool_map, maxpool_map_bruteforce
 from .distill import kl_rows, distill_head
 from .tiling_search import sparse_head_output, search_head
+from .attention_bwd import sparse_attention_bwd
 
 __all__ = [
     "tile_grid", "slot_tokens", "valid_slots", "gather", "scatter", "HeadTiling",
     "tripool", "project", "tile_scores", "keep_count", "select_topk",
     "sparse_attention", "dense_attention", "csr_to_block_mask",
     "maxpool_map", "maxpool_map_bruteforce", "kl_rows", "distill_head",
-    "sparse_head_output", "search_head",
+    "sparse_head_output", "search_head", "sparse_attention_bwd",
 ]

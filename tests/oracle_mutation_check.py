@@ -41,6 +41,10 @@ MUTS = [
  ("tiling_search.py", "rp, ci = select_topk(s, keep_count(ht.n, sparsity_pct))", "rp, ci = select_topk(s.T, keep_count(ht.n, sparsity_pct))"),
  ("tiling_search.py", "return scatter(np.nan_to_num(o), T, H, W, shape)", "return np.nan_to_num(o)[:T * H * W]"),
  ("tiling_search.py", "full, _ = dense_attention(q, k, v, sm_scale)", "full, _ = dense_attention(q, k, v, 1.0)"),
+ ("attention_bwd.py", "ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+ ("attention_bwd.py", "np.add.at(dk, key_slots, sm_scale * ds.T @ q[q_slots])", "dk[key_slots] += sm_scale * ds.T @ q[q_slots]"),
+ ("attention_bwd.py", "dq[q_slots] = sm_scale * ds @ k[key_slots]", "dq[q_slots] = ds @ k[key_slots]"),
+ ("attention_bwd.py", "np.add.at(dv, key_slots, p.T @ do[q_slots])", "np.add.at(dv, key_slots, ds.T @ do[q_slots])"),
 ]
 env = dict(os.environ)
 survivors = []
