@@ -208,6 +208,42 @@ int veda_sparse_attn_fwd_tokens(const veda_layout* L, const void* q_perm, const 
                                 const int32_t* col_idx, float sm_scale, void* o,
                                 float* lse, void* stream);
 
+/* Backward of the tile-skipping attention (Veda §2.3 kernel; the pages
+ * fine-tune with the sparse path in place but give no backward kernel): the
+ * gradients of the forward's output with respect to Q, K and V over exactly
+ * the kept tiles of the forward's CSR.  With P the forward's softmax of query
+ * row r over its kept real keys, D_r = dO_r . O_r:
+ *   dV_c = sum_r P_rc dO_r,  dS_rc = P_rc (dO_r . V_c - D_r),
+ *   dQ_r = sm_scale sum_c dS_rc K_c,  dK_c = sm_scale sum_r dS_rc Q_r
+ * (a tile listed twice in a row contributes twice, as in the forward).
+ *  q, k, v     bf16 [N][num_heads][head_dim], token order (the forward's inputs)
+ *  o           bf16 token order: the forward's output (veda_sparse_attn_fwd_tokens)
+ *  d_o         bf16 token order: gradient of the loss with respect to o
+ *  lse         f32 [tile_off[num_heads]*S]: the forward's log-sum-exp (tile-slot order)
+ *  row_ptr, col_idx  the forward's CSR, each row's entries ascending (as
+ *              veda_select_tiles writes them); entries outside [0, n_tiles[hd])
+ *              are skipped.  nnz = row_ptr[tile_off[num_heads]] (host value)
+ *  workspace   at least veda_sparse_attn_bwd_workspace(L, nnz) bytes,
+ *              16-byte aligned; holds the gathered operands, D and the
+ *              transposed CSR; contents unspecified on entry and exit
+ *  dq, dk, dv  bf16 token order (outputs): every element is written; a key
+ *              tile no row keeps gets dK = dV = 0, an empty row dQ = 0; must
+ *              not overlap the inputs
+ * bf16 matrix-core products with f32 accumulation; deterministic.  A row that
+ * is not sorted gives wrong gradients (never an out-of-bounds access); with
+ * VEDA_DEBUG_SYNC=1 the CSR (monotone rows, in-range and ascending entries,
+ * nnz) is checked and VEDA_ERR_BAD_CSR returned.  Supported: (head_dim,
+ * tile_size) in {(64,64), (128,128)}, 16-byte aligned tensors. */
+int veda_sparse_attn_bwd(const veda_layout* L, const void* q, const void* k, const void* v,
+                         const void* o, const void* d_o, const float* lse,
+                         const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                         float sm_scale, void* workspace, int64_t workspace_bytes, void* dq,
+                         void* dk, void* dv, void* stream);
+
+/* Workspace bytes veda_sparse_attn_bwd needs for a CSR of nnz entries.
+ * Host-only.  bytes (host) output. */
+int veda_sparse_attn_bwd_workspace(const veda_layout* L, int64_t nnz, int64_t* bytes);
+
 /* Max-pooled attention map, the distillation target (Veda §2.1 target
  * construction; Veda §2.3: two passes over a random subset of query tiles).
  * For subset entry s, q_tiles[s] = global tile index g (tile_off[hd] <= g <

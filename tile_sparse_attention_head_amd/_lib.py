@@ -100,6 +100,9 @@ def lib() -> ctypes.CDLL:
         "veda_distill_grad_workspace": (c_i32, [P, c_i32, c_i32, ctypes.POINTER(c_i64)]),
         "veda_head_sq_error": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp]),
         "veda_head_sq_error_workspace": (c_i32, [P, ctypes.POINTER(c_i64)]),
+        "veda_sparse_attn_bwd": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
+                                         c_f32, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]),
+        "veda_sparse_attn_bwd_workspace": (c_i32, [P, c_i64, ctypes.POINTER(c_i64)]),
         "veda_status_string": (ctypes.c_char_p, [c_i32]),
         "veda_layout_sizeof": (c_i64, []),
     }
@@ -394,3 +397,30 @@ def veda_head_sq_error(L: veda_layout, a, b, err, workspace, ref=None, stream=No
     have = workspace.numel() * workspace.element_size()
     _check(lib().veda_head_sq_error(ctypes.byref(L), pa, pb, pe, pr, pw, have, _stream(stream)),
            "veda_head_sq_error")
+
+
+def veda_sparse_attn_bwd_workspace(L: veda_layout, nnz: int) -> int:
+    out = c_i64(0)
+    _check(lib().veda_sparse_attn_bwd_workspace(ctypes.byref(L), int(nnz), ctypes.byref(out)),
+           "veda_sparse_attn_bwd_workspace")
+    return int(out.value)
+
+
+def veda_sparse_attn_bwd(L: veda_layout, q, k, v, o, d_o, lse, row_ptr, col_idx, nnz: int,
+                         sm_scale: float, workspace, dq, dk, dv, stream=None) -> None:
+    """dQ, dK, dV (bf16 token order) of the tile-skipping attention; workspace
+    of at least veda_sparse_attn_bwd_workspace(L, nnz) bytes."""
+    torch = _torch()
+    bf = torch.bfloat16
+    n = tokens_numel(L)
+    ins = [_dev(t, name, bf, n) for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"),
+                                                (d_o, "d_o"))]
+    pl = _dev(lse, "lse", torch.float32, L.total_tiles * L.tile_size)
+    prp = _dev(row_ptr, "row_ptr", torch.int32, L.total_tiles + 1)
+    pci = _dev(col_idx, "col_idx", torch.int32, int(nnz))
+    pw = _dev(workspace, "workspace", None, 0)
+    have = workspace.numel() * workspace.element_size()
+    outs = [_dev(t, name, bf, n) for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    _check(lib().veda_sparse_attn_bwd(ctypes.byref(L), *ins, pl, prp, pci, int(nnz),
+                                      float(sm_scale), pw, have, *outs, _stream(stream)),
+           "veda_sparse_attn_bwd")

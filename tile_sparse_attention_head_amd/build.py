@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libveda.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "permute.hip", "tripool.hip", "select.hip", "sparse_attn.hip",
-           "oracle_map.hip", "distill.hip", "head_error.hip"]
+           "oracle_map.hip", "distill.hip", "head_error.hip", "sparse_attn_bwd.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

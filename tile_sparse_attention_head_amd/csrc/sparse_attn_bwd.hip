@@ -1,0 +1,475 @@
+// Backward of the tile-skipping attention: dQ, dK, dV over the same kept
+// tiles as the forward (Veda §2.3 tile-skipping kernel; the pages fine-tune
+// with the sparse path in place but give no backward kernel).  With
+// P = softmax(sm_scale Q K^T) over a query tile's kept real keys, dO the
+// output gradient and D_r = dO_r . O_r (= sum_c P_rc dP_rc):
+//
+//   dP = dO V^T,  dS = P (dP - D),  dQ = sm_scale dS K,
+//   dK = sm_scale dS^T Q,  dV = P^T dO.
+//
+// Kernels, all on the matrix cores in the forward's transposed forms:
+//  * prep: the inputs gathered into tile order (Q, K, V, dO) and
+//    tile-transposed order (Q, K, dO); per query slot D and lse*log2(e)
+//    (+inf for padding slots, so their probabilities are exactly 0); the CSR
+//    transposed (per key tile, the query tiles keeping it, ascending, found
+//    by binary search in each sorted row: deterministic, no atomics).
+//  * dQ: one workgroup per query tile, wave w owns 32 queries (Q and dO rows
+//    in registers); per 64-key step S^T = K Q^T (seeded with the mask rows),
+//    dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+//  * dK/dV: one workgroup per key tile, wave w owns 32 keys (K and V rows in
+//    registers); per 32-query step of every query tile keeping the key tile:
+//    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.  Padding query
+//    rows have P = 0; rows of padding keys are computed and never stored.
+// Steps stage their operands HBM -> LDS with buffer_load ... lds; one
+// workgroup's copies overlap the other resident workgroup's products.
+// Results are written straight to token order; every output row is written
+// once (a tile that no CSR row keeps gets dK = dV = 0, an empty row dQ = 0).
+#include "attn_common.hpp"
+
+namespace veda {
+namespace {
+
+using namespace attn;
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Row (token * heads + head) of slot u of a tile with extent e, or -1 for a
+// padding slot.
+__device__ __forceinline__ int64_t slot_row(const DevLayout& L, const TileExtent& e, int h,
+                                            int u) {
+  const int dw = u % e.pw, r = u / e.pw, dh = r % e.ph, dt = r / e.ph;
+  if (dt >= e.lt || dh >= e.lh || dw >= e.lw) return -1;
+  const int64_t tok =
+      ((int64_t)(e.it * e.pt + dt) * L.H + (e.ih * e.ph + dh)) * L.W + (e.iw * e.pw + dw);
+  return tok * L.heads + h;
+}
+
+// ---------------------------------------------------------------- prep
+// delta[g*S + u] = dO . O of the slot's token (0 for padding); lse2 = lse *
+// log2(e) for real slots, +inf for padding.  o and d_o in token order.
+__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(DevLayout L,
+                                                             const __bf16* __restrict__ o,
+                                                             const __bf16* __restrict__ d_o,
+                                                             const float* __restrict__ lse,
+                                                             float* __restrict__ delta,
+                                                             float* __restrict__ lse2) {
+  const int64_t g = blockIdx.x;
+  const int h = head_of_tile(L, g);
+  const TileExtent e = tile_extent(L, h, (int)(g - L.tile_off[h]));
+  const int cpr = L.d / 8;                  // 16-byte chunks per row (a power of two)
+  const int rpp = kThreads / cpr;
+  const int c = threadIdx.x % cpr;
+  for (int u0 = 0; u0 < L.S; u0 += rpp) {
+    const int u = u0 + (int)threadIdx.x / cpr;
+    const int64_t row = u < L.S ? slot_row(L, e, h, u) : -1;
+    float acc = 0.f;
+    if (row >= 0) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * L.d + 8 * c);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(d_o + row * L.d + 8 * c);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc = fmaf((float)a[x], (float)b[x], acc);
+    }
+    for (int off = cpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (u < L.S && c == 0) {
+      const int64_t slot = g * L.S + u;
+      delta[slot] = acc;
+      lse2[slot] = row >= 0 ? lse[slot] * kLog2e : INFINITY;
+    }
+  }
+}
+
+// occurrences of j in the ascending entries [b, e) of col_idx
+__device__ __forceinline__ int count_in_row(const int32_t* __restrict__ ci, int b, int e, int j) {
+  int lo = b, hi = e;
+  while (lo < hi) {                     // first entry >= j
+    const int m = (lo + hi) >> 1;
+    if (ci[m] < j) lo = m + 1; else hi = m;
+  }
+  int lo2 = lo, hi2 = e;
+  while (lo2 < hi2) {                   // first entry > j
+    const int m = (lo2 + hi2) >> 1;
+    if (ci[m] <= j) lo2 = m + 1; else hi2 = m;
+  }
+  return lo2 - lo;
+}
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < kThreads / 64; ++w) {
+    if (w < wave) base += wave_tot[w];
+    tot += wave_tot[w];
+  }
+  *total = tot;
+  return base + incl - v;
+}
+
+// per key tile g: how many (query tile, occurrence) pairs keep it
+__global__ __launch_bounds__(kThreads) void csrt_count_kernel(DevLayout L,
+                                                              const int32_t* __restrict__ rp,
+                                                              const int32_t* __restrict__ ci,
+                                                              int32_t* __restrict__ cnt) {
+  __shared__ int wave_tot[kThreads / 64];
+  const int64_t g = blockIdx.x;
+  const int h = head_of_tile(L, g);
+  const int64_t off = L.tile_off[h];
+  const int n = (int)(L.tile_off[h + 1] - off), j = (int)(g - off);
+  int c = 0;
+  for (int i = threadIdx.x; i < n; i += kThreads)
+    c += count_in_row(ci, rp[off + i], rp[off + i + 1], j);
+  int tot = 0;
+  block_exclusive_scan(c, wave_tot, &tot);
+  if (threadIdx.x == 0) cnt[g] = tot;
+}
+
+// ptr[g] = sum of cnt[0..g), ptr[tiles] = total: one workgroup, chunks in order
+__global__ __launch_bounds__(kThreads) void csrt_scan_kernel(int64_t tiles,
+                                                             const int32_t* __restrict__ cnt,
+                                                             int32_t* __restrict__ ptr) {
+  __shared__ int wave_tot[kThreads / 64];
+  int carry = 0;
+  for (int64_t x0 = 0; x0 < tiles; x0 += kThreads) {
+    const int64_t x = x0 + threadIdx.x;
+    const int v = x < tiles ? cnt[x] : 0;
+    int tot = 0;
+    const int ex = block_exclusive_scan(v, wave_tot, &tot);
+    if (x < tiles) ptr[x] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) ptr[tiles] = carry;
+}
+
+// rowt[ptr[g] ..] = the head-local query tiles keeping key tile g, ascending
+// (a tile kept twice by one row appears twice).  Writes stay below `cap`
+// (the CSR's entry count) even for rows that are not sorted.
+__global__ __launch_bounds__(kThreads) void csrt_fill_kernel(DevLayout L,
+                                                             const int32_t* __restrict__ rp,
+                                                             const int32_t* __restrict__ ci,
+                                                             const int32_t* __restrict__ ptr,
+                                                             int32_t cap,
+                                                             int32_t* __restrict__ rowt) {
+  __shared__ int wave_tot[kThreads / 64];
+  const int64_t g = blockIdx.x;
+  const int h = head_of_tile(L, g);
+  const int64_t off = L.tile_off[h];
+  const int n = (int)(L.tile_off[h + 1] - off), j = (int)(g - off);
+  int base = ptr[g];
+  for (int i0 = 0; i0 < n; i0 += kThreads) {
+    const int i = i0 + threadIdx.x;
+    const int c = i < n ? count_in_row(ci, rp[off + i], rp[off + i + 1], j) : 0;
+    int tot = 0;
+    const int ex = block_exclusive_scan(c, wave_tot, &tot);
+    for (int r = 0; r < c; ++r)
+      if (base + ex + r < cap) rowt[base + ex + r] = i;
+    base += tot;
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D, int S>
+__global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
+    DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const __bf16* __restrict__ kt, const __bf16* __restrict__ d_o,
+    const float* __restrict__ lse2, const float* __restrict__ delta,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, float scale_log2,
+    float sm_scale, __bf16* __restrict__ dq) {
+  constexpr int NW = S / 32, SK = 64, SPT = S / SK, KS = D / 16, DB = D / 32, TILE = S * D * 2;
+  using KR = StepBuf<SK, D / 8, true, D * 2, NW>;      // K or V rows of a step, swap23 order
+  using KT = StepBuf<D, SK / 8, false, S * 2, NW>;     // K^T: D rows of the step's 64 keys
+  __shared__ __attribute__((aligned(1024))) unsigned char k_s[KR::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_s[KR::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char kt_s[KT::BYTES];
+  __shared__ BiasTable<SPT, 9> btab;
+
+  const int64_t g = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = head_of_tile(L, g);
+  const int64_t head_base = L.tile_off[h];
+  const int n_h = (int)(L.tile_off[h + 1] - head_base);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hf = lane >> 5;
+  const int64_t qrow = g * S + wave * 32 + n;
+
+  bf16x8 qr[KS], dor[KS];
+  load_q_regs<D>(qr, q + qrow * D, hf);
+  load_q_regs<D>(dor, d_o + qrow * D, hf);
+  const float l2 = lse2[qrow], dl = delta[qrow];
+
+  cint32* rp = (cint32*)row_ptr;
+  cint32* cp = (cint32*)col_idx;
+  int beg = rp[g], end = rp[g + 1];
+  if (end < beg) end = beg;
+  const int N = (end - beg) * SPT;
+  const unsigned char* kb = reinterpret_cast<const unsigned char*>(k) + head_base * TILE;
+  const unsigned char* vb = reinterpret_cast<const unsigned char*>(v) + head_base * TILE;
+  const unsigned char* ktb = reinterpret_cast<const unsigned char*>(kt) + head_base * TILE;
+  const auto krs = make_rsrc(kb, (int64_t)n_h * TILE);
+  const auto vrs = make_rsrc(vb, (int64_t)n_h * TILE);
+  const auto ktrs = make_rsrc(ktb, (int64_t)n_h * TILE);
+  uint32_t ro[KR::PER_WAVE], to[KT::PER_WAVE];
+  KR::offsets(ro, wave, lane);
+  KT::offsets(to, wave, lane);
+  build_bias_table<SPT, 9>(btab, L, h, tid, 2 * S);
+
+  f32x16 dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
+
+  for (int s = 0; s < N; ++s) {
+    const int c = cp[beg + s / SPT];
+    const bool ok = c >= 0 && c < n_h;
+    const int cut = ok ? cut_of(tile_extent(L, h, c)) : 8;
+    const int cc = ok ? c : 0;
+    KR::copy(krs, (uint32_t)(cc * TILE + (s % SPT) * SK * D * 2), k_s, ro, wave);
+    KR::copy(vrs, (uint32_t)(cc * TILE + (s % SPT) * SK * D * 2), v_s, ro, wave);
+    KT::copy(ktrs, (uint32_t)(cc * TILE + (s % SPT) * SK * 2), kt_s, to, wave);
+    wait_all();
+    __syncthreads();
+    f32x16 st[2], dpt[2];
+    load_bias(st, &btab.v[cut][s % SPT][0][hf][0]);
+    dpt[0] = f32x16{};
+    dpt[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        st[b] = mfma32(KR::read(k_s, b * 32 + n, 2 * kk + hf), qr[kk], st[b]);
+        dpt[b] = mfma32(KR::read(v_s, b * 32 + n, 2 * kk + hf), dor[kk], dpt[b]);
+      }
+    // element i of block b is key 32b + 16(i/8) + 8hf + i%8 of the step
+    bf16x8 ds[4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2f(fmaf(st[b][i], scale_log2, -l2));
+        ds[2 * b + i / 8][i % 8] = (__bf16)(p * (dpt[b][i] - dl));
+      }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        dqa[db] = mfma32(KT::read(kt_s, db * 32 + n, 2 * t + hf), ds[t], dqa[db]);
+    __syncthreads();   // every wave is past its reads before the next copies
+  }
+
+  const TileExtent e = tile_extent(L, h, (int)(g - head_base));
+  const int64_t row = slot_row(L, e, h, wave * 32 + n);
+  if (row >= 0) {
+    __bf16* out = dq + row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 w;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) w[b] = (__bf16)(dqa[db][4 * a + b] * sm_scale);
+        *reinterpret_cast<bf16x4*>(out + db * 32 + 8 * a + 4 * hf) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D, int S>
+__global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
+    DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ qt,
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
+    const __bf16* __restrict__ dot, const float* __restrict__ lse2,
+    const float* __restrict__ delta, const int32_t* __restrict__ colt_ptr,
+    const int32_t* __restrict__ rowt, int32_t cap, float scale_log2, float sm_scale,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
+  constexpr int NW = S / 32, SQ = 32, SPQ = S / SQ, KS = D / 16, DB = D / 32, TILE = S * D * 2;
+  using QR = StepBuf<SQ, D / 8, true, D * 2, NW>;      // Q or dO rows of a step, swap23 order
+  using QT = StepBuf<D, SQ / 8, false, S * 2, NW>;     // Q^T or dO^T: D rows of 32 queries
+  __shared__ __attribute__((aligned(1024))) unsigned char q_s[QR::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char do_s[QR::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char qt_s[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char dot_s[QT::BYTES];
+  __shared__ float l2_s[SQ], dl_s[SQ];
+
+  const int64_t g = xcd_remap(blockIdx.x, gridDim.x);   // key tile
+  const int h = head_of_tile(L, g);
+  const int64_t head_base = L.tile_off[h];
+  const int n_h = (int)(L.tile_off[h + 1] - head_base);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hf = lane >> 5;
+  const int64_t krow = g * S + wave * 32 + n;
+
+  bf16x8 kr[KS], vr[KS];
+  load_q_regs<D>(kr, k + krow * D, hf);
+  load_q_regs<D>(vr, v + krow * D, hf);
+
+  cint32* cpt = (cint32*)colt_ptr;
+  cint32* rt = (cint32*)rowt;
+  const int a0 = min(cpt[g], cap), a1 = max(a0, min(cpt[g + 1], cap));
+  const int N = (a1 - a0) * SPQ;
+  auto rs = [&](const __bf16* base) {
+    return make_rsrc(reinterpret_cast<const unsigned char*>(base) + head_base * TILE,
+                     (int64_t)n_h * TILE);
+  };
+  const auto qrs = rs(q), dors = rs(d_o), qtrs = rs(qt), dotrs = rs(dot);
+  uint32_t ro[QR::PER_WAVE], to[QT::PER_WAVE];
+  QR::offsets(ro, wave, lane);
+  QT::offsets(to, wave, lane);
+
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+
+  for (int s = 0; s < N; ++s) {
+    const int i = min(max(rt[a0 + s / SPQ], 0), n_h - 1);   // head-local query tile
+    const int qs = s % SPQ;
+    const uint32_t rof = (uint32_t)(i * TILE + qs * SQ * D * 2);
+    const uint32_t tof = (uint32_t)(i * TILE + qs * SQ * 2);
+    QR::copy(qrs, rof, q_s, ro, wave);
+    QR::copy(dors, rof, do_s, ro, wave);
+    QT::copy(qtrs, tof, qt_s, to, wave);
+    QT::copy(dotrs, tof, dot_s, to, wave);
+    if (tid < SQ) {
+      const int64_t slot = (head_base + i) * S + qs * SQ + tid;
+      l2_s[tid] = lse2[slot];
+      dl_s[tid] = delta[slot];
+    }
+    wait_all();
+    __syncthreads();
+    f32x16 sa = f32x16{}, dpa = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      sa = mfma32(QR::read(q_s, n, 2 * kk + hf), kr[kk], sa);
+      dpa = mfma32(QR::read(do_s, n, 2 * kk + hf), vr[kk], dpa);
+    }
+    // element i is query 16(i/8) + 8hf + i%8 of the step
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int qq = 16 * (x / 8) + 8 * hf + (x % 8);
+      const float p = exp2f(fmaf(sa[x], scale_log2, -l2_s[qq]));
+      pb[x / 8][x % 8] = (__bf16)p;
+      dsb[x / 8][x % 8] = (__bf16)(p * (dpa[x] - dl_s[qq]));
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dva[db] = mfma32(QT::read(dot_s, db * 32 + n, 2 * t + hf), pb[t], dva[db]);
+        dka[db] = mfma32(QT::read(qt_s, db * 32 + n, 2 * t + hf), dsb[t], dka[db]);
+      }
+    __syncthreads();
+  }
+
+  const TileExtent e = tile_extent(L, h, (int)(g - head_base));
+  const int64_t row = slot_row(L, e, h, wave * 32 + n);
+  if (row >= 0) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 wk, wv;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          wk[b] = (__bf16)(dka[db][4 * a + b] * sm_scale);
+          wv[b] = (__bf16)dva[db][4 * a + b];
+        }
+        *reinterpret_cast<bf16x4*>(dk + row * D + db * 32 + 8 * a + 4 * hf) = wk;
+        *reinterpret_cast<bf16x4*>(dv + row * D + db * 32 + 8 * a + 4 * hf) = wv;
+      }
+  }
+}
+
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+struct BwdWs {
+  void *qp, *kp, *vp, *dop, *qtp, *ktp, *dotp;
+  float *lse2, *delta;
+  int32_t *cnt, *colt_ptr, *rowt;
+};
+
+BwdWs carve(const DevLayout& L, int64_t nnz, void* base, int64_t* total) {
+  BwdWs w;
+  char* p = static_cast<char*>(base);
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) -> void* {
+    void* q = p ? p + o : nullptr;
+    o += round256(bytes);
+    return q;
+  };
+  const int64_t tiles = L.tile_off[L.heads];
+  const int64_t tb = tiles * L.S * L.d * 2;
+  w.qp = take(tb); w.kp = take(tb); w.vp = take(tb); w.dop = take(tb);
+  w.qtp = take(tb); w.ktp = take(tb); w.dotp = take(tb);
+  w.lse2 = static_cast<float*>(take(tiles * L.S * 4));
+  w.delta = static_cast<float*>(take(tiles * L.S * 4));
+  w.cnt = static_cast<int32_t*>(take(tiles * 4));
+  w.colt_ptr = static_cast<int32_t*>(take((tiles + 1) * 4));
+  w.rowt = static_cast<int32_t*>(take(nnz * 4 + 4));
+  *total = o;
+  return w;
+}
+
+template <int D, int S>
+void launch_products(const DevLayout& L, const BwdWs& w, const int32_t* row_ptr,
+                     const int32_t* col_idx, int32_t cap, float sm_scale, void* dq, void* dk,
+                     void* dv, hipStream_t s) {
+  const unsigned G = (unsigned)L.tile_off[L.heads];
+  const float sl2 = sm_scale * kLog2e;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, S>), dim3(G), dim3(2 * S), 0, s, L,
+                     (const __bf16*)w.qp, (const __bf16*)w.kp, (const __bf16*)w.vp,
+                     (const __bf16*)w.ktp, (const __bf16*)w.dop, w.lse2, w.delta, row_ptr, col_idx,
+                     sl2, sm_scale, (__bf16*)dq);
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, S>), dim3(G), dim3(2 * S), 0, s, L,
+                     (const __bf16*)w.qp, (const __bf16*)w.qtp, (const __bf16*)w.kp,
+                     (const __bf16*)w.vp, (const __bf16*)w.dop, (const __bf16*)w.dotp, w.lse2,
+                     w.delta, w.colt_ptr, w.rowt, cap, sl2, sm_scale, (__bf16*)dk, (__bf16*)dv);
+}
+
+}  // namespace
+
+int64_t attn_bwd_workspace_bytes(const DevLayout& L, int64_t nnz) {
+  int64_t total = 0;
+  carve(L, nnz, nullptr, &total);
+  return total;
+}
+
+int launch_sparse_attn_bwd(const DevLayout& L, const void* q, const void* k, const void* v,
+                           const void* o, const void* d_o, const float* lse,
+                           const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                           float sm_scale, void* workspace, void* dq, void* dk, void* dv,
+                           hipStream_t s) {
+  const int64_t tiles = L.tile_off[L.heads];
+  if (tiles == 0) return VEDA_OK;
+  int64_t total = 0;
+  const BwdWs w = carve(L, nnz, workspace, &total);
+  const struct { const void* x; void* y; int dir; } perms[] = {
+      {q, w.qp, VEDA_FWD}, {k, w.kp, VEDA_FWD}, {v, w.vp, VEDA_FWD}, {d_o, w.dop, VEDA_FWD},
+      {q, w.qtp, VEDA_FWD_T}, {k, w.ktp, VEDA_FWD_T}, {d_o, w.dotp, VEDA_FWD_T}};
+  for (const auto& p : perms)
+    if (launch_permute(L, VEDA_BF16, p.dir, p.x, p.y, s) != VEDA_OK) return VEDA_ERR_LAUNCH;
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L,
+                     (const __bf16*)o, (const __bf16*)d_o, lse, w.delta, w.lse2);
+  hipLaunchKernelGGL(csrt_count_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L, row_ptr,
+                     col_idx, w.cnt);
+  hipLaunchKernelGGL(csrt_scan_kernel, dim3(1), dim3(kThreads), 0, s, tiles, w.cnt, w.colt_ptr);
+  hipLaunchKernelGGL(csrt_fill_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L, row_ptr,
+                     col_idx, w.colt_ptr, (int32_t)nnz, w.rowt);
+  if (L.d == 128)
+    launch_products<128, 128>(L, w, row_ptr, col_idx, (int32_t)nnz, sm_scale, dq, dk, dv, s);
+  else
+    launch_products<64, 64>(L, w, row_ptr, col_idx, (int32_t)nnz, sm_scale, dq, dk, dv, s);
+  return launch_status();
+}
+
+}  // namespace veda

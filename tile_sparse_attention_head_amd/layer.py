@@ -15,8 +15,9 @@ runs the fused sequence:
 ``forward_unfused`` runs the same method one step per call (permute,
 veda_tripool_score, select, veda_sparse_attn_fwd, inverse permute); both give
 identical results.  ``maxpool_map`` runs veda_oracle_maxpool_map for a subset
-of query tiles, and ``distill_grad`` the estimator's distillation step
-(veda_distill_grad) against that map.  All calls go on the current torch stream without
+of query tiles, ``distill_grad`` the estimator's distillation step
+(veda_distill_grad) against that map, and ``backward`` the attention's
+gradients (veda_sparse_attn_bwd).  All calls go on the current torch stream without
 synchronising.
 """
 from __future__ import annotations
@@ -52,6 +53,7 @@ class TileSparseAttention:
         self.lse = torch.empty(L.total_tiles * tile_size, dtype=f32, device=dev)
         self._map_ws = None   # veda_oracle_maxpool_map workspace, sized on first use
         self._distill_ws = None   # veda_distill_grad workspace, sized on first use
+        self._bwd_ws = None       # veda_sparse_attn_bwd workspace, sized on first use
         self.desc = torch.empty(2 * L.total_tiles * 3 * head_dim, dtype=f32, device=dev)
         self.phi = torch.empty(2 * L.total_tiles * self.d_e, dtype=f32, device=dev)
         self.scores = torch.empty(L.total_scores, dtype=f32, device=dev)
@@ -121,6 +123,20 @@ class TileSparseAttention:
         self.attend(sm_scale, True, stream)
         self.unpermute(out, stream)
         return out
+
+    def backward(self, q, k, v, out, d_out, sm_scale: float, grads=None, stream=None):
+        """dQ, dK, dV (token order) of the last ``forward`` (its inputs q, k,
+        v and output ``out``, its lse and CSR still in this layer) for the
+        output gradient ``d_out``."""
+        torch = self.torch
+        if grads is None:
+            grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        need = V.veda_sparse_attn_bwd_workspace(self.L, self.nnz)
+        if getattr(self, "_bwd_ws", None) is None or self._bwd_ws.numel() < need:
+            self._bwd_ws = torch.empty(max(16, need), dtype=torch.uint8, device=q.device)
+        V.veda_sparse_attn_bwd(self.L, q, k, v, out, d_out, self.lse, self.row_ptr, self.col_idx,
+                               self.nnz, sm_scale, self._bwd_ws, *grads, stream=stream)
+        return grads
 
     def maxpool_map(self, q_tiles, sm_scale: float, lse=None, out_map=None, stream=None):
         """Max-pooled map of the query tiles ``q_tiles`` (int32 global tile
