@@ -263,6 +263,30 @@ class Bench:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    def time_backward(self, reps: int = 5):
+        """The attention backward (veda_sparse_attn_bwd) of the last step's
+        forward, for a seeded output gradient: mean ms over ``reps`` calls."""
+        torch = self.torch
+        rng = np.random.default_rng(1)
+        import workloads
+        g = workloads.bf16_round(rng.normal(size=tuple(self.q.shape)).astype(np.float32))
+        d_out = torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).to(self.q.device)
+        sm = self.cfg.sm_scale
+        grads = self.layer.backward(self.q, self.k, self.v, self.out, d_out, sm)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            self.layer.backward(self.q, self.k, self.v, self.out, d_out, sm, grads=grads)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def backward_flops(self):
+        """Five S x S x d products per kept pair (S recomputed once, dP, dQ,
+        dK, dV): 10 S^2 d.  The kernels execute 14 S^2 d (S and dP in both)."""
+        return 10.0 * self.cfg.tile_size ** 2 * self.cfg.head_dim * self.pairs
+
     def valid_flops_c(self):
         """4*d*sum over kept pairs of |real query slots| * |real key slots|."""
         L, d = self.L, self.cfg.head_dim
@@ -382,6 +406,9 @@ def main():
                     help="skip the 95 %% and 0 %% (dense) context runs")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one torch copy of this many MiB (counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the step: time the attention backward of the workload "
+                         "(--steps calls after one forward step); prints one JSON line")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: attention at 95%% and 0%% over the 720P "
                          "241-frame layer at T = 9, 18, 36, 61 frames, and the map on the "
@@ -399,6 +426,16 @@ def main():
 
     if args.sweep:
         print(json.dumps(sweep()))
+        return
+    if args.backward:
+        bb = Bench(args.workload, args.sparsity)
+        bb.run(1, args.warmup, with_map=False)
+        ms = bb.time_backward(args.steps)
+        print(json.dumps({"workload": args.workload, "sparsity_pct": args.sparsity,
+                          "backward_ms": ms, "kept_pairs": bb.pairs,
+                          "tflops": bb.backward_flops() / (ms * 1e-3) / 1e12,
+                          "frac_peak": bb.backward_flops() / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                          "forward_attn_ms_for_reference": None}))
         return
 
     b = Bench(args.workload, args.sparsity)
@@ -444,6 +481,12 @@ def main():
                  + 2.0 * 3 * cfg.head_dim * de * (n_sub + L.total_tiles))
         context["distill"] = {"ms": dms, "subset_tiles": n_sub, "gflop": flops / 1e9,
                               "tflops": flops / (dms * 1e-3) / 1e12}
+        # attention backward of this step's forward
+        bms = b.time_backward()
+        context["backward"] = {
+            "ms": bms, "tflops": b.backward_flops() / (bms * 1e-3) / 1e12,
+            "frac_peak": b.backward_flops() / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "flops_per_pair": "10 S^2 d (S recomputed once, dP, dQ, dK, dV)"}
         # head-aware tiling search over the four 128-slot shapes on this layer:
         # full attention once, then the fused layer and the per-head error for
         # each shape (wall time, buffers allocated per candidate included)

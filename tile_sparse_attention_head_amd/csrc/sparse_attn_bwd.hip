@@ -252,7 +252,7 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(fmaf(st[b][i], scale_log2, -l2));
+        const float p = exp2_(fmaf(st[b][i], scale_log2, -l2));
         ds[2 * b + i / 8][i % 8] = (__bf16)(p * (dpt[b][i] - dl));
       }
 #pragma unroll
@@ -291,11 +291,13 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
   constexpr int NW = S / 32, SQ = 32, SPQ = S / SQ, KS = D / 16, DB = D / 32, TILE = S * D * 2;
   using QR = StepBuf<SQ, D / 8, true, D * 2, NW>;      // Q or dO rows of a step, swap23 order
   using QT = StepBuf<D, SQ / 8, false, S * 2, NW>;     // Q^T or dO^T: D rows of 32 queries
-  __shared__ __attribute__((aligned(1024))) unsigned char q_s[QR::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char do_s[QR::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char qt_s[QT::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char dot_s[QT::BYTES];
-  __shared__ float l2_s[SQ], dl_s[SQ];
+  // two of everything: the copies of step s+1 land while step s computes
+  __shared__ __attribute__((aligned(1024))) unsigned char q_s[2][QR::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char do_s[2][QR::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char qt_s[2][QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char dot_s[2][QT::BYTES];
+  __shared__ __attribute__((aligned(16))) float l2_s[2][SQ];
+  __shared__ __attribute__((aligned(16))) float dl_s[2][SQ];
 
   const int64_t g = xcd_remap(blockIdx.x, gridDim.x);   // key tile
   const int h = head_of_tile(L, g);
@@ -319,9 +321,32 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
                      (int64_t)n_h * TILE);
   };
   const auto qrs = rs(q), dors = rs(d_o), qtrs = rs(qt), dotrs = rs(dot);
+  const auto l2rs = make_rsrc(lse2 + head_base * S, (int64_t)n_h * S * 4);
+  const auto dlrs = make_rsrc(delta + head_base * S, (int64_t)n_h * S * 4);
   uint32_t ro[QR::PER_WAVE], to[QT::PER_WAVE];
   QR::offsets(ro, wave, lane);
   QT::offsets(to, wave, lane);
+
+  // copies of step s into buffer b
+  auto stage = [&](int s, int b) {
+    const int i = min(max(rt[a0 + s / SPQ], 0), n_h - 1);   // head-local query tile
+    const int qs = s % SPQ;
+    const uint32_t rof = (uint32_t)(i * TILE + qs * SQ * D * 2);
+    const uint32_t tof = (uint32_t)(i * TILE + qs * SQ * 2);
+    QR::copy(qrs, rof, q_s[b], ro, wave);
+    QR::copy(dors, rof, do_s[b], ro, wave);
+    QT::copy(qtrs, tof, qt_s[b], to, wave);
+    QT::copy(dotrs, tof, dot_s[b], to, wave);
+    // the step's 32 lse2 and D values: 8 lanes x 16 bytes through the same
+    // LDS copy path (no register round trip, no wait of its own)
+    if (wave == 0 && lane < SQ / 4) {
+      const uint32_t so = (uint32_t)((i * S + qs * SQ) * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(l2rs, (lds_void*)&l2_s[b][0], 16, lane * 16, so, 0,
+                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(dlrs, (lds_void*)&dl_s[b][0], 16, lane * 16, so, 0,
+                                               0);
+    }
+  };
 
   f32x16 dka[DB], dva[DB];
 #pragma unroll
@@ -330,45 +355,53 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     dva[db] = f32x16{};
   }
 
+  if (N > 0) stage(0, 0);
   for (int s = 0; s < N; ++s) {
-    const int i = min(max(rt[a0 + s / SPQ], 0), n_h - 1);   // head-local query tile
-    const int qs = s % SPQ;
-    const uint32_t rof = (uint32_t)(i * TILE + qs * SQ * D * 2);
-    const uint32_t tof = (uint32_t)(i * TILE + qs * SQ * 2);
-    QR::copy(qrs, rof, q_s, ro, wave);
-    QR::copy(dors, rof, do_s, ro, wave);
-    QT::copy(qtrs, tof, qt_s, to, wave);
-    QT::copy(dotrs, tof, dot_s, to, wave);
-    if (tid < SQ) {
-      const int64_t slot = (head_base + i) * S + qs * SQ + tid;
-      l2_s[tid] = lse2[slot];
-      dl_s[tid] = delta[slot];
-    }
+    const int b = s & 1;
+    // step s's copies landed (own: the wait; everyone's: the barrier), and
+    // every wave is past its reads of step s-1, whose buffer the next copies
+    // overwrite
     wait_all();
     __syncthreads();
+    if (s + 1 < N) stage(s + 1, b ^ 1);
+    const unsigned char* qb = q_s[b];
+    const unsigned char* dob = do_s[b];
+    const unsigned char* qtb = qt_s[b];
+    const unsigned char* dotb = dot_s[b];
     f32x16 sa = f32x16{}, dpa = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      sa = mfma32(QR::read(q_s, n, 2 * kk + hf), kr[kk], sa);
-      dpa = mfma32(QR::read(do_s, n, 2 * kk + hf), vr[kk], dpa);
+      sa = mfma32(QR::read(qb, n, 2 * kk + hf), kr[kk], sa);
+      dpa = mfma32(QR::read(dob, n, 2 * kk + hf), vr[kk], dpa);
     }
-    // element i is query 16(i/8) + 8hf + i%8 of the step
+    // element x is query 16(x/8) + 8hf + x%8 of the step: its lse2 and D
+    // are two runs of 8 consecutive floats, read as four 16-byte vectors each
+    float l2v[16], dlv[16];
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int q0 = 16 * (v4 / 2) + 8 * hf + 4 * (v4 % 2);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&l2_s[b][q0]);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(&dl_s[b][q0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        l2v[4 * v4 + e] = a[e];
+        dlv[4 * v4 + e] = c[e];
+      }
+    }
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const int qq = 16 * (x / 8) + 8 * hf + (x % 8);
-      const float p = exp2f(fmaf(sa[x], scale_log2, -l2_s[qq]));
+      const float p = exp2_(fmaf(sa[x], scale_log2, -l2v[x]));
       pb[x / 8][x % 8] = (__bf16)p;
-      dsb[x / 8][x % 8] = (__bf16)(p * (dpa[x] - dl_s[qq]));
+      dsb[x / 8][x % 8] = (__bf16)(p * (dpa[x] - dlv[x]));
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dva[db] = mfma32(QT::read(dot_s, db * 32 + n, 2 * t + hf), pb[t], dva[db]);
-        dka[db] = mfma32(QT::read(qt_s, db * 32 + n, 2 * t + hf), dsb[t], dka[db]);
+        dva[db] = mfma32(QT::read(dotb, db * 32 + n, 2 * t + hf), pb[t], dva[db]);
+        dka[db] = mfma32(QT::read(qtb, db * 32 + n, 2 * t + hf), dsb[t], dka[db]);
       }
-    __syncthreads();
   }
 
   const TileExtent e = tile_extent(L, h, (int)(g - head_base));
