@@ -508,7 +508,7 @@ def main():
             if s == args.sparsity:
                 continue
             c = Bench(args.workload, s)
-            w2, sm2, _ = c.run(max(3, args.steps // 4), 2, with_map=False)
+            w2, sm2, _ = c.run(max(10, args.steps // 2), 3, with_map=False)
             d2 = dict(zip(names, [float(x) for x in sm2]))
             a_ms = d2["sparse_attn"]
             context[f"sparsity_{s}"] = {

@@ -46,14 +46,21 @@ __device__ __forceinline__ int64_t slot_row(const DevLayout& L, const TileExtent
 }
 
 // ---------------------------------------------------------------- prep
-// delta[g*S + u] = dO . O of the slot's token (0 for padding); lse2 = lse *
-// log2(e) for real slots, +inf for padding.  o and d_o in token order.
+// Per query slot, from the slot's token (o and d_o in token order):
+//   delta = dO . O,  lse2 = lse * log2(e)           (dQ kernel)
+//   seed_s = -lse / sm_scale,  seed_dp = -delta     (dK/dV kernel: the initial
+//   values of its S and dP accumulators, so that P = exp2(sm_scale log2(e) S)
+//   and dS = P dP with no further per-element work)
+// Padding slots: delta = 0, lse2 = +inf, seed_s = -inf (probabilities 0).
 __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(DevLayout L,
                                                              const __bf16* __restrict__ o,
                                                              const __bf16* __restrict__ d_o,
                                                              const float* __restrict__ lse,
+                                                             float sm_scale,
                                                              float* __restrict__ delta,
-                                                             float* __restrict__ lse2) {
+                                                             float* __restrict__ lse2,
+                                                             float* __restrict__ seed_s,
+                                                             float* __restrict__ seed_dp) {
   const int64_t g = blockIdx.x;
   const int h = head_of_tile(L, g);
   const TileExtent e = tile_extent(L, h, (int)(g - L.tile_off[h]));
@@ -75,6 +82,8 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(DevLayout L,
       const int64_t slot = g * L.S + u;
       delta[slot] = acc;
       lse2[slot] = row >= 0 ? lse[slot] * kLog2e : INFINITY;
+      seed_s[slot] = row >= 0 ? -lse[slot] / sm_scale : -INFINITY;
+      seed_dp[slot] = -acc;
     }
   }
 }
@@ -284,20 +293,22 @@ template <int D, int S>
 __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ qt,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
-    const __bf16* __restrict__ dot, const float* __restrict__ lse2,
-    const float* __restrict__ delta, const int32_t* __restrict__ colt_ptr,
+    const __bf16* __restrict__ dot, const float* __restrict__ seed_s,
+    const float* __restrict__ seed_dp, const int32_t* __restrict__ colt_ptr,
     const int32_t* __restrict__ rowt, int32_t cap, float scale_log2, float sm_scale,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
   constexpr int NW = S / 32, SQ = 32, SPQ = S / SQ, KS = D / 16, DB = D / 32, TILE = S * D * 2;
   using QR = StepBuf<SQ, D / 8, true, D * 2, NW>;      // Q or dO rows of a step, swap23 order
   using QT = StepBuf<D, SQ / 8, false, S * 2, NW>;     // Q^T or dO^T: D rows of 32 queries
-  // two of everything: the copies of step s+1 land while step s computes
-  __shared__ __attribute__((aligned(1024))) unsigned char q_s[2][QR::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char do_s[2][QR::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char qt_s[2][QT::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char dot_s[2][QT::BYTES];
-  __shared__ __attribute__((aligned(16))) float l2_s[2][SQ];
-  __shared__ __attribute__((aligned(16))) float dl_s[2][SQ];
+  // two of everything: the copies of step s+1 land while step s computes.
+  // Separate objects per parity, chosen at compile time, so that the reads of
+  // one buffer are never ordered after the copies into the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char q_s0[QR::BYTES], q_s1[QR::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char do_s0[QR::BYTES], do_s1[QR::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char qt_s0[QT::BYTES], qt_s1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char dot_s0[QT::BYTES], dot_s1[QT::BYTES];
+  // the step's seeds of its S and dP accumulators (-lse/sm_scale, -D)
+  __shared__ __attribute__((aligned(16))) float ss_s0[SQ], ss_s1[SQ], sd_s0[SQ], sd_s1[SQ];
 
   const int64_t g = xcd_remap(blockIdx.x, gridDim.x);   // key tile
   const int h = head_of_tile(L, g);
@@ -321,30 +332,35 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
                      (int64_t)n_h * TILE);
   };
   const auto qrs = rs(q), dors = rs(d_o), qtrs = rs(qt), dotrs = rs(dot);
-  const auto l2rs = make_rsrc(lse2 + head_base * S, (int64_t)n_h * S * 4);
-  const auto dlrs = make_rsrc(delta + head_base * S, (int64_t)n_h * S * 4);
+  const auto ssrs = make_rsrc(seed_s + head_base * S, (int64_t)n_h * S * 4);
+  const auto sdrs = make_rsrc(seed_dp + head_base * S, (int64_t)n_h * S * 4);
   uint32_t ro[QR::PER_WAVE], to[QT::PER_WAVE];
   QR::offsets(ro, wave, lane);
   QT::offsets(to, wave, lane);
 
-  // copies of step s into buffer b
-  auto stage = [&](int s, int b) {
+  // copies of step s into the buffers of parity PAR
+  auto stage = [&](int s, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    unsigned char* qb = PAR ? q_s1 : q_s0;
+    unsigned char* dob = PAR ? do_s1 : do_s0;
+    unsigned char* qtb = PAR ? qt_s1 : qt_s0;
+    unsigned char* dotb = PAR ? dot_s1 : dot_s0;
+    float* ssb = PAR ? ss_s1 : ss_s0;
+    float* sdb = PAR ? sd_s1 : sd_s0;
     const int i = min(max(rt[a0 + s / SPQ], 0), n_h - 1);   // head-local query tile
     const int qs = s % SPQ;
     const uint32_t rof = (uint32_t)(i * TILE + qs * SQ * D * 2);
     const uint32_t tof = (uint32_t)(i * TILE + qs * SQ * 2);
-    QR::copy(qrs, rof, q_s[b], ro, wave);
-    QR::copy(dors, rof, do_s[b], ro, wave);
-    QT::copy(qtrs, tof, qt_s[b], to, wave);
-    QT::copy(dotrs, tof, dot_s[b], to, wave);
-    // the step's 32 lse2 and D values: 8 lanes x 16 bytes through the same
-    // LDS copy path (no register round trip, no wait of its own)
+    QR::copy(qrs, rof, qb, ro, wave);
+    QR::copy(dors, rof, dob, ro, wave);
+    QT::copy(qtrs, tof, qtb, to, wave);
+    QT::copy(dotrs, tof, dotb, to, wave);
+    // the step's 32 + 32 seeds: 8 lanes x 16 bytes each through the same LDS
+    // copy path (no register round trip, no wait of its own)
     if (wave == 0 && lane < SQ / 4) {
       const uint32_t so = (uint32_t)((i * S + qs * SQ) * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(l2rs, (lds_void*)&l2_s[b][0], 16, lane * 16, so, 0,
-                                               0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(dlrs, (lds_void*)&dl_s[b][0], 16, lane * 16, so, 0,
-                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ssrs, (lds_void*)ssb, 16, lane * 16, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sdrs, (lds_void*)sdb, 16, lane * 16, so, 0, 0);
     }
   };
 
@@ -355,45 +371,47 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     dva[db] = f32x16{};
   }
 
-  if (N > 0) stage(0, 0);
-  for (int s = 0; s < N; ++s) {
-    const int b = s & 1;
+  using Z = std::integral_constant<int, 0>;
+  using O1 = std::integral_constant<int, 1>;
+  auto step = [&](int s, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    const unsigned char* qb = PAR ? q_s1 : q_s0;
+    const unsigned char* dob = PAR ? do_s1 : do_s0;
+    const unsigned char* qtb = PAR ? qt_s1 : qt_s0;
+    const unsigned char* dotb = PAR ? dot_s1 : dot_s0;
+    const float* ssb = PAR ? ss_s1 : ss_s0;
+    const float* sdb = PAR ? sd_s1 : sd_s0;
     // step s's copies landed (own: the wait; everyone's: the barrier), and
-    // every wave is past its reads of step s-1, whose buffer the next copies
-    // overwrite
+    // every wave is past its reads of step s-1, whose buffers the next
+    // copies overwrite
     wait_all();
     __syncthreads();
-    if (s + 1 < N) stage(s + 1, b ^ 1);
-    const unsigned char* qb = q_s[b];
-    const unsigned char* dob = do_s[b];
-    const unsigned char* qtb = qt_s[b];
-    const unsigned char* dotb = dot_s[b];
-    f32x16 sa = f32x16{}, dpa = f32x16{};
+    if (s + 1 < N) stage(s + 1, std::integral_constant<int, 1 - PAR>{});
+    // element x is query 16(x/8) + 8hf + x%8 of the step: S starts from
+    // -lse/sm_scale and dP from -D, two runs of 8 consecutive seeds each
+    f32x16 sa, dpa;
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int q0 = 16 * (v4 / 2) + 8 * hf + 4 * (v4 % 2);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(ssb + q0);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(sdb + q0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sa[4 * v4 + e] = x[e];
+        dpa[4 * v4 + e] = y[e];
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       sa = mfma32(QR::read(qb, n, 2 * kk + hf), kr[kk], sa);
       dpa = mfma32(QR::read(dob, n, 2 * kk + hf), vr[kk], dpa);
     }
-    // element x is query 16(x/8) + 8hf + x%8 of the step: its lse2 and D
-    // are two runs of 8 consecutive floats, read as four 16-byte vectors each
-    float l2v[16], dlv[16];
-#pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      const int q0 = 16 * (v4 / 2) + 8 * hf + 4 * (v4 % 2);
-      const f32x4 a = *reinterpret_cast<const f32x4*>(&l2_s[b][q0]);
-      const f32x4 c = *reinterpret_cast<const f32x4*>(&dl_s[b][q0]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        l2v[4 * v4 + e] = a[e];
-        dlv[4 * v4 + e] = c[e];
-      }
-    }
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const float p = exp2_(fmaf(sa[x], scale_log2, -l2v[x]));
+      const float p = exp2_(sa[x] * scale_log2);
       pb[x / 8][x % 8] = (__bf16)p;
-      dsb[x / 8][x % 8] = (__bf16)(p * (dpa[x] - dlv[x]));
+      dsb[x / 8][x % 8] = (__bf16)(p * dpa[x]);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -402,7 +420,15 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
         dva[db] = mfma32(QT::read(dotb, db * 32 + n, 2 * t + hf), pb[t], dva[db]);
         dka[db] = mfma32(QT::read(qtb, db * 32 + n, 2 * t + hf), dsb[t], dka[db]);
       }
+  };
+
+  if (N > 0) stage(0, Z{});
+  int s = 0;
+  for (; s + 1 < N; s += 2) {
+    step(s, Z{});
+    step(s + 1, O1{});
   }
+  if (s < N) step(s, Z{});
 
   const TileExtent e = tile_extent(L, h, (int)(g - head_base));
   const int64_t row = slot_row(L, e, h, wave * 32 + n);
@@ -427,7 +453,7 @@ int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 struct BwdWs {
   void *qp, *kp, *vp, *dop, *qtp, *ktp, *dotp;
-  float *lse2, *delta;
+  float *lse2, *delta, *seed_s, *seed_dp;
   int32_t *cnt, *colt_ptr, *rowt;
 };
 
@@ -446,6 +472,8 @@ BwdWs carve(const DevLayout& L, int64_t nnz, void* base, int64_t* total) {
   w.qtp = take(tb); w.ktp = take(tb); w.dotp = take(tb);
   w.lse2 = static_cast<float*>(take(tiles * L.S * 4));
   w.delta = static_cast<float*>(take(tiles * L.S * 4));
+  w.seed_s = static_cast<float*>(take(tiles * L.S * 4));
+  w.seed_dp = static_cast<float*>(take(tiles * L.S * 4));
   w.cnt = static_cast<int32_t*>(take(tiles * 4));
   w.colt_ptr = static_cast<int32_t*>(take((tiles + 1) * 4));
   w.rowt = static_cast<int32_t*>(take(nnz * 4 + 4));
@@ -465,8 +493,8 @@ void launch_products(const DevLayout& L, const BwdWs& w, const int32_t* row_ptr,
                      sl2, sm_scale, (__bf16*)dq);
   hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, S>), dim3(G), dim3(2 * S), 0, s, L,
                      (const __bf16*)w.qp, (const __bf16*)w.qtp, (const __bf16*)w.kp,
-                     (const __bf16*)w.vp, (const __bf16*)w.dop, (const __bf16*)w.dotp, w.lse2,
-                     w.delta, w.colt_ptr, w.rowt, cap, sl2, sm_scale, (__bf16*)dk, (__bf16*)dv);
+                     (const __bf16*)w.vp, (const __bf16*)w.dop, (const __bf16*)w.dotp, w.seed_s,
+                     w.seed_dp, w.colt_ptr, w.rowt, cap, sl2, sm_scale, (__bf16*)dk, (__bf16*)dv);
 }
 
 }  // namespace
@@ -492,7 +520,8 @@ int launch_sparse_attn_bwd(const DevLayout& L, const void* q, const void* k, con
   for (const auto& p : perms)
     if (launch_permute(L, VEDA_BF16, p.dir, p.x, p.y, s) != VEDA_OK) return VEDA_ERR_LAUNCH;
   hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L,
-                     (const __bf16*)o, (const __bf16*)d_o, lse, w.delta, w.lse2);
+                     (const __bf16*)o, (const __bf16*)d_o, lse, sm_scale, w.delta, w.lse2,
+                     w.seed_s, w.seed_dp);
   hipLaunchKernelGGL(csrt_count_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L, row_ptr,
                      col_idx, w.cnt);
   hipLaunchKernelGGL(csrt_scan_kernel, dim3(1), dim3(kThreads), 0, s, tiles, w.cnt, w.colt_ptr);

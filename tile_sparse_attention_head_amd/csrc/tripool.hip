@@ -80,11 +80,12 @@ __global__ __launch_bounds__(kPoolThreads) void tripool_pool_kernel(DevLayout L,
 }
 
 // ---- batched f32 C[m][n] = sum_k A[m][k] B[n][k] (+ bias[n]) -------------
-// 64x64 output tile per workgroup, 4x4 outputs per lane, K in steps of 32.
-// Each lane fetches 8 consecutive k of one A row and one B row per step (two
-// 16-byte loads each when VEC: K % 4 == 0 and 16-byte aligned operands), and
-// the next step's values are fetched while the current step is multiplied.
-constexpr int BN = 64, BK = 32, kGemmThreads = 256;
+// 64x64 output tile per workgroup, 4x4 outputs per lane, K in steps of 64
+// (few steps: these products are short and latency-bound).  Each lane
+// fetches 16 consecutive k of one A row and one B row per step (four 16-byte
+// loads each when VEC: K % 4 == 0 and 16-byte aligned operands), and the next
+// step's values are fetched while the current step is multiplied.
+constexpr int BN = 64, BK = 64, kGemmThreads = 256;
 
 // projection: few, deep (K = 3d) products -> smaller tiles for more workgroups
 constexpr int kProjBM = 32, kScoreBM = 64;
@@ -122,23 +123,27 @@ __device__ __forceinline__ void gemm_abt_tile(const GemmArgs& a, int m0, int n0)
   __shared__ float Bs[BK][BN + 4];
   const int t = threadIdx.x;
   const int tm = (t / 16) * RM, tn = (t % 16) * 4;
-  const int r = t / 4, kc = (t % 4) * 8;   // fetched row and k offset within the step
+  const int r = t / 4, kc = (t % 4) * 16;  // fetched row and k offset within the step
   const bool fa = r < BM;                  // this lane also fetches an A row
   float acc[RM][4] = {};
-  float va[8], vb[8];
-  if (fa) gemm_fetch<VEC>(a.A, a.lda, m0 + r, a.M, kc, a.K, va);
-  gemm_fetch<VEC>(a.B, a.ldb, n0 + r, a.N, kc, a.K, vb);
+  float va[16], vb[16];
+  auto fetch = [&](int k) {   // 16 consecutive k of one A row and one B row
+    if (fa) {
+      gemm_fetch<VEC>(a.A, a.lda, m0 + r, a.M, k, a.K, *reinterpret_cast<float(*)[8]>(va));
+      gemm_fetch<VEC>(a.A, a.lda, m0 + r, a.M, k + 8, a.K, *reinterpret_cast<float(*)[8]>(va + 8));
+    }
+    gemm_fetch<VEC>(a.B, a.ldb, n0 + r, a.N, k, a.K, *reinterpret_cast<float(*)[8]>(vb));
+    gemm_fetch<VEC>(a.B, a.ldb, n0 + r, a.N, k + 8, a.K, *reinterpret_cast<float(*)[8]>(vb + 8));
+  };
+  fetch(kc);
   for (int k0 = 0; k0 < a.K; k0 += BK) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 16; ++c) {
       if (fa) As[kc + c][r] = va[c];
       Bs[kc + c][r] = vb[c];
     }
     __syncthreads();
-    if (k0 + BK < a.K) {   // next step's values, in flight during the products
-      if (fa) gemm_fetch<VEC>(a.A, a.lda, m0 + r, a.M, k0 + BK + kc, a.K, va);
-      gemm_fetch<VEC>(a.B, a.ldb, n0 + r, a.N, k0 + BK + kc, a.K, vb);
-    }
+    if (k0 + BK < a.K) fetch(k0 + BK + kc);   // next step's values, in flight during the products
 #pragma unroll
     for (int kk = 0; kk < BK; ++kk) {
       float am[RM];
