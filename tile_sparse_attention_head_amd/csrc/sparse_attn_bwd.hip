@@ -8,8 +8,8 @@
 //   dK = sm_scale dS^T Q,  dV = P^T dO.
 //
 // Kernels, all on the matrix cores in the forward's transposed forms:
-//  * prep: the inputs gathered into tile order (Q, K, V, dO) and
-//    tile-transposed order (Q, K, dO); per query slot D and lse*log2(e)
+//  * prep: the inputs gathered into tile order (Q, K, V, dO) and K into
+//    tile-transposed order; per query slot D and lse*log2(e)
 //    (+inf for padding slots, so their probabilities are exactly 0); the CSR
 //    transposed (per key tile, the query tiles keeping it, ascending, found
 //    by binary search in each sorted row: deterministic, no atomics).
@@ -18,8 +18,9 @@
 //    dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
 //  * dK/dV: one workgroup per key tile, wave w owns 32 keys (K and V rows in
 //    registers); per 32-query step of every query tile keeping the key tile:
-//    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.  Padding query
-//    rows have P = 0; rows of padding keys are computed and never stored.
+//    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS, with dO^T and
+//    Q^T read transposed out of the staged rows.  Padding query rows have
+//    P = 0; rows of padding keys are computed and never stored.
 // Steps stage their operands HBM -> LDS with buffer_load ... lds; one
 // workgroup's copies overlap the other resident workgroup's products.
 // Results are written straight to token order; every output row is written
@@ -289,26 +290,55 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- dK, dV
+// A operand of a product over queries: 32 rows of the step's Q or dO taken
+// as columns (d = 32db + l%32), 16 queries (16t + 8(l/32) + 0..7), read
+// from the row-major, swap23-ordered step buffer with two LDS transpose
+// reads (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i gets as
+// element e the (i%4)-th of the four values at the address lane 4e + i/4
+// gives; lane 4e+r of group G therefore points at row 16t + 4(G/2) + e (+8
+// for the second read) -- queries 16t + 8(G/2) + e (+4) in swap23 order --
+// and column 32db + 16(G%2) + 4r.
+template <int ROWB>
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* buf, int lane, int db, int t) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const int G = lane >> 4, j = lane & 15;
+  const int row = 16 * t + 4 * (G >> 1) + (j >> 2);
+  const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
+  const unsigned char* p0 = buf + row * ROWB + col * 2;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + 8 * ROWB));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// One workgroup per key tile, wave w owning keys 32w..32w+31 (their K and V
+// rows in registers).  Per 32-query step of every query tile that keeps the
+// key tile:  S = Q K^T (seeded with -lse/sm_scale), dP = dO V^T (seeded with
+// -D), P = exp2(sm_scale log2e S), dS = P dP, dV^T += dO^T P, dK^T += Q^T dS.
+// The C layout of S (lane = key, 8 consecutive queries per half) is the B
+// operand layout of the products over queries, so P and dS feed them as they
+// are; their A operands are the step's dO and Q rows read transposed from
+// LDS.  Only Q and dO rows are staged (18 KiB a step), four steps deep:
+// step s+3 is copied while step s computes.
 template <int D, int S>
 __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
-    DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ qt,
-    const __bf16* __restrict__ k, const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
-    const __bf16* __restrict__ dot, const float* __restrict__ seed_s,
-    const float* __restrict__ seed_dp, const int32_t* __restrict__ colt_ptr,
-    const int32_t* __restrict__ rowt, int32_t cap, float scale_log2, float sm_scale,
-    __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
+    DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
+    const float* __restrict__ seed_s, const float* __restrict__ seed_dp,
+    const int32_t* __restrict__ colt_ptr, const int32_t* __restrict__ rowt, int32_t cap,
+    float scale_log2, float sm_scale, __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
   constexpr int NW = S / 32, SQ = 32, SPQ = S / SQ, KS = D / 16, DB = D / 32, TILE = S * D * 2;
+  constexpr int NB = 4;                                 // steps in flight
   using QR = StepBuf<SQ, D / 8, true, D * 2, NW>;      // Q or dO rows of a step, swap23 order
-  using QT = StepBuf<D, SQ / 8, false, S * 2, NW>;     // Q^T or dO^T: D rows of 32 queries
-  // two of everything: the copies of step s+1 land while step s computes.
-  // Separate objects per parity, chosen at compile time, so that the reads of
-  // one buffer are never ordered after the copies into the other.
-  __shared__ __attribute__((aligned(1024))) unsigned char q_s0[QR::BYTES], q_s1[QR::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char do_s0[QR::BYTES], do_s1[QR::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char qt_s0[QT::BYTES], qt_s1[QT::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char dot_s0[QT::BYTES], dot_s1[QT::BYTES];
-  // the step's seeds of its S and dP accumulators (-lse/sm_scale, -D)
-  __shared__ __attribute__((aligned(16))) float ss_s0[SQ], ss_s1[SQ], sd_s0[SQ], sd_s1[SQ];
+  // per step buffer: Q rows, dO rows, then the 32 + 32 seeds of S and dP
+  constexpr int SEEDS = 2 * QR::BYTES, BUF = SEEDS + 256;
+  __shared__ __attribute__((aligned(1024))) unsigned char b0[BUF], b1[BUF], b2[BUF], b3[BUF];
+  auto buf = [&](auto par) -> unsigned char* {
+    constexpr int P = decltype(par)::value;
+    return P == 0 ? b0 : P == 1 ? b1 : P == 2 ? b2 : b3;
+  };
 
   const int64_t g = xcd_remap(blockIdx.x, gridDim.x);   // key tile
   const int h = head_of_tile(L, g);
@@ -331,36 +361,31 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     return make_rsrc(reinterpret_cast<const unsigned char*>(base) + head_base * TILE,
                      (int64_t)n_h * TILE);
   };
-  const auto qrs = rs(q), dors = rs(d_o), qtrs = rs(qt), dotrs = rs(dot);
+  const auto qrs = rs(q), dors = rs(d_o);
   const auto ssrs = make_rsrc(seed_s + head_base * S, (int64_t)n_h * S * 4);
   const auto sdrs = make_rsrc(seed_dp + head_base * S, (int64_t)n_h * S * 4);
-  uint32_t ro[QR::PER_WAVE], to[QT::PER_WAVE];
+  uint32_t ro[QR::PER_WAVE];
   QR::offsets(ro, wave, lane);
-  QT::offsets(to, wave, lane);
 
-  // copies of step s into the buffers of parity PAR
+  // copies of step s into buffer PAR.  Every wave issues the same number of
+  // copies (each also copies the 256 seed bytes: identical bytes to the same
+  // place), so one vmcnt value counts a step's copies in every wave.
+  constexpr int CPS = 2 * QR::PER_WAVE + 2;             // copy instructions per step and wave
   auto stage = [&](int s, auto par) {
-    constexpr int PAR = decltype(par)::value;
-    unsigned char* qb = PAR ? q_s1 : q_s0;
-    unsigned char* dob = PAR ? do_s1 : do_s0;
-    unsigned char* qtb = PAR ? qt_s1 : qt_s0;
-    unsigned char* dotb = PAR ? dot_s1 : dot_s0;
-    float* ssb = PAR ? ss_s1 : ss_s0;
-    float* sdb = PAR ? sd_s1 : sd_s0;
+    unsigned char* bb = buf(par);
     const int i = min(max(rt[a0 + s / SPQ], 0), n_h - 1);   // head-local query tile
     const int qs = s % SPQ;
     const uint32_t rof = (uint32_t)(i * TILE + qs * SQ * D * 2);
-    const uint32_t tof = (uint32_t)(i * TILE + qs * SQ * 2);
-    QR::copy(qrs, rof, qb, ro, wave);
-    QR::copy(dors, rof, dob, ro, wave);
-    QT::copy(qtrs, tof, qtb, to, wave);
-    QT::copy(dotrs, tof, dotb, to, wave);
-    // the step's 32 + 32 seeds: 8 lanes x 16 bytes each through the same LDS
-    // copy path (no register round trip, no wait of its own)
-    if (wave == 0 && lane < SQ / 4) {
-      const uint32_t so = (uint32_t)((i * S + qs * SQ) * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ssrs, (lds_void*)ssb, 16, lane * 16, so, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sdrs, (lds_void*)sdb, 16, lane * 16, so, 0, 0);
+    QR::copy(qrs, rof, bb, ro, wave);
+    QR::copy(dors, rof, bb + QR::BYTES, ro, wave);
+    // the 32 seeds of S, then those of dP: lanes 0-7, 16 bytes each (the
+    // descriptor, the LDS place and the step offset are uniform)
+    const uint32_t so = (uint32_t)((i * S + qs * SQ) * 4);
+    if (lane < 8) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ssrs, (lds_void*)(bb + SEEDS), 16, lane * 16, so,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sdrs, (lds_void*)(bb + SEEDS + 128), 16, lane * 16,
+                                               so, 0, 0);
     }
   };
 
@@ -371,24 +396,26 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     dva[db] = f32x16{};
   }
 
-  using Z = std::integral_constant<int, 0>;
-  using O1 = std::integral_constant<int, 1>;
   auto step = [&](int s, auto par) {
     constexpr int PAR = decltype(par)::value;
-    const unsigned char* qb = PAR ? q_s1 : q_s0;
-    const unsigned char* dob = PAR ? do_s1 : do_s0;
-    const unsigned char* qtb = PAR ? qt_s1 : qt_s0;
-    const unsigned char* dotb = PAR ? dot_s1 : dot_s0;
-    const float* ssb = PAR ? ss_s1 : ss_s0;
-    const float* sdb = PAR ? sd_s1 : sd_s0;
-    // step s's copies landed (own: the wait; everyone's: the barrier), and
-    // every wave is past its reads of step s-1, whose buffers the next
-    // copies overwrite
-    wait_all();
-    __syncthreads();
-    if (s + 1 < N) stage(s + 1, std::integral_constant<int, 1 - PAR>{});
-    // element x is query 16(x/8) + 8hf + x%8 of the step: S starts from
-    // -lse/sm_scale and dP from -D, two runs of 8 consecutive seeds each
+    const unsigned char* qb = buf(par);
+    const unsigned char* dob = qb + QR::BYTES;
+    const float* ssb = reinterpret_cast<const float*>(qb + SEEDS);
+    const float* sdb = ssb + SQ;
+    // step s's copies landed: the copies of the (up to two) later steps
+    // already issued may stay in flight; the barrier makes every wave's
+    // copies visible and every wave past its reads of step s-1, whose buffer
+    // the next copies overwrite
+    // (a bare s_barrier: a fenced barrier would also drain those later copies)
+    if (s + 2 < N)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(2 * CPS) : "memory");
+    else if (s + 1 < N)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(CPS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s + 3 < N) stage(s + 3, std::integral_constant<int, (PAR + 3) % NB>{});
+    // element x is query 16(x/8) + 8hf + x%8 of the step: S and dP start from
+    // their seeds, two runs of 8 consecutive values each
     f32x16 sa, dpa;
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
@@ -417,18 +444,28 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dva[db] = mfma32(QT::read(dotb, db * 32 + n, 2 * t + hf), pb[t], dva[db]);
-        dka[db] = mfma32(QT::read(qtb, db * 32 + n, 2 * t + hf), dsb[t], dka[db]);
+        dva[db] = mfma32(tr_operand<QR::ROWB>(dob, lane, db, t), pb[t], dva[db]);
+        dka[db] = mfma32(tr_operand<QR::ROWB>(qb, lane, db, t), dsb[t], dka[db]);
       }
   };
 
-  if (N > 0) stage(0, Z{});
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  if (N > 0) stage(0, C0{});
+  if (N > 1) stage(1, C1{});
+  if (N > 2) stage(2, C2{});
   int s = 0;
-  for (; s + 1 < N; s += 2) {
-    step(s, Z{});
-    step(s + 1, O1{});
+  for (; s + 3 < N; s += 4) {
+    step(s, C0{});
+    step(s + 1, C1{});
+    step(s + 2, C2{});
+    step(s + 3, C3{});
   }
-  if (s < N) step(s, Z{});
+  if (s < N) step(s, C0{});
+  if (s + 1 < N) step(s + 1, C1{});
+  if (s + 2 < N) step(s + 2, C2{});
 
   const TileExtent e = tile_extent(L, h, (int)(g - head_base));
   const int64_t row = slot_row(L, e, h, wave * 32 + n);
@@ -452,7 +489,7 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 struct BwdWs {
-  void *qp, *kp, *vp, *dop, *qtp, *ktp, *dotp;
+  void *qp, *kp, *vp, *dop, *ktp;
   float *lse2, *delta, *seed_s, *seed_dp;
   int32_t *cnt, *colt_ptr, *rowt;
 };
@@ -469,7 +506,7 @@ BwdWs carve(const DevLayout& L, int64_t nnz, void* base, int64_t* total) {
   const int64_t tiles = L.tile_off[L.heads];
   const int64_t tb = tiles * L.S * L.d * 2;
   w.qp = take(tb); w.kp = take(tb); w.vp = take(tb); w.dop = take(tb);
-  w.qtp = take(tb); w.ktp = take(tb); w.dotp = take(tb);
+  w.ktp = take(tb);
   w.lse2 = static_cast<float*>(take(tiles * L.S * 4));
   w.delta = static_cast<float*>(take(tiles * L.S * 4));
   w.seed_s = static_cast<float*>(take(tiles * L.S * 4));
@@ -492,9 +529,9 @@ void launch_products(const DevLayout& L, const BwdWs& w, const int32_t* row_ptr,
                      (const __bf16*)w.ktp, (const __bf16*)w.dop, w.lse2, w.delta, row_ptr, col_idx,
                      sl2, sm_scale, (__bf16*)dq);
   hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, S>), dim3(G), dim3(2 * S), 0, s, L,
-                     (const __bf16*)w.qp, (const __bf16*)w.qtp, (const __bf16*)w.kp,
-                     (const __bf16*)w.vp, (const __bf16*)w.dop, (const __bf16*)w.dotp, w.seed_s,
-                     w.seed_dp, w.colt_ptr, w.rowt, cap, sl2, sm_scale, (__bf16*)dk, (__bf16*)dv);
+                     (const __bf16*)w.qp, (const __bf16*)w.kp, (const __bf16*)w.vp,
+                     (const __bf16*)w.dop, w.seed_s, w.seed_dp, w.colt_ptr, w.rowt, cap, sl2,
+                     sm_scale, (__bf16*)dk, (__bf16*)dv);
 }
 
 }  // namespace
@@ -516,7 +553,7 @@ int launch_sparse_attn_bwd(const DevLayout& L, const void* q, const void* k, con
   const BwdWs w = carve(L, nnz, workspace, &total);
   const struct { const void* x; void* y; int dir; } perms[] = {
       {q, w.qp, VEDA_FWD}, {k, w.kp, VEDA_FWD}, {v, w.vp, VEDA_FWD}, {d_o, w.dop, VEDA_FWD},
-      {q, w.qtp, VEDA_FWD_T}, {k, w.ktp, VEDA_FWD_T}, {d_o, w.dotp, VEDA_FWD_T}};
+      {k, w.ktp, VEDA_FWD_T}};
   for (const auto& p : perms)
     if (launch_permute(L, VEDA_BF16, p.dir, p.x, p.y, s) != VEDA_OK) return VEDA_ERR_LAUNCH;
   hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L,
