@@ -507,8 +507,10 @@ def main():
         for s in (95, 0):
             if s == args.sparsity:
                 continue
+            # the same step as the headline run (map included), so the
+            # stages see the same cache and clock conditions
             c = Bench(args.workload, s)
-            w2, sm2, _ = c.run(max(10, args.steps // 2), 3, with_map=False)
+            w2, sm2, _ = c.run(max(10, args.steps // 2), 3)
             d2 = dict(zip(names, [float(x) for x in sm2]))
             a_ms = d2["sparse_attn"]
             context[f"sparsity_{s}"] = {
@@ -524,7 +526,7 @@ def main():
         # the same layer one method step per call (tile-order O, then the
         # inverse permutation): what the fused calls save
         u = Bench(args.workload, args.sparsity, fused=False)
-        _, smu, _ = u.run(max(3, args.steps // 2), 2, with_map=False)
+        _, smu, _ = u.run(max(10, args.steps // 2), 3)
         du = dict(zip(u.stages, [float(x) for x in smu]))
         context["unfused"] = {"ms_per_layer": sum(du[n] for n in u.stages if n != "map"),
                               "stage_ms": {n: du[n] for n in u.stages if n != "map"}}
