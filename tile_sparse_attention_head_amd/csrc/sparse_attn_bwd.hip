@@ -290,28 +290,92 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- dK, dV
-// A operand of a product over queries: 32 rows of the step's Q or dO taken
-// as columns (d = 32db + l%32), 16 queries (16t + 8(l/32) + 0..7), read
-// from the row-major, swap23-ordered step buffer with two LDS transpose
-// reads (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i gets as
-// element e the (i%4)-th of the four values at the address lane 4e + i/4
-// gives; lane 4e+r of group G therefore points at row 16t + 4(G/2) + e (+8
-// for the second read) -- queries 16t + 8(G/2) + e (+4) in swap23 order --
-// and column 32db + 16(G%2) + 4r.
-template <int ROWB>
-__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* buf, int lane, int db, int t) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4s lds_v4s;
-  const int G = lane >> 4, j = lane & 15;
-  const int row = 16 * t + 4 * (G >> 1) + (j >> 2);
-  const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
-  const unsigned char* p0 = buf + row * ROWB + col * 2;
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + 8 * ROWB));
-  typedef short v8s __attribute__((ext_vector_type(8)));
-  const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, both);
-}
+// Q or dO rows of one 32-query step in LDS, laid out so that both of the
+// dK/dV kernel's read patterns are free of bank conflicts (64 banks of 4
+// bytes; a 128-bit read serves 16 lanes a cycle, a 64-bit one 32):
+//   [32-dim block b][row r][64 bytes], the four 16-byte chunks of a row's
+//   block stored in the order c ^ ((r >> 2) & 3).
+// * Row reads (the A operand of S and dP: lane l reads row l % 32, chunk
+//   2kk + l / 32): 16 consecutive rows fall on 4 distinct 64-byte windows
+//   (r % 4) and, within each, on 4 distinct chunks ((r >> 2) % 4).
+// * Transposed reads (ds_read_b64_tr_b16, the A operand of dV and dK): 32
+//   lanes read 4 consecutive rows of one block, 256 contiguous bytes.
+// A lane's address for either pattern is one of two per-lane bases plus an
+// immediate (block and row group).  Row r holds HBM row swap23(r) of the
+// step, rows GSTRIDE bytes apart.  It is filled by 1 KiB copy rounds (64
+// lanes x 16 bytes of consecutive LDS) shared by NW waves.
+template <int R, int D, int GSTRIDE, int NW>
+struct TrBuf {
+  static constexpr int DB = D / 32;
+  static constexpr int BLK = R * 64;                  // bytes of one 32-dim block
+  static constexpr int BYTES = DB * BLK;
+  static constexpr int ROUNDS = BYTES / 1024;
+  static constexpr int PER_WAVE = (ROUNDS + NW - 1) / NW;
+  static_assert(R == 32 && BYTES % 1024 == 0, "32-row steps of whole copy rounds");
+  // round i of wave w fills LDS block w + NW*i; past the last block it fills
+  // block w again with the same bytes (every wave issues PER_WAVE rounds)
+  static __device__ __forceinline__ int block(int wave, int i) {
+    const int q = wave + NW * i;
+    return q < ROUNDS ? q : wave;
+  }
+  static __device__ __forceinline__ void offsets(uint32_t (&off)[PER_WAVE], int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int u = block(wave, i) * 64 + lane;   // 16-byte unit of the buffer
+      const int b = u / (R * 4), r = (u / 4) % R;
+      const int c = (u & 3) ^ ((r >> 2) & 3);
+      off[i] = (uint32_t)(swap23(r) * GSTRIDE + (4 * b + c) * 16);
+    }
+  }
+  static __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, uint32_t so,
+                                              unsigned char* lds, const uint32_t (&off)[PER_WAVE],
+                                              int wave) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + block(wave, i) * 1024), 16,
+                                               off[i], so, 0, 0);
+  }
+  // Row reads: row l % 32, chunk 2kk + l / 32.  base[p] is the lane's offset
+  // for even (p = 0) and odd (p = 1) kk; block kk / 2 is the immediate.
+  static __device__ __forceinline__ void row_bases(int (&base)[2], int lane) {
+    const int r = lane & 31, y = (lane >> 5) ^ ((r >> 2) & 3);
+    base[0] = r * 64 + 16 * y;
+    base[1] = r * 64 + 16 * (y ^ 2);
+  }
+  static __device__ __forceinline__ bf16x8 row(const unsigned char* buf, const int (&base)[2],
+                                               int kk) {
+    return *reinterpret_cast<const bf16x8*>(buf + (kk / 2) * BLK + base[kk & 1]);
+  }
+  // Transposed reads: the A operand of a product over the step's queries, 32
+  // dims of block db as rows (d = 32db + l%32), 16 queries (16t + 8(l/32) +
+  // 0..7) as the contraction.  Within each group of 16 lanes
+  // ds_read_b64_tr_b16 gives lane i, as element e, the (i%4)-th of the four
+  // values at the address lane 4e + i/4 supplies; lane 4e+x of group G
+  // therefore supplies row 16t + 4(G/2) + e (+8 for the second read) -- rows
+  // of queries 16t + 8(G/2) + e (+4) in swap23 order -- at dims 32db +
+  // 16(G%2) + 4x .. +3: chunk 2(G%2) + x/2 of the block, bytes 8(x%2) on.
+  // base[s] is the lane's offset for the first (s = 0) and second read.
+  static __device__ __forceinline__ void tr_bases(int (&base)[2], int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int c = 2 * (G & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int r = 4 * (G >> 1) + (j >> 2) + 8 * s;   // row within a 16-row group
+      base[s] = r * 64 + 16 * (c ^ ((r >> 2) & 3)) + 8 * (j & 1);
+    }
+  }
+  static __device__ __forceinline__ bf16x8 tr(const unsigned char* buf, const int (&base)[2],
+                                              int db, int t) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const unsigned char* p = buf + db * BLK + t * 16 * 64;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + base[0]));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + base[1]));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, both);
+  }
+};
 
 // One workgroup per key tile, wave w owning keys 32w..32w+31 (their K and V
 // rows in registers).  Per 32-query step of every query tile that keeps the
@@ -331,7 +395,7 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     float scale_log2, float sm_scale, __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
   constexpr int NW = S / 32, SQ = 32, SPQ = S / SQ, KS = D / 16, DB = D / 32, TILE = S * D * 2;
   constexpr int NB = 4;                                 // steps in flight
-  using QR = StepBuf<SQ, D / 8, true, D * 2, NW>;      // Q or dO rows of a step, swap23 order
+  using QR = TrBuf<SQ, D, D * 2, NW>;                 // Q or dO rows of a step, swap23 order
   // per step buffer: Q rows, dO rows, then the 32 + 32 seeds of S and dP
   constexpr int SEEDS = 2 * QR::BYTES, BUF = SEEDS + 256;
   __shared__ __attribute__((aligned(1024))) unsigned char b0[BUF], b1[BUF], b2[BUF], b3[BUF];
@@ -366,6 +430,9 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
   const auto sdrs = make_rsrc(seed_dp + head_base * S, (int64_t)n_h * S * 4);
   uint32_t ro[QR::PER_WAVE];
   QR::offsets(ro, wave, lane);
+  int rb[2], tb[2];
+  QR::row_bases(rb, lane);
+  QR::tr_bases(tb, lane);
 
   // copies of step s into buffer PAR.  Every wave issues the same number of
   // copies (each also copies the 256 seed bytes: identical bytes to the same
@@ -430,8 +497,8 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      sa = mfma32(QR::read(qb, n, 2 * kk + hf), kr[kk], sa);
-      dpa = mfma32(QR::read(dob, n, 2 * kk + hf), vr[kk], dpa);
+      sa = mfma32(QR::row(qb, rb, kk), kr[kk], sa);
+      dpa = mfma32(QR::row(dob, rb, kk), vr[kk], dpa);
     }
     bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -444,8 +511,8 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dva[db] = mfma32(tr_operand<QR::ROWB>(dob, lane, db, t), pb[t], dva[db]);
-        dka[db] = mfma32(tr_operand<QR::ROWB>(qb, lane, db, t), dsb[t], dka[db]);
+        dva[db] = mfma32(QR::tr(dob, tb, db, t), pb[t], dva[db]);
+        dka[db] = mfma32(QR::tr(qb, tb, db, t), dsb[t], dka[db]);
       }
   };
 
