@@ -495,11 +495,31 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
         dpa[4 * v4 + e] = y[e];
       }
     }
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      sa = mfma32(QR::row(qb, rb, kk), kr[kk], sa);
-      dpa = mfma32(QR::row(dob, rb, kk), vr[kk], dpa);
-    }
+    // The products are laid out by hand in slots of one MFMA each, with the
+    // LDS read of a later slot's operand; the compiler may not move work
+    // across slots.  S and dP alternate (operand reads LA1 slots ahead); the
+    // first dV/dK operands are read while P and dS are computed, then dV
+    // and dK alternate (reads LA2 slots ahead).
+    constexpr int LA1 = 2, N1 = 2 * KS, LA2 = 3, N2 = 4 * DB;
+    auto op1 = [&](int i) { return QR::row((i & 1) ? dob : qb, rb, i >> 1); };
+    auto op2 = [&](int i) { return QR::tr((i & 1) ? qb : dob, tb, (i >> 1) % DB, i / (2 * DB)); };
+    bf16x8 o1[LA1 + 1], o2[LA2 + 1];
+    static_for<0, LA1>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      o1[i] = op1(i);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, N1>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + LA1 < N1) o1[(i + LA1) % (LA1 + 1)] = op1(i + LA1);
+      if constexpr (i & 1) dpa = mfma32(o1[i % (LA1 + 1)], vr[i >> 1], dpa);
+      else sa = mfma32(o1[i % (LA1 + 1)], kr[i >> 1], sa);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<0, LA2>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      o2[i] = op2(i);
+    });
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
@@ -507,13 +527,15 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
       pb[x / 8][x % 8] = (__bf16)p;
       dsb[x / 8][x % 8] = (__bf16)(p * dpa[x]);
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dva[db] = mfma32(QR::tr(dob, tb, db, t), pb[t], dva[db]);
-        dka[db] = mfma32(QR::tr(qb, tb, db, t), dsb[t], dka[db]);
-      }
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, N2>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int db = (i >> 1) % DB, t = i / (2 * DB);
+      if constexpr (i + LA2 < N2) o2[(i + LA2) % (LA2 + 1)] = op2(i + LA2);
+      if constexpr (i & 1) dka[db] = mfma32(o2[i % (LA2 + 1)], dsb[t], dka[db]);
+      else dva[db] = mfma32(o2[i % (LA2 + 1)], pb[t], dva[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   using C0 = std::integral_constant<int, 0>;
