@@ -8,14 +8,15 @@
 //   dK = sm_scale dS^T Q,  dV = P^T dO.
 //
 // Kernels, all on the matrix cores in the forward's transposed forms:
-//  * prep: the inputs gathered into tile order (Q, K, V, dO) and K into
-//    tile-transposed order; per query slot D and lse*log2(e)
+//  * prep: the inputs gathered into tile order (Q, K, V, dO); per query
+//    slot D and lse*log2(e)
 //    (+inf for padding slots, so their probabilities are exactly 0); the CSR
 //    transposed (per key tile, the query tiles keeping it, ascending, found
 //    by binary search in each sorted row: deterministic, no atomics).
 //  * dQ: one workgroup per query tile, wave w owns 32 queries (Q and dO rows
 //    in registers); per 64-key step S^T = K Q^T (seeded with the mask rows),
-//    dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+//    dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T, with K^T read
+//    transposed out of the staged K rows.
 //  * dK/dV: one workgroup per key tile, wave w owns 32 keys (K and V rows in
 //    registers); per 32-query step of every query tile keeping the key tile:
 //    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS, with dO^T and
@@ -185,125 +186,21 @@ __global__ __launch_bounds__(kThreads) void csrt_fill_kernel(DevLayout L,
   }
 }
 
-// ---------------------------------------------------------------- dQ
-template <int D, int S>
-__global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
-    DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-    const __bf16* __restrict__ v, const __bf16* __restrict__ kt, const __bf16* __restrict__ d_o,
-    const float* __restrict__ lse2, const float* __restrict__ delta,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, float scale_log2,
-    float sm_scale, __bf16* __restrict__ dq) {
-  constexpr int NW = S / 32, SK = 64, SPT = S / SK, KS = D / 16, DB = D / 32, TILE = S * D * 2;
-  using KR = StepBuf<SK, D / 8, true, D * 2, NW>;      // K or V rows of a step, swap23 order
-  using KT = StepBuf<D, SK / 8, false, S * 2, NW>;     // K^T: D rows of the step's 64 keys
-  __shared__ __attribute__((aligned(1024))) unsigned char k_s[KR::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_s[KR::BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char kt_s[KT::BYTES];
-  __shared__ BiasTable<SPT, 9> btab;
-
-  const int64_t g = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = head_of_tile(L, g);
-  const int64_t head_base = L.tile_off[h];
-  const int n_h = (int)(L.tile_off[h + 1] - head_base);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, hf = lane >> 5;
-  const int64_t qrow = g * S + wave * 32 + n;
-
-  bf16x8 qr[KS], dor[KS];
-  load_q_regs<D>(qr, q + qrow * D, hf);
-  load_q_regs<D>(dor, d_o + qrow * D, hf);
-  const float l2 = lse2[qrow], dl = delta[qrow];
-
-  cint32* rp = (cint32*)row_ptr;
-  cint32* cp = (cint32*)col_idx;
-  int beg = rp[g], end = rp[g + 1];
-  if (end < beg) end = beg;
-  const int N = (end - beg) * SPT;
-  const unsigned char* kb = reinterpret_cast<const unsigned char*>(k) + head_base * TILE;
-  const unsigned char* vb = reinterpret_cast<const unsigned char*>(v) + head_base * TILE;
-  const unsigned char* ktb = reinterpret_cast<const unsigned char*>(kt) + head_base * TILE;
-  const auto krs = make_rsrc(kb, (int64_t)n_h * TILE);
-  const auto vrs = make_rsrc(vb, (int64_t)n_h * TILE);
-  const auto ktrs = make_rsrc(ktb, (int64_t)n_h * TILE);
-  uint32_t ro[KR::PER_WAVE], to[KT::PER_WAVE];
-  KR::offsets(ro, wave, lane);
-  KT::offsets(to, wave, lane);
-  build_bias_table<SPT, 9>(btab, L, h, tid, 2 * S);
-
-  f32x16 dqa[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
-
-  for (int s = 0; s < N; ++s) {
-    const int c = cp[beg + s / SPT];
-    const bool ok = c >= 0 && c < n_h;
-    const int cut = ok ? cut_of(tile_extent(L, h, c)) : 8;
-    const int cc = ok ? c : 0;
-    KR::copy(krs, (uint32_t)(cc * TILE + (s % SPT) * SK * D * 2), k_s, ro, wave);
-    KR::copy(vrs, (uint32_t)(cc * TILE + (s % SPT) * SK * D * 2), v_s, ro, wave);
-    KT::copy(ktrs, (uint32_t)(cc * TILE + (s % SPT) * SK * 2), kt_s, to, wave);
-    wait_all();
-    __syncthreads();
-    f32x16 st[2], dpt[2];
-    load_bias(st, &btab.v[cut][s % SPT][0][hf][0]);
-    dpt[0] = f32x16{};
-    dpt[1] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        st[b] = mfma32(KR::read(k_s, b * 32 + n, 2 * kk + hf), qr[kk], st[b]);
-        dpt[b] = mfma32(KR::read(v_s, b * 32 + n, 2 * kk + hf), dor[kk], dpt[b]);
-      }
-    // element i of block b is key 32b + 16(i/8) + 8hf + i%8 of the step
-    bf16x8 ds[4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2_(fmaf(st[b][i], scale_log2, -l2));
-        ds[2 * b + i / 8][i % 8] = (__bf16)(p * (dpt[b][i] - dl));
-      }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        dqa[db] = mfma32(KT::read(kt_s, db * 32 + n, 2 * t + hf), ds[t], dqa[db]);
-    __syncthreads();   // every wave is past its reads before the next copies
-  }
-
-  const TileExtent e = tile_extent(L, h, (int)(g - head_base));
-  const int64_t row = slot_row(L, e, h, wave * 32 + n);
-  if (row >= 0) {
-    __bf16* out = dq + row * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        bf16x4 w;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) w[b] = (__bf16)(dqa[db][4 * a + b] * sm_scale);
-        *reinterpret_cast<bf16x4*>(out + db * 32 + 8 * a + 4 * hf) = w;
-      }
-  }
-}
-
-// ---------------------------------------------------------------- dK, dV
-// Q or dO rows of one 32-query step in LDS, laid out so that both of the
-// dK/dV kernel's read patterns are free of bank conflicts (64 banks of 4
-// bytes; a 128-bit read serves 16 lanes a cycle, a 64-bit one 32):
+// R rows of one step (Q or dO rows of 32 queries for dK/dV, K or V rows of
+// 64 keys for dQ) in LDS, laid out so that both read patterns of the
+// backward products are free of bank conflicts (64 banks of 4 bytes; a
+// 128-bit read serves 16 lanes a cycle, a 64-bit one 32):
 //   [32-dim block b][row r][64 bytes], the four 16-byte chunks of a row's
 //   block stored in the order c ^ ((r >> 2) & 3).
-// * Row reads (the A operand of S and dP: lane l reads row l % 32, chunk
-//   2kk + l / 32): 16 consecutive rows fall on 4 distinct 64-byte windows
-//   (r % 4) and, within each, on 4 distinct chunks ((r >> 2) % 4).
-// * Transposed reads (ds_read_b64_tr_b16, the A operand of dV and dK): 32
-//   lanes read 4 consecutive rows of one block, 256 contiguous bytes.
+// * Row reads (the A operand of S and dP: lane l reads row 32rb + l % 32,
+//   chunk 2kk + l / 32): 16 consecutive rows fall on 4 distinct 64-byte
+//   windows (r % 4) and, within each, on 4 distinct chunks ((r >> 2) % 4).
+// * Transposed reads (ds_read_b64_tr_b16, the A operand of dV, dK and dQ):
+//   32 lanes read 4 consecutive rows of one block, 256 contiguous bytes.
 // A lane's address for either pattern is one of two per-lane bases plus an
-// immediate (block and row group).  Row r holds HBM row swap23(r) of the
-// step, rows GSTRIDE bytes apart.  It is filled by 1 KiB copy rounds (64
-// lanes x 16 bytes of consecutive LDS) shared by NW waves.
+// immediate (block and row group).  Row r holds HBM row swap23(r) of its
+// 32-row block of the step, rows GSTRIDE bytes apart.  It is filled by 1 KiB
+// copy rounds (64 lanes x 16 bytes of consecutive LDS) shared by NW waves.
 template <int R, int D, int GSTRIDE, int NW>
 struct TrBuf {
   static constexpr int DB = D / 32;
@@ -311,7 +208,7 @@ struct TrBuf {
   static constexpr int BYTES = DB * BLK;
   static constexpr int ROUNDS = BYTES / 1024;
   static constexpr int PER_WAVE = (ROUNDS + NW - 1) / NW;
-  static_assert(R == 32 && BYTES % 1024 == 0, "32-row steps of whole copy rounds");
+  static_assert(R % 32 == 0 && BYTES % 1024 == 0, "32-row blocks, whole copy rounds");
   // round i of wave w fills LDS block w + NW*i; past the last block it fills
   // block w again with the same bytes (every wave issues PER_WAVE rounds)
   static __device__ __forceinline__ int block(int wave, int i) {
@@ -324,7 +221,7 @@ struct TrBuf {
       const int u = block(wave, i) * 64 + lane;   // 16-byte unit of the buffer
       const int b = u / (R * 4), r = (u / 4) % R;
       const int c = (u & 3) ^ ((r >> 2) & 3);
-      off[i] = (uint32_t)(swap23(r) * GSTRIDE + (4 * b + c) * 16);
+      off[i] = (uint32_t)(((r & ~31) | swap23(r & 31)) * GSTRIDE + (4 * b + c) * 16);
     }
   }
   static __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, uint32_t so,
@@ -335,24 +232,25 @@ struct TrBuf {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + block(wave, i) * 1024), 16,
                                                off[i], so, 0, 0);
   }
-  // Row reads: row l % 32, chunk 2kk + l / 32.  base[p] is the lane's offset
-  // for even (p = 0) and odd (p = 1) kk; block kk / 2 is the immediate.
+  // Row reads: row 32rb + l % 32, chunk 2kk + l / 32.  base[p] is the lane's
+  // offset for even (p = 0) and odd (p = 1) kk; block kk / 2 and row block rb
+  // are the immediate.
   static __device__ __forceinline__ void row_bases(int (&base)[2], int lane) {
     const int r = lane & 31, y = (lane >> 5) ^ ((r >> 2) & 3);
     base[0] = r * 64 + 16 * y;
     base[1] = r * 64 + 16 * (y ^ 2);
   }
   static __device__ __forceinline__ bf16x8 row(const unsigned char* buf, const int (&base)[2],
-                                               int kk) {
-    return *reinterpret_cast<const bf16x8*>(buf + (kk / 2) * BLK + base[kk & 1]);
+                                               int kk, int rb = 0) {
+    return *reinterpret_cast<const bf16x8*>(buf + (kk / 2) * BLK + rb * 32 * 64 + base[kk & 1]);
   }
-  // Transposed reads: the A operand of a product over the step's queries, 32
-  // dims of block db as rows (d = 32db + l%32), 16 queries (16t + 8(l/32) +
-  // 0..7) as the contraction.  Within each group of 16 lanes
+  // Transposed reads: the A operand of a product over the step's rows, 32
+  // dims of block db as rows (d = 32db + l%32), 16 step rows (16t + 8(l/32)
+  // + 0..7, t < R/16) as the contraction.  Within each group of 16 lanes
   // ds_read_b64_tr_b16 gives lane i, as element e, the (i%4)-th of the four
   // values at the address lane 4e + i/4 supplies; lane 4e+x of group G
-  // therefore supplies row 16t + 4(G/2) + e (+8 for the second read) -- rows
-  // of queries 16t + 8(G/2) + e (+4) in swap23 order -- at dims 32db +
+  // therefore supplies row 16t + 4(G/2) + e (+8 for the second read) -- step
+  // rows 16t + 8(G/2) + e (+4) in swap23 order -- at dims 32db +
   // 16(G%2) + 4x .. +3: chunk 2(G%2) + x/2 of the block, bytes 8(x%2) on.
   // base[s] is the lane's offset for the first (s = 0) and second read.
   static __device__ __forceinline__ void tr_bases(int (&base)[2], int lane) {
@@ -377,6 +275,137 @@ struct TrBuf {
   }
 };
 
+// ---------------------------------------------------------------- dQ
+// One workgroup per query tile, wave w owning queries 32w..32w+31 (Q and dO
+// rows in registers).  Per 64-key step of every kept key tile:
+// S^T = K Q^T (seeded with the step's mask rows), dP^T = V dO^T,
+// dS^T = P^T (dP^T - D), dQ^T += K^T dS^T, the A operand K^T read
+// transposed out of the staged K rows.  K and V rows of a step are staged
+// in two buffers: step s+1 is copied while step s computes.
+template <int D, int S>
+__global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
+    DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
+    const float* __restrict__ lse2, const float* __restrict__ delta,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, float scale_log2,
+    float sm_scale, __bf16* __restrict__ dq) {
+  constexpr int NW = S / 32, SK = 64, SPT = S / SK, KS = D / 16, DB = D / 32, TILE = S * D * 2;
+  using KR = TrBuf<SK, D, D * 2, NW>;                 // K or V rows of a step
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[KR::BYTES], v0[KR::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[KR::BYTES], v1[KR::BYTES];
+  __shared__ BiasTable<SPT, 9> btab;
+
+  const int64_t g = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = head_of_tile(L, g);
+  const int64_t head_base = L.tile_off[h];
+  const int n_h = (int)(L.tile_off[h + 1] - head_base);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hf = lane >> 5;
+  const int64_t qrow = g * S + wave * 32 + n;
+
+  bf16x8 qr[KS], dor[KS];
+  load_q_regs<D>(qr, q + qrow * D, hf);
+  load_q_regs<D>(dor, d_o + qrow * D, hf);
+  const float l2 = lse2[qrow], dl = delta[qrow];
+
+  cint32* rp = (cint32*)row_ptr;
+  cint32* cp = (cint32*)col_idx;
+  int beg = rp[g], end = rp[g + 1];
+  if (end < beg) end = beg;
+  const int N = (end - beg) * SPT;
+  const auto krs = make_rsrc(reinterpret_cast<const unsigned char*>(k) + head_base * TILE,
+                             (int64_t)n_h * TILE);
+  const auto vrs = make_rsrc(reinterpret_cast<const unsigned char*>(v) + head_base * TILE,
+                             (int64_t)n_h * TILE);
+  uint32_t ro[KR::PER_WAVE];
+  KR::offsets(ro, wave, lane);
+  int rb[2], tb[2];
+  KR::row_bases(rb, lane);
+  KR::tr_bases(tb, lane);
+  build_bias_table<SPT, 9>(btab, L, h, tid, 2 * S);
+
+  // key tile of step s: an entry outside [0, n_h) is a tile whose keys are
+  // all masked (cut 8), read from tile 0
+  auto tile_of = [&](int s, int& cut) {
+    const int c = cp[beg + s / SPT];
+    const bool ok = c >= 0 && c < n_h;
+    cut = ok ? cut_of(tile_extent(L, h, c)) : 8;
+    return ok ? c : 0;
+  };
+  auto stage = [&](int s, unsigned char* kd, unsigned char* vd) {
+    int cut;
+    const int c = tile_of(s, cut);
+    const uint32_t so = (uint32_t)(c * TILE + (s % SPT) * SK * D * 2);
+    KR::copy(krs, so, kd, ro, wave);
+    KR::copy(vrs, so, vd, ro, wave);
+  };
+
+  f32x16 dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
+
+  auto step = [&](int s, const unsigned char* ks, const unsigned char* vs, unsigned char* kn,
+                  unsigned char* vn) {
+    // step s landed in every wave and every wave is past step s-1, whose
+    // buffers the copies of step s+1 overwrite (a bare s_barrier: nothing
+    // else is in flight)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s + 1 < N) stage(s + 1, kn, vn);
+    int cut;
+    tile_of(s, cut);
+    f32x16 st[2], dpt[2];
+    load_bias(st, &btab.v[cut][s % SPT][0][hf][0]);
+    dpt[0] = f32x16{};
+    dpt[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        st[b] = mfma32(KR::row(ks, rb, kk, b), qr[kk], st[b]);
+        dpt[b] = mfma32(KR::row(vs, rb, kk, b), dor[kk], dpt[b]);
+      }
+    // element i of block b is key 32b + 16(i/8) + 8hf + i%8 of the step
+    bf16x8 ds[4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2_(fmaf(st[b][i], scale_log2, -l2));
+        ds[2 * b + i / 8][i % 8] = (__bf16)(p * (dpt[b][i] - dl));
+      }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        dqa[db] = mfma32(KR::tr(ks, tb, db, t), ds[t], dqa[db]);
+  };
+
+  if (N > 0) stage(0, k0, v0);
+  int s = 0;
+  for (; s + 1 < N; s += 2) {
+    step(s, k0, v0, k1, v1);
+    step(s + 1, k1, v1, k0, v0);
+  }
+  if (s < N) step(s, k0, v0, k1, v1);
+
+  const TileExtent e = tile_extent(L, h, (int)(g - head_base));
+  const int64_t row = slot_row(L, e, h, wave * 32 + n);
+  if (row >= 0) {
+    __bf16* out = dq + row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 w;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) w[b] = (__bf16)(dqa[db][4 * a + b] * sm_scale);
+        *reinterpret_cast<bf16x4*>(out + db * 32 + 8 * a + 4 * hf) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
 // One workgroup per key tile, wave w owning keys 32w..32w+31 (their K and V
 // rows in registers).  Per 32-query step of every query tile that keeps the
 // key tile:  S = Q K^T (seeded with -lse/sm_scale), dP = dO V^T (seeded with
@@ -578,7 +607,7 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 struct BwdWs {
-  void *qp, *kp, *vp, *dop, *ktp;
+  void *qp, *kp, *vp, *dop;
   float *lse2, *delta, *seed_s, *seed_dp;
   int32_t *cnt, *colt_ptr, *rowt;
 };
@@ -595,7 +624,6 @@ BwdWs carve(const DevLayout& L, int64_t nnz, void* base, int64_t* total) {
   const int64_t tiles = L.tile_off[L.heads];
   const int64_t tb = tiles * L.S * L.d * 2;
   w.qp = take(tb); w.kp = take(tb); w.vp = take(tb); w.dop = take(tb);
-  w.ktp = take(tb);
   w.lse2 = static_cast<float*>(take(tiles * L.S * 4));
   w.delta = static_cast<float*>(take(tiles * L.S * 4));
   w.seed_s = static_cast<float*>(take(tiles * L.S * 4));
@@ -615,8 +643,8 @@ void launch_products(const DevLayout& L, const BwdWs& w, const int32_t* row_ptr,
   const float sl2 = sm_scale * kLog2e;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, S>), dim3(G), dim3(2 * S), 0, s, L,
                      (const __bf16*)w.qp, (const __bf16*)w.kp, (const __bf16*)w.vp,
-                     (const __bf16*)w.ktp, (const __bf16*)w.dop, w.lse2, w.delta, row_ptr, col_idx,
-                     sl2, sm_scale, (__bf16*)dq);
+                     (const __bf16*)w.dop, w.lse2, w.delta, row_ptr, col_idx, sl2, sm_scale,
+                     (__bf16*)dq);
   hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, S>), dim3(G), dim3(2 * S), 0, s, L,
                      (const __bf16*)w.qp, (const __bf16*)w.kp, (const __bf16*)w.vp,
                      (const __bf16*)w.dop, w.seed_s, w.seed_dp, w.colt_ptr, w.rowt, cap, sl2,
@@ -641,8 +669,7 @@ int launch_sparse_attn_bwd(const DevLayout& L, const void* q, const void* k, con
   int64_t total = 0;
   const BwdWs w = carve(L, nnz, workspace, &total);
   const struct { const void* x; void* y; int dir; } perms[] = {
-      {q, w.qp, VEDA_FWD}, {k, w.kp, VEDA_FWD}, {v, w.vp, VEDA_FWD}, {d_o, w.dop, VEDA_FWD},
-      {k, w.ktp, VEDA_FWD_T}};
+      {q, w.qp, VEDA_FWD}, {k, w.kp, VEDA_FWD}, {v, w.vp, VEDA_FWD}, {d_o, w.dop, VEDA_FWD}};
   for (const auto& p : perms)
     if (launch_permute(L, VEDA_BF16, p.dir, p.x, p.y, s) != VEDA_OK) return VEDA_ERR_LAUNCH;
   hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L,
