@@ -35,6 +35,9 @@ using namespace attn;
 
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt operand: vmcnt(0) expcnt(7) lgkmcnt(0) (vmcnt bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmLgkm0 = 0x0070;
 
 // Row (token * heads + head) of slot u of a tile with extent e, or -1 for a
 // padding slot.
@@ -333,27 +336,32 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
     cut = ok ? cut_of(tile_extent(L, h, c)) : 8;
     return ok ? c : 0;
   };
+  // copies of step s; returns its mask cut
   auto stage = [&](int s, unsigned char* kd, unsigned char* vd) {
     int cut;
     const int c = tile_of(s, cut);
     const uint32_t so = (uint32_t)(c * TILE + (s % SPT) * SK * D * 2);
     KR::copy(krs, so, kd, ro, wave);
     KR::copy(vrs, so, vd, ro, wave);
+    return cut;
   };
 
   f32x16 dqa[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
 
+  int cut_next = 0;   // mask cut of the step staged last
   auto step = [&](int s, const unsigned char* ks, const unsigned char* vs, unsigned char* kn,
                   unsigned char* vn) {
     // step s landed in every wave and every wave is past step s-1, whose
-    // buffers the copies of step s+1 overwrite (a bare s_barrier: nothing
-    // else is in flight)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (s + 1 < N) stage(s + 1, kn, vn);
-    int cut;
-    tile_of(s, cut);
+    // buffers the copies of step s+1 overwrite.  The wait is the builtin, so
+    // that the compiler knows no copy is in flight after it (it would
+    // otherwise wait for the next step's copies before this step's reads);
+    // the barrier is a bare s_barrier that no memory access crosses.
+    __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+    asm volatile("s_barrier" ::: "memory");
+    const int cut = cut_next;
+    if (s + 1 < N) cut_next = stage(s + 1, kn, vn);
     f32x16 st[2], dpt[2];
     load_bias(st, &btab.v[cut][s % SPT][0][hf][0]);
     dpt[0] = f32x16{};
@@ -381,7 +389,7 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
         dqa[db] = mfma32(KR::tr(ks, tb, db, t), ds[t], dqa[db]);
   };
 
-  if (N > 0) stage(0, k0, v0);
+  if (N > 0) cut_next = stage(0, k0, v0);
   int s = 0;
   for (; s + 1 < N; s += 2) {
     step(s, k0, v0, k1, v1);
