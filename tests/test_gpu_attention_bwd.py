@@ -148,3 +148,34 @@ def test_backward_deterministic():
     _, _, g2 = _forward_backward(r)
     for x, t in zip(a, g2):
         assert np.array_equal(x, bf16_bits(t))
+
+
+def test_backward_bench_config_writes_every_row():
+    """Every element of dQ, dK and dV is written at the Wan-1.3B-like 90 %
+    layer (outputs start as NaN): the dK/dV workgroups, dispatched heaviest
+    key tile first, cover every key tile once, including the tiles no query
+    tile keeps (their dK = dV = 0)."""
+    _say("backward wan1.3b 90% every row written")
+    torch = need_gpu()
+    r = Run("wan1.3b-480p-81f", sparsity=90)
+    out = r.forward_fused()
+    rng = np.random.default_rng(13)
+    do = to_dev_bf16(bf16_round(rng.normal(size=(r.wl.q.shape[0], r.heads, r.d)).astype(np.float32)))
+    grads = tuple(torch.full_like(r.q, float("nan")) for _ in range(3))
+    r.layer.backward(r.q, r.k, r.v, out, do, r.sm_scale, grads=grads)
+    torch.cuda.synchronize()
+    for name, t in zip(("dq", "dk", "dv"), grads):
+        assert bool(torch.isfinite(t).all()), name
+    # key tiles no row keeps: zero dK and dV on their real slots
+    for h in range(r.heads):
+        rp, ci = r.csr_head(h)
+        kept = np.zeros(r.L.n(h), bool)
+        kept[ci[(ci >= 0) & (ci < r.L.n(h))]] = True
+        if kept.all():
+            continue
+        ht = r.tilings[h]
+        gk = oracle.gather(bf16_f64(grads[1])[:, h, :], r.T, r.H, r.W, ht.shape)
+        gv = oracle.gather(bf16_f64(grads[2])[:, h, :], r.T, r.H, r.W, ht.shape)
+        for j in np.flatnonzero(~kept)[:8]:
+            sl = slice(j * r.S, (j + 1) * r.S)
+            assert np.all(gk[sl][ht.valid[sl]] == 0) and np.all(gv[sl][ht.valid[sl]] == 0), (h, j)

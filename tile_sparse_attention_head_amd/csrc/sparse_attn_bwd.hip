@@ -17,8 +17,9 @@
 //    in registers); per 64-key step S^T = K Q^T (seeded with the mask rows),
 //    dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T, with K^T read
 //    transposed out of the staged K rows.
-//  * dK/dV: one workgroup per key tile, wave w owns 32 keys (K and V rows in
-//    registers); per 32-query step of every query tile keeping the key tile:
+//  * dK/dV: one workgroup per key tile, the heaviest key tiles dispatched
+//    first; wave w owns 32 keys (K and V rows in registers); per 32-query
+//    step of every query tile keeping the key tile:
 //    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS, with dO^T and
 //    Q^T read transposed out of the staged rows.  Padding query rows have
 //    P = 0; rows of padding keys are computed and never stored.
@@ -161,6 +162,55 @@ __global__ __launch_bounds__(kThreads) void csrt_scan_kernel(int64_t tiles,
     carry += tot;
   }
   if (threadIdx.x == 0) ptr[tiles] = carry;
+}
+
+// Dispatch order of the dK/dV workgroups, longest first.  How many query
+// tiles keep a key tile varies widely (tiles no row keeps, tiles nearly
+// every row keeps), and one workgroup computes one key tile, so the heavy
+// tiles must start first or they alone set the kernel's end.  Workgroup b
+// takes order[b]: the key tiles by descending pair count, in 64 buckets of
+// 2^shift counts (order within a bucket arbitrary), dealt round-robin to the
+// XCDs by the hardware.  (Sorting within each XCD's contiguous range
+// instead, which keeps neighbouring key tiles on one L2, measured slower.)
+// Each key tile's gradients are computed by one workgroup whatever the
+// order, so the order changes the time only, never a result.  One
+// workgroup; `segs` contiguous ranges are sorted separately (1: the grid).
+constexpr int kOrderBuckets = 64;
+__global__ __launch_bounds__(kThreads) void csrt_order_kernel(int64_t tiles, int segs,
+                                                              const int32_t* __restrict__ cnt,
+                                                              int32_t* __restrict__ order) {
+  __shared__ int hist[kOrderBuckets];
+  __shared__ int red[kThreads / 64];
+  int m = 0;
+  for (int64_t x = threadIdx.x; x < tiles; x += kThreads) m = max(m, cnt[x]);
+  for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = 0;
+  for (int w = 0; w < kThreads / 64; ++w) m = max(m, red[w]);
+  int shift = 0;
+  while ((m >> shift) >= kOrderBuckets) ++shift;
+  auto bucket = [&](int64_t x) { return kOrderBuckets - 1 - (cnt[x] >> shift); };
+  const int64_t per = tiles / segs, rem = tiles % segs;
+  for (int sg = 0; sg < segs; ++sg) {
+    const int64_t lo = sg * per + min<int64_t>(sg, rem), hi = lo + per + (sg < rem ? 1 : 0);
+    if (threadIdx.x < kOrderBuckets) hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int64_t x = lo + threadIdx.x; x < hi; x += kThreads) atomicAdd(&hist[bucket(x)], 1);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int a = 0;
+      for (int b = 0; b < kOrderBuckets; ++b) {
+        const int t = hist[b];
+        hist[b] = a;
+        a += t;
+      }
+    }
+    __syncthreads();
+    for (int64_t x = lo + threadIdx.x; x < hi; x += kThreads)
+      order[lo + atomicAdd(&hist[bucket(x)], 1)] = (int32_t)x;
+    __syncthreads();
+  }
 }
 
 // rowt[ptr[g] ..] = the head-local query tiles keeping key tile g, ascending
@@ -428,8 +478,9 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
     const float* __restrict__ seed_s, const float* __restrict__ seed_dp,
-    const int32_t* __restrict__ colt_ptr, const int32_t* __restrict__ rowt, int32_t cap,
-    float scale_log2, float sm_scale, __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
+    const int32_t* __restrict__ colt_ptr, const int32_t* __restrict__ rowt,
+    const int32_t* __restrict__ order, int32_t cap, float scale_log2, float sm_scale,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
   constexpr int NW = S / 32, SQ = 32, SPQ = S / SQ, KS = D / 16, DB = D / 32, TILE = S * D * 2;
   constexpr int NB = 4;                                 // steps in flight
   using QR = TrBuf<SQ, D, D * 2, NW>;                 // Q or dO rows of a step, swap23 order
@@ -441,7 +492,7 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dkv_kernel(
     return P == 0 ? b0 : P == 1 ? b1 : P == 2 ? b2 : b3;
   };
 
-  const int64_t g = xcd_remap(blockIdx.x, gridDim.x);   // key tile
+  const int64_t g = ((cint32*)order)[blockIdx.x];   // key tile, longest first
   const int h = head_of_tile(L, g);
   const int64_t head_base = L.tile_off[h];
   const int n_h = (int)(L.tile_off[h + 1] - head_base);
@@ -617,7 +668,7 @@ int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 struct BwdWs {
   void *qp, *kp, *vp, *dop;
   float *lse2, *delta, *seed_s, *seed_dp;
-  int32_t *cnt, *colt_ptr, *rowt;
+  int32_t *cnt, *colt_ptr, *rowt, *order;
 };
 
 BwdWs carve(const DevLayout& L, int64_t nnz, void* base, int64_t* total) {
@@ -639,6 +690,7 @@ BwdWs carve(const DevLayout& L, int64_t nnz, void* base, int64_t* total) {
   w.cnt = static_cast<int32_t*>(take(tiles * 4));
   w.colt_ptr = static_cast<int32_t*>(take((tiles + 1) * 4));
   w.rowt = static_cast<int32_t*>(take(nnz * 4 + 4));
+  w.order = static_cast<int32_t*>(take(tiles * 4));
   *total = o;
   return w;
 }
@@ -655,8 +707,8 @@ void launch_products(const DevLayout& L, const BwdWs& w, const int32_t* row_ptr,
                      (__bf16*)dq);
   hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, S>), dim3(G), dim3(2 * S), 0, s, L,
                      (const __bf16*)w.qp, (const __bf16*)w.kp, (const __bf16*)w.vp,
-                     (const __bf16*)w.dop, w.seed_s, w.seed_dp, w.colt_ptr, w.rowt, cap, sl2,
-                     sm_scale, (__bf16*)dk, (__bf16*)dv);
+                     (const __bf16*)w.dop, w.seed_s, w.seed_dp, w.colt_ptr, w.rowt, w.order, cap,
+                     sl2, sm_scale, (__bf16*)dk, (__bf16*)dv);
 }
 
 }  // namespace
@@ -686,6 +738,8 @@ int launch_sparse_attn_bwd(const DevLayout& L, const void* q, const void* k, con
   hipLaunchKernelGGL(csrt_count_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L, row_ptr,
                      col_idx, w.cnt);
   hipLaunchKernelGGL(csrt_scan_kernel, dim3(1), dim3(kThreads), 0, s, tiles, w.cnt, w.colt_ptr);
+  hipLaunchKernelGGL(csrt_order_kernel, dim3(1), dim3(kThreads), 0, s, tiles,
+                     1, w.cnt, w.order);
   hipLaunchKernelGGL(csrt_fill_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L, row_ptr,
                      col_idx, w.colt_ptr, (int32_t)nnz, w.rowt);
   if (L.d == 128)
