@@ -412,17 +412,40 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
     asm volatile("s_barrier" ::: "memory");
     const int cut = cut_next;
     if (s + 1 < N) cut_next = stage(s + 1, kn, vn);
+    // S^T starts from the step's mask rows, dP^T from -D (so dS = P dP)
     f32x16 st[2], dpt[2];
     load_bias(st, &btab.v[cut][s % SPT][0][hf][0]);
-    dpt[0] = f32x16{};
-    dpt[1] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        st[b] = mfma32(KR::row(ks, rb, kk, b), qr[kk], st[b]);
-        dpt[b] = mfma32(KR::row(vs, rb, kk, b), dor[kk], dpt[b]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      dpt[0][i] = -dl;
+      dpt[1][i] = -dl;
+    }
+    // Products laid out by hand in slots of one MFMA each, with the LDS read
+    // of a later slot's operand; the compiler may not move work across
+    // slots.  S^T and dP^T alternate (row reads LA1 slots ahead); the first
+    // K^T operands are read while P and dS are computed, then the dQ^T
+    // products (transposed reads LA2 slots ahead).
+    constexpr int LA1 = 2, N1 = 4 * KS, LA2 = 3, N2 = 4 * DB;
+    auto op1 = [&](int i) { return KR::row((i & 1) ? vs : ks, rb, i >> 2, (i >> 1) & 1); };
+    auto op2 = [&](int i) { return KR::tr(ks, tb, i % DB, i / DB); };
+    bf16x8 o1[LA1 + 1], o2[LA2 + 1];
+    static_for<0, LA1>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      o1[i] = op1(i);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, N1>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int kk = i >> 2, b = (i >> 1) & 1;
+      if constexpr (i + LA1 < N1) o1[(i + LA1) % (LA1 + 1)] = op1(i + LA1);
+      if constexpr (i & 1) dpt[b] = mfma32(o1[i % (LA1 + 1)], dor[kk], dpt[b]);
+      else st[b] = mfma32(o1[i % (LA1 + 1)], qr[kk], st[b]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<0, LA2>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      o2[i] = op2(i);
+    });
     // element i of block b is key 32b + 16(i/8) + 8hf + i%8 of the step
     bf16x8 ds[4];
 #pragma unroll
@@ -430,13 +453,15 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = exp2_(fmaf(st[b][i], scale_log2, -l2));
-        ds[2 * b + i / 8][i % 8] = (__bf16)(p * (dpt[b][i] - dl));
+        ds[2 * b + i / 8][i % 8] = (__bf16)(p * dpt[b][i]);
       }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        dqa[db] = mfma32(KR::tr(ks, tb, db, t), ds[t], dqa[db]);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, N2>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + LA2 < N2) o2[(i + LA2) % (LA2 + 1)] = op2(i + LA2);
+      dqa[i % DB] = mfma32(o2[i % (LA2 + 1)], ds[i / DB], dqa[i % DB]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   if (N > 0) cut_next = stage(0, k0, v0);
