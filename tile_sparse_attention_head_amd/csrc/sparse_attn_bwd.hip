@@ -8,11 +8,12 @@
 //   dK = sm_scale dS^T Q,  dV = P^T dO.
 //
 // Kernels, all on the matrix cores in the forward's transposed forms:
-//  * prep: the inputs gathered into tile order (Q, K, V, dO); per query
-//    slot D and lse*log2(e)
+//  * prep: the inputs gathered into tile order (Q, K, V; dO in the pass that
+//    computes D); per query slot D and lse*log2(e)
 //    (+inf for padding slots, so their probabilities are exactly 0); the CSR
-//    transposed (per key tile, the query tiles keeping it, ascending, found
-//    by binary search in each sorted row: deterministic, no atomics).
+//    transposed (per key tile, the query tiles keeping it, ascending: counts
+//    by integer atomics, positions by binary search in each sorted row, so
+//    the lists are deterministic); the dK/dV dispatch order.
 //  * dQ: one workgroup per query tile, wave w owns 32 queries (Q and dO rows
 //    in registers); per 64-key step S^T = K Q^T (seeded with the mask rows),
 //    dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T, with K^T read
@@ -58,6 +59,8 @@ __device__ __forceinline__ int64_t slot_row(const DevLayout& L, const TileExtent
 //   values of its S and dP accumulators, so that P = exp2(sm_scale log2(e) S)
 //   and dS = P dP with no further per-element work)
 // Padding slots: delta = 0, lse2 = +inf, seed_s = -inf (probabilities 0).
+// The same pass gathers dO into tile order (dop, zero rows for padding
+// slots) and clears the key-tile pair counts of tile g.
 __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(DevLayout L,
                                                              const __bf16* __restrict__ o,
                                                              const __bf16* __restrict__ d_o,
@@ -66,8 +69,11 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(DevLayout L,
                                                              float* __restrict__ delta,
                                                              float* __restrict__ lse2,
                                                              float* __restrict__ seed_s,
-                                                             float* __restrict__ seed_dp) {
+                                                             float* __restrict__ seed_dp,
+                                                             __bf16* __restrict__ dop,
+                                                             int32_t* __restrict__ cnt) {
   const int64_t g = blockIdx.x;
+  if (threadIdx.x == 0) cnt[g] = 0;
   const int h = head_of_tile(L, g);
   const TileExtent e = tile_extent(L, h, (int)(g - L.tile_off[h]));
   const int cpr = L.d / 8;                  // 16-byte chunks per row (a power of two)
@@ -77,12 +83,14 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(DevLayout L,
     const int u = u0 + (int)threadIdx.x / cpr;
     const int64_t row = u < L.S ? slot_row(L, e, h, u) : -1;
     float acc = 0.f;
+    bf16x8 b = {};
     if (row >= 0) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * L.d + 8 * c);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(d_o + row * L.d + 8 * c);
+      b = *reinterpret_cast<const bf16x8*>(d_o + row * L.d + 8 * c);
 #pragma unroll
       for (int x = 0; x < 8; ++x) acc = fmaf((float)a[x], (float)b[x], acc);
     }
+    if (u < L.S) *reinterpret_cast<bf16x8*>(dop + (g * L.S + u) * L.d + 8 * c) = b;
     for (int off = cpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (u < L.S && c == 0) {
       const int64_t slot = g * L.S + u;
@@ -129,39 +137,25 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* t
   return base + incl - v;
 }
 
-// per key tile g: how many (query tile, occurrence) pairs keep it
+// per key tile: how many (query tile, occurrence) pairs keep it.  One thread
+// per CSR row adds its in-range entries with integer atomics (the counts do
+// not depend on the order of the additions); cnt starts at zero.  Entries
+// past `cap` (the CSR's entry count) are not read.
 __global__ __launch_bounds__(kThreads) void csrt_count_kernel(DevLayout L,
                                                               const int32_t* __restrict__ rp,
                                                               const int32_t* __restrict__ ci,
+                                                              int32_t cap,
                                                               int32_t* __restrict__ cnt) {
-  __shared__ int wave_tot[kThreads / 64];
-  const int64_t g = blockIdx.x;
-  const int h = head_of_tile(L, g);
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= L.tile_off[L.heads]) return;
+  const int h = head_of_tile(L, i);
   const int64_t off = L.tile_off[h];
-  const int n = (int)(L.tile_off[h + 1] - off), j = (int)(g - off);
-  int c = 0;
-  for (int i = threadIdx.x; i < n; i += kThreads)
-    c += count_in_row(ci, rp[off + i], rp[off + i + 1], j);
-  int tot = 0;
-  block_exclusive_scan(c, wave_tot, &tot);
-  if (threadIdx.x == 0) cnt[g] = tot;
-}
-
-// ptr[g] = sum of cnt[0..g), ptr[tiles] = total: one workgroup, chunks in order
-__global__ __launch_bounds__(kThreads) void csrt_scan_kernel(int64_t tiles,
-                                                             const int32_t* __restrict__ cnt,
-                                                             int32_t* __restrict__ ptr) {
-  __shared__ int wave_tot[kThreads / 64];
-  int carry = 0;
-  for (int64_t x0 = 0; x0 < tiles; x0 += kThreads) {
-    const int64_t x = x0 + threadIdx.x;
-    const int v = x < tiles ? cnt[x] : 0;
-    int tot = 0;
-    const int ex = block_exclusive_scan(v, wave_tot, &tot);
-    if (x < tiles) ptr[x] = carry + ex;
-    carry += tot;
+  const int n = (int)(L.tile_off[h + 1] - off);
+  const int b = max(rp[i], 0), e = min(rp[i + 1], cap);
+  for (int p = b; p < e; ++p) {
+    const int j = ci[p];
+    if (j >= 0 && j < n) atomicAdd(&cnt[off + j], 1);
   }
-  if (threadIdx.x == 0) ptr[tiles] = carry;
 }
 
 // Dispatch order of the dK/dV workgroups, longest first.  How many query
@@ -173,12 +167,11 @@ __global__ __launch_bounds__(kThreads) void csrt_scan_kernel(int64_t tiles,
 // XCDs by the hardware.  (Sorting within each XCD's contiguous range
 // instead, which keeps neighbouring key tiles on one L2, measured slower.)
 // Each key tile's gradients are computed by one workgroup whatever the
-// order, so the order changes the time only, never a result.  One
-// workgroup; `segs` contiguous ranges are sorted separately (1: the grid).
+// order, so the order changes the time only, never a result.  Run by one workgroup;
+// `segs` contiguous ranges are sorted separately (1: the grid).
 constexpr int kOrderBuckets = 64;
-__global__ __launch_bounds__(kThreads) void csrt_order_kernel(int64_t tiles, int segs,
-                                                              const int32_t* __restrict__ cnt,
-                                                              int32_t* __restrict__ order) {
+__device__ void csrt_order(int64_t tiles, int segs, const int32_t* __restrict__ cnt,
+                           int32_t* __restrict__ order) {
   __shared__ int hist[kOrderBuckets];
   __shared__ int red[kThreads / 64];
   int m = 0;
@@ -211,6 +204,26 @@ __global__ __launch_bounds__(kThreads) void csrt_order_kernel(int64_t tiles, int
       order[lo + atomicAdd(&hist[bucket(x)], 1)] = (int32_t)x;
     __syncthreads();
   }
+}
+
+// ptr[g] = sum of cnt[0..g), ptr[tiles] = total, then the dK/dV dispatch
+// order (csrt_order): one workgroup, chunks in order
+__global__ __launch_bounds__(kThreads) void csrt_scan_kernel(int64_t tiles,
+                                                             const int32_t* __restrict__ cnt,
+                                                             int32_t* __restrict__ ptr,
+                                                             int32_t* __restrict__ order) {
+  __shared__ int wave_tot[kThreads / 64];
+  int carry = 0;
+  for (int64_t x0 = 0; x0 < tiles; x0 += kThreads) {
+    const int64_t x = x0 + threadIdx.x;
+    const int v = x < tiles ? cnt[x] : 0;
+    int tot = 0;
+    const int ex = block_exclusive_scan(v, wave_tot, &tot);
+    if (x < tiles) ptr[x] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) ptr[tiles] = carry;
+  csrt_order(tiles, 1, cnt, order);
 }
 
 // rowt[ptr[g] ..] = the head-local query tiles keeping key tile g, ascending
@@ -754,17 +767,16 @@ int launch_sparse_attn_bwd(const DevLayout& L, const void* q, const void* k, con
   int64_t total = 0;
   const BwdWs w = carve(L, nnz, workspace, &total);
   const struct { const void* x; void* y; int dir; } perms[] = {
-      {q, w.qp, VEDA_FWD}, {k, w.kp, VEDA_FWD}, {v, w.vp, VEDA_FWD}, {d_o, w.dop, VEDA_FWD}};
+      {q, w.qp, VEDA_FWD}, {k, w.kp, VEDA_FWD}, {v, w.vp, VEDA_FWD}};
   for (const auto& p : perms)
     if (launch_permute(L, VEDA_BF16, p.dir, p.x, p.y, s) != VEDA_OK) return VEDA_ERR_LAUNCH;
   hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L,
                      (const __bf16*)o, (const __bf16*)d_o, lse, sm_scale, w.delta, w.lse2,
-                     w.seed_s, w.seed_dp);
-  hipLaunchKernelGGL(csrt_count_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L, row_ptr,
-                     col_idx, w.cnt);
-  hipLaunchKernelGGL(csrt_scan_kernel, dim3(1), dim3(kThreads), 0, s, tiles, w.cnt, w.colt_ptr);
-  hipLaunchKernelGGL(csrt_order_kernel, dim3(1), dim3(kThreads), 0, s, tiles,
-                     1, w.cnt, w.order);
+                     w.seed_s, w.seed_dp, (__bf16*)w.dop, w.cnt);
+  hipLaunchKernelGGL(csrt_count_kernel, dim3((unsigned)((tiles + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, L, row_ptr, col_idx, (int32_t)nnz, w.cnt);
+  hipLaunchKernelGGL(csrt_scan_kernel, dim3(1), dim3(kThreads), 0, s, tiles, w.cnt, w.colt_ptr,
+                     w.order);
   hipLaunchKernelGGL(csrt_fill_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L, row_ptr,
                      col_idx, w.colt_ptr, (int32_t)nnz, w.rowt);
   if (L.d == 128)
