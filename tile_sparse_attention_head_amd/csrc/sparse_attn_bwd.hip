@@ -227,8 +227,8 @@ __global__ __launch_bounds__(kThreads) void csrt_scan_kernel(int64_t tiles,
 }
 
 // rowt[ptr[g] ..] = the head-local query tiles keeping key tile g, ascending
-// (a tile kept twice by one row appears twice).  Writes stay below `cap`
-// (the CSR's entry count) even for rows that are not sorted.
+// (a tile kept twice by one row appears twice).  Reads and writes stay below
+// `cap` (the CSR's entry count) even for rows that are not sorted.
 __global__ __launch_bounds__(kThreads) void csrt_fill_kernel(DevLayout L,
                                                              const int32_t* __restrict__ rp,
                                                              const int32_t* __restrict__ ci,
@@ -243,7 +243,8 @@ __global__ __launch_bounds__(kThreads) void csrt_fill_kernel(DevLayout L,
   int base = ptr[g];
   for (int i0 = 0; i0 < n; i0 += kThreads) {
     const int i = i0 + threadIdx.x;
-    const int c = i < n ? count_in_row(ci, rp[off + i], rp[off + i + 1], j) : 0;
+    const int c =
+        i < n ? count_in_row(ci, max(rp[off + i], 0), min(rp[off + i + 1], cap), j) : 0;
     int tot = 0;
     const int ex = block_exclusive_scan(c, wave_tot, &tot);
     for (int r = 0; r < c; ++r)
@@ -353,8 +354,8 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
     const float* __restrict__ lse2, const float* __restrict__ delta,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, float scale_log2,
-    float sm_scale, __bf16* __restrict__ dq) {
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int32_t cap,
+    float scale_log2, float sm_scale, __bf16* __restrict__ dq) {
   constexpr int NW = S / 32, SK = 64, SPT = S / SK, KS = D / 16, DB = D / 32, TILE = S * D * 2;
   using KR = TrBuf<SK, D, D * 2, NW>;                 // K or V rows of a step
   __shared__ __attribute__((aligned(1024))) unsigned char k0[KR::BYTES], v0[KR::BYTES];
@@ -377,8 +378,8 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
 
   cint32* rp = (cint32*)row_ptr;
   cint32* cp = (cint32*)col_idx;
-  int beg = rp[g], end = rp[g + 1];
-  if (end < beg) end = beg;
+  // the row, clamped to the CSR's entries [0, cap)
+  const int beg = min(max(rp[g], 0), cap), end = max(beg, min(rp[g + 1], cap));
   const int N = (end - beg) * SPT;
   const auto krs = make_rsrc(reinterpret_cast<const unsigned char*>(k) + head_base * TILE,
                              (int64_t)n_h * TILE);
@@ -741,8 +742,8 @@ void launch_products(const DevLayout& L, const BwdWs& w, const int32_t* row_ptr,
   const float sl2 = sm_scale * kLog2e;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, S>), dim3(G), dim3(2 * S), 0, s, L,
                      (const __bf16*)w.qp, (const __bf16*)w.kp, (const __bf16*)w.vp,
-                     (const __bf16*)w.dop, w.lse2, w.delta, row_ptr, col_idx, sl2, sm_scale,
-                     (__bf16*)dq);
+                     (const __bf16*)w.dop, w.lse2, w.delta, row_ptr, col_idx, cap, sl2,
+                     sm_scale, (__bf16*)dq);
   hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, S>), dim3(G), dim3(2 * S), 0, s, L,
                      (const __bf16*)w.qp, (const __bf16*)w.kp, (const __bf16*)w.vp,
                      (const __bf16*)w.dop, w.seed_s, w.seed_dp, w.colt_ptr, w.rowt, w.order, cap,
