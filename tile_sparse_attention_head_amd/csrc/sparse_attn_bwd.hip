@@ -16,16 +16,17 @@
 //    the lists are deterministic); the dK/dV dispatch order.
 //  * dQ: one workgroup per query tile, wave w owns 32 queries (Q and dO rows
 //    in registers); per 64-key step S^T = K Q^T (seeded with the mask rows),
-//    dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T, with K^T read
-//    transposed out of the staged K rows.
+//    dP^T = V dO^T - D (seeded with -D), dS^T = P^T dP^T, dQ^T += K^T dS^T,
+//    with K^T read transposed out of the staged K rows.
 //  * dK/dV: one workgroup per key tile, the heaviest key tiles dispatched
 //    first; wave w owns 32 keys (K and V rows in registers); per 32-query
 //    step of every query tile keeping the key tile:
 //    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS, with dO^T and
 //    Q^T read transposed out of the staged rows.  Padding query rows have
 //    P = 0; rows of padding keys are computed and never stored.
-// Steps stage their operands HBM -> LDS with buffer_load ... lds; one
-// workgroup's copies overlap the other resident workgroup's products.
+// Steps stage their operands HBM -> LDS with buffer_load ... lds, two (dQ)
+// or four (dK/dV) steps deep, so a step's copies overlap earlier steps'
+// products.
 // Results are written straight to token order; every output row is written
 // once (a tile that no CSR row keeps gets dK = dV = 0, an empty row dQ = 0).
 #include "attn_common.hpp"
@@ -345,10 +346,10 @@ struct TrBuf {
 // ---------------------------------------------------------------- dQ
 // One workgroup per query tile, wave w owning queries 32w..32w+31 (Q and dO
 // rows in registers).  Per 64-key step of every kept key tile:
-// S^T = K Q^T (seeded with the step's mask rows), dP^T = V dO^T,
-// dS^T = P^T (dP^T - D), dQ^T += K^T dS^T, the A operand K^T read
-// transposed out of the staged K rows.  K and V rows of a step are staged
-// in two buffers: step s+1 is copied while step s computes.
+// S^T = K Q^T (seeded with the step's mask rows), dP^T = V dO^T - D
+// (seeded with -D), dS^T = P^T dP^T, dQ^T += K^T dS^T, the A operand K^T
+// read transposed out of the staged K rows.  K and V rows of a step are
+// staged in two buffers: step s+1 is copied while step s computes.
 template <int D, int S>
 __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
