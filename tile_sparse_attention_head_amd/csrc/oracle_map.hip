@@ -303,19 +303,48 @@ __global__ __launch_bounds__(256) void map_reduce_kernel(
 
 }  // namespace
 
-int64_t map_chunks(int64_t n_sub, int64_t max_tiles) {
+// Pass-1 chunks per subset tile.  Pass 1 runs n_sub * c equal workgroups,
+// `slots` of them at a time; its time is about rounds(c) * (work of one
+// workgroup) with rounds(c) = ceil(n_sub c / slots) and one workgroup's work
+// ceil(max_tiles / c) * SPT steps plus a fixed cost of about kChunkFixed
+// steps (loading its queries, the first copies, the final partials).  c is
+// the smallest minimiser over 1 .. kMaxChunks: a last round that would run
+// nearly empty is avoided by cutting the key tiles finer.
+constexpr int64_t kChunkFixed = 6;
+int64_t map_chunks(int64_t n_sub, int64_t max_tiles, int64_t spt, int64_t slots) {
   if (n_sub <= 0) return 1;
-  int64_t c = (1536 + n_sub - 1) / n_sub;   // about 1.5 K workgroups in pass 1
-  if (c > kMaxChunks) c = kMaxChunks;
-  if (c > max_tiles) c = max_tiles;
-  return c < 1 ? 1 : c;
+  if (slots < 1) slots = 1;
+  int64_t best = 1, best_t = -1;
+  for (int64_t c = 1; c <= kMaxChunks && c <= max_tiles; ++c) {
+    const int64_t rounds = (n_sub * c + slots - 1) / slots;
+    const int64_t t = rounds * ((max_tiles + c - 1) / c * spt + kChunkFixed);
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      best = c;
+    }
+  }
+  return best;
 }
 
+// Workgroups of pass 1 resident at once on the current device.
+template <int D, int S>
+int64_t map_slots() {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, map_stats_kernel<D, S>, 2 * S, 0) !=
+          hipSuccess)
+    return 1;
+  return (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+}
+
+// The workspace holds the partials of kMaxChunks chunks, whatever the
+// launch chooses.
 int64_t map_workspace_bytes(const DevLayout& L, int64_t n_sub) {
   if (n_sub <= 0) return 0;
   const int64_t S = L.S;
   const int64_t rm = ((n_sub * L.max_tiles * S * 4) + 255) / 256 * 256;
-  const int64_t mlb = n_sub * map_chunks(n_sub, L.max_tiles) * S * 8;
+  const int64_t mlb = n_sub * kMaxChunks * S * 8;
   return rm + mlb;
 }
 
@@ -324,7 +353,8 @@ int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm
                       hipStream_t s) {
   if (n_sub == 0) return VEDA_OK;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
-  const int chunks = (int)map_chunks(n_sub, L.max_tiles);
+  const int64_t slots = L.d == 128 ? map_slots<128, 128>() : map_slots<64, 64>();
+  const int chunks = (int)map_chunks(n_sub, L.max_tiles, L.S / 64, slots);
   float* rowmax = static_cast<float*>(workspace);
   const int64_t rm = ((n_sub * (int64_t)L.max_tiles * L.S * 4) + 255) / 256 * 256;
   float2* ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(workspace) + rm);

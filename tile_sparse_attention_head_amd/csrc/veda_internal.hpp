@@ -83,9 +83,7 @@ int launch_sparse_attn(const DevLayout& L, const void* q, const void* k, const v
 int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm_scale,
                       const int32_t* q_tiles, int n_sub, void* workspace, float* lse,
                       float* map, hipStream_t s);
-// Key-tile chunks per subset entry in the map's first pass, and the bytes of
-// workspace the map needs (row maxima, then per-chunk partial sums).
-int64_t map_chunks(int64_t n_sub, int64_t max_tiles);
+// Bytes of workspace the map needs (row maxima, then per-chunk partial sums).
 int64_t map_workspace_bytes(const DevLayout& L, int64_t n_sub);
 
 // Distillation step: workspace bytes, and the launch.
