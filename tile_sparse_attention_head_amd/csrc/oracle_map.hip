@@ -15,7 +15,10 @@
 //     per key tile, the maximum over the tile's real rows of
 //     exp2(largest logit - lse).
 // Splitting the key tiles into chunks gives pass 1 enough workgroups to fill
-// the chip whatever the subset size.
+// the chip whatever the subset size; the chunk count is chosen so that the
+// last round of workgroups is not nearly empty, and the workgroups are
+// ordered chunk-major so that those running together on one XCD share a
+// key-tile range in L2.
 //
 // Pass 1 uses the tile products of the attention kernel: 4 waves of 32
 // queries, K copied HBM -> LDS in 64-key steps two steps ahead, and per step
@@ -60,8 +63,11 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char k1[KB::BYTES];
   __shared__ BiasTable<SPT> btab;
 
+  // chunk-major: the workgroups running together on one XCD take the same
+  // key-tile range for consecutive subset tiles, which share it in L2
   const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
-  const int sub = (int)(b / chunks), c = (int)(b % chunks);
+  const int64_t n_sub = gridDim.x / chunks;
+  const int sub = (int)(b % n_sub), c = (int)(b / n_sub);
   const int64_t g = ((cint32*)q_tiles)[sub];
   if (g < 0 || g >= L.tile_off[L.heads]) return;   // the reduce pass writes a zero row
   const int h = head_of_tile(L, g);
