@@ -14,7 +14,10 @@ whose inputs are already resident in HBM, through the layer's fused calls:
 
 The context runs also time the same layer one method step per call
 (veda_tile_permute, veda_tripool_score, veda_select_tiles,
-veda_sparse_attn_fwd, inverse veda_tile_permute).
+veda_sparse_attn_fwd, inverse veda_tile_permute), the layer at 95 % and 0 %
+sparsity, with cold caches, the distillation step, the attention backward and
+the tiling search, and record the GPU clocks and socket power (amd-smi) while
+the attention kernel runs back to back.
 
 W untimed steps run first, then exactly K steps are timed between two device
 synchronisations.  Every stage is also bracketed by HIP events on the stream
@@ -394,6 +397,41 @@ def sweep():
     return out
 
 
+def clock_power(launch, kernel_ms: float, seconds: float = 1.5):
+    """GPU clocks and socket power while `launch` (one kernel) runs back to
+    back: about `seconds` of launches are queued and `amd-smi` (a child
+    process) is sampled in the middle.  None where amd-smi is missing or
+    fails."""
+    import shutil
+    import subprocess
+    import torch
+    exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if exe is None:
+        return None
+    torch.cuda.synchronize()
+    for _ in range(max(10, int(seconds * 1e3 / max(kernel_ms, 1e-3)))):
+        launch()
+    time.sleep(seconds * 0.4)
+    try:
+        r = subprocess.run([exe, "metric", "-g", "0", "-c", "-p", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        torch.cuda.synchronize()
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clk = g["clock"]
+        gfx = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")
+               and isinstance(clk[k].get("clk"), dict)]
+        return {"socket_power_w": g["power"]["socket_power"]["value"], "gfx_mhz_per_xcd": gfx,
+                "gfx_mhz_median": float(np.median(gfx)) if gfx else None,
+                "max_gfx_mhz": next((clk[k]["max_clk"]["value"] for k in sorted(clk)
+                                     if k.startswith("gfx_")), None),
+                "sampled": "amd-smi metric -c -p, %.1f s into %.1f s of back-to-back launches"
+                           % (seconds * 0.4, seconds)}
+    except Exception as exc:   # the tool's output format is not ours to rely on
+        torch.cuda.synchronize()
+        return {"error": f"{type(exc).__name__}: {exc}"[:200]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -541,6 +579,9 @@ def main():
                                  "attn_ms": dc["sparse_attn"], "map_ms": dc["map"]}
         del flush
         torch.cuda.empty_cache()
+        # the clock the attention kernel runs at, and the power it draws
+        context["clock_power_under_attention"] = clock_power(
+            lambda: b.layer.attend_tokens(b.cfg.sm_scale, b.out, with_lse=True), attn_ms)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1024 * 1024 // 4
