@@ -397,26 +397,42 @@ def sweep():
     return out
 
 
-def clock_power(launch, kernel_ms: float, seconds: float = 1.5):
+def clock_power(launch, seconds: float = 1.5):
     """GPU clocks and socket power while `launch` (one kernel) runs back to
-    back: about `seconds` of launches are queued and `amd-smi` (a child
-    process) is sampled in the middle.  None where amd-smi is missing or
-    fails."""
+    back for `seconds`: launches go out in batches of 20 (a synchronisation
+    after each keeps the queue short) while a thread runs `amd-smi` (a child
+    process) half way through.  None where amd-smi is missing; an error
+    record where its output cannot be read."""
     import shutil
     import subprocess
+    import threading
     import torch
     exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
     if exe is None:
         return None
+    out = {}
+
+    def sample():
+        time.sleep(seconds * 0.5)
+        try:
+            out["r"] = subprocess.run([exe, "metric", "-g", "0", "-c", "-p", "--json"],
+                                      capture_output=True, text=True, timeout=30)
+        except Exception as exc:
+            out["err"] = exc
+
     torch.cuda.synchronize()
-    for _ in range(max(10, int(seconds * 1e3 / max(kernel_ms, 1e-3)))):
-        launch()
-    time.sleep(seconds * 0.4)
-    try:
-        r = subprocess.run([exe, "metric", "-g", "0", "-c", "-p", "--json"], capture_output=True,
-                           text=True, timeout=30)
+    th = threading.Thread(target=sample)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds or th.is_alive():
+        for _ in range(20):
+            launch()
         torch.cuda.synchronize()
-        d = json.loads(r.stdout)
+    th.join()
+    try:
+        if "err" in out:
+            raise out["err"]
+        d = json.loads(out["r"].stdout)
         g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
         clk = g["clock"]
         gfx = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")
@@ -425,10 +441,9 @@ def clock_power(launch, kernel_ms: float, seconds: float = 1.5):
                 "gfx_mhz_median": float(np.median(gfx)) if gfx else None,
                 "max_gfx_mhz": next((clk[k]["max_clk"]["value"] for k in sorted(clk)
                                      if k.startswith("gfx_")), None),
-                "sampled": "amd-smi metric -c -p, %.1f s into %.1f s of back-to-back launches"
-                           % (seconds * 0.4, seconds)}
+                "sampled": "amd-smi metric -c -p, %.2f s into %.1f s of back-to-back launches"
+                           % (seconds * 0.5, seconds)}
     except Exception as exc:   # the tool's output format is not ours to rely on
-        torch.cuda.synchronize()
         return {"error": f"{type(exc).__name__}: {exc}"[:200]}
 
 
@@ -581,7 +596,9 @@ def main():
         torch.cuda.empty_cache()
         # the clock the attention kernel runs at, and the power it draws
         context["clock_power_under_attention"] = clock_power(
-            lambda: b.layer.attend_tokens(b.cfg.sm_scale, b.out, with_lse=True), attn_ms)
+            lambda: b.layer.attend_tokens(b.cfg.sm_scale, b.out, with_lse=True))
+        context["clock_power_under_map"] = clock_power(
+            lambda: b.layer.maxpool_map(b.q_tiles, b.cfg.sm_scale, b.map_lse, b.map_out))
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1024 * 1024 // 4
