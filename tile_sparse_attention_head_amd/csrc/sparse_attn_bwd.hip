@@ -138,22 +138,21 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* t
   return base + incl - v;
 }
 
-// per key tile: how many (query tile, occurrence) pairs keep it.  One thread
-// per CSR row adds its in-range entries with integer atomics (the counts do
-// not depend on the order of the additions); cnt starts at zero.  Entries
-// past `cap` (the CSR's entry count) are not read.
-__global__ __launch_bounds__(kThreads) void csrt_count_kernel(DevLayout L,
-                                                              const int32_t* __restrict__ rp,
-                                                              const int32_t* __restrict__ ci,
-                                                              int32_t cap,
-                                                              int32_t* __restrict__ cnt) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= L.tile_off[L.heads]) return;
+// per key tile: how many (query tile, occurrence) pairs keep it.  One wave
+// per CSR row, one lane per entry, adds the row's in-range entries with
+// integer atomics (the counts do not depend on the order of the additions);
+// cnt starts at zero.  Entries past `cap` (the CSR's entry count) are not
+// read.
+__global__ __launch_bounds__(64) void csrt_count_kernel(DevLayout L,
+                                                        const int32_t* __restrict__ rp,
+                                                        const int32_t* __restrict__ ci,
+                                                        int32_t cap, int32_t* __restrict__ cnt) {
+  const int64_t i = blockIdx.x;
   const int h = head_of_tile(L, i);
   const int64_t off = L.tile_off[h];
   const int n = (int)(L.tile_off[h + 1] - off);
   const int b = max(rp[i], 0), e = min(rp[i + 1], cap);
-  for (int p = b; p < e; ++p) {
+  for (int p = b + (int)threadIdx.x; p < e; p += 64) {
     const int j = ci[p];
     if (j >= 0 && j < n) atomicAdd(&cnt[off + j], 1);
   }
@@ -775,8 +774,8 @@ int launch_sparse_attn_bwd(const DevLayout& L, const void* q, const void* k, con
   hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L,
                      (const __bf16*)o, (const __bf16*)d_o, lse, sm_scale, w.delta, w.lse2,
                      w.seed_s, w.seed_dp, (__bf16*)w.dop, w.cnt);
-  hipLaunchKernelGGL(csrt_count_kernel, dim3((unsigned)((tiles + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, L, row_ptr, col_idx, (int32_t)nnz, w.cnt);
+  hipLaunchKernelGGL(csrt_count_kernel, dim3((unsigned)tiles), dim3(64), 0, s, L, row_ptr,
+                     col_idx, (int32_t)nnz, w.cnt);
   hipLaunchKernelGGL(csrt_scan_kernel, dim3(1), dim3(kThreads), 0, s, tiles, w.cnt, w.colt_ptr,
                      w.order);
   hipLaunchKernelGGL(csrt_fill_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L, row_ptr,
