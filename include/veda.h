@@ -225,7 +225,8 @@ int veda_sparse_attn_fwd_tokens(const veda_layout* L, const void* q_perm, const 
  *              are skipped.  nnz = row_ptr[tile_off[num_heads]] (host value)
  *  workspace   at least veda_sparse_attn_bwd_workspace(L, nnz) bytes,
  *              16-byte aligned; holds the gathered operands, D and the
- *              transposed CSR; contents unspecified on entry and exit
+ *              accumulator seeds, the transposed CSR and the order the key
+ *              tiles are processed in; contents unspecified on entry and exit
  *  dq, dk, dv  bf16 token order (outputs): every element is written; a key
  *              tile no row keeps gets dK = dV = 0, an empty row dQ = 0; must
  *              not overlap the inputs
