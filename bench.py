@@ -29,7 +29,9 @@ TFLOP/s: the matrix work the tile kernels compute (4*S^2*d per kept
 (query tile, key tile) pair of the attention, plus 2*S^2*d per (subset query
 tile, key tile) pair of the map -- its one Q K^T product; the second pass
 reads the row maxima the first one stored) divided by the step time.
-``roofline`` is for the stage that takes the longest (the dominant kernel);
+``roofline`` is for the stage that takes the longest (the dominant kernel;
+with the context runs it also carries the clock measured under that kernel
+and its fraction of the peak at that clock);
 ``kernels`` gives the same record for every stage: matrix-bound kernels in
 TFLOP/s against the bf16 peak, data-movement kernels in GB/s of algorithmic
 bytes against the HBM peak, with ``traffic`` the HBM bytes per launch read
@@ -604,6 +606,13 @@ def main():
             lambda: b.layer.attend_tokens(b.cfg.sm_scale, b.out, with_lse=True))
         context["clock_power_under_map"] = clock_power(
             lambda: b.layer.maxpool_map(b.q_tiles, b.cfg.sm_scale, b.map_lse, b.map_out))
+        # the attention kernel's fraction of the MFMA peak at the clock the
+        # power limit leaves it (the published peak assumes 2.4 GHz)
+        cp = context["clock_power_under_attention"]
+        if roofline.get("unit") == "TFLOP/s" and isinstance(cp, dict) and cp.get("gfx_mhz_median"):
+            roofline["measured_clock_mhz"] = cp["gfx_mhz_median"]
+            roofline["frac_at_measured_clock"] = (
+                roofline["achieved"] / (roofline["peak"] * cp["gfx_mhz_median"] / 2400.0))
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1024 * 1024 // 4
