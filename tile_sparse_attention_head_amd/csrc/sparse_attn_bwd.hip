@@ -167,8 +167,8 @@ __global__ __launch_bounds__(64) void csrt_count_kernel(DevLayout L,
 // XCDs by the hardware.  (Sorting within each XCD's contiguous range
 // instead, which keeps neighbouring key tiles on one L2, measured slower.)
 // Each key tile's gradients are computed by one workgroup whatever the
-// order, so the order changes the time only, never a result.  Run by one workgroup;
-// `segs` contiguous ranges are sorted separately (1: the grid).
+// order, so the order changes the time only, never a result.  Run by one
+// workgroup; `segs` contiguous ranges are sorted separately (1: the grid).
 constexpr int kOrderBuckets = 64;
 __device__ void csrt_order(int64_t tiles, int segs, const int32_t* __restrict__ cnt,
                            int32_t* __restrict__ order) {
