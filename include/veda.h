@@ -241,8 +241,23 @@ int veda_sparse_attn_bwd(const veda_layout* L, const void* q, const void* k, con
                          float sm_scale, void* workspace, int64_t workspace_bytes, void* dq,
                          void* dk, void* dv, void* stream);
 
-/* Workspace bytes veda_sparse_attn_bwd needs for a CSR of nnz entries.
- * Host-only.  bytes (host) output. */
+/* veda_sparse_attn_bwd with Q and K already in tile order, as the forward's
+ * gathers left them (veda_tile_permute_pool / veda_tile_permute FWD): their
+ * two gathers are skipped.  Same results, bit for bit, as
+ * veda_sparse_attn_bwd on the token-order tensors they were gathered from.
+ *  q_perm, k_perm  bf16 [tile_off[num_heads]*S][head_dim], tile order,
+ *              zero padding slots
+ *  workspace   at least veda_sparse_attn_bwd_workspace(L, nnz) bytes
+ * Every other argument, result and limit as veda_sparse_attn_bwd (dq, dk, dv
+ * must not overlap q_perm or k_perm either). */
+int veda_sparse_attn_bwd_tiles(const veda_layout* L, const void* q_perm, const void* k_perm,
+                               const void* v, const void* o, const void* d_o, const float* lse,
+                               const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                               float sm_scale, void* workspace, int64_t workspace_bytes,
+                               void* dq, void* dk, void* dv, void* stream);
+
+/* Workspace bytes veda_sparse_attn_bwd and veda_sparse_attn_bwd_tiles need
+ * for a CSR of nnz entries.  Host-only.  bytes (host) output. */
 int veda_sparse_attn_bwd_workspace(const veda_layout* L, int64_t nnz, int64_t* bytes);
 
 /* Max-pooled attention map, the distillation target (Veda §2.1 target

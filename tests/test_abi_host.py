@@ -258,3 +258,69 @@ def test_product_path_does_not_touch_the_oracle(repo_root):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "tile_sparse_attention_head_amd" not in src, f
                 assert not re.search(r"^\s*(import|from)\s+workloads\b", src, re.M), f
+
+
+@pytest.mark.parametrize("entry", ["veda_sparse_attn_bwd", "veda_sparse_attn_bwd_tiles"])
+def test_backward_rejections_and_workspace(lib, entry):
+    """Both backward entry points validate every argument before any launch
+    (the fake addresses are never dereferenced)."""
+    L = _layout()
+    Lp = ctypes.byref(L)
+    fake = 1 << 20
+    ws = ctypes.c_int64(0)
+    assert lib.veda_sparse_attn_bwd_workspace(Lp, 100, ctypes.byref(ws)) == 0
+    need = ws.value
+    tile_bytes = L.total_tiles * L.tile_size * L.head_dim * 2
+    assert need >= 4 * tile_bytes      # gathered Q, K, V and dO at least
+    assert lib.veda_sparse_attn_bwd_workspace(Lp, -1, ctypes.byref(ws)) == -1
+    assert lib.veda_sparse_attn_bwd_workspace(Lp, 100, None) == -1
+    B = getattr(lib, entry)
+    span = 1 << 32                      # far apart: no two fake buffers overlap
+    ok = dict(q=fake, k=fake + span, v=fake + 2 * span, o=fake + 3 * span, do=fake + 4 * span,
+              lse=fake, rp=fake, ci=fake, nnz=100, sc=0.1, ws=fake, wsb=need,
+              dq=fake + 5 * span, dk=fake + 6 * span, dv=fake + 7 * span)
+
+    def call(layout=Lp, **kw):
+        a = dict(ok, **kw)
+        return B(layout, a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["rp"], a["ci"],
+                 a["nnz"], a["sc"], a["ws"], a["wsb"], a["dq"], a["dk"], a["dv"], None)
+
+    for name in ("q", "k", "v", "o", "do", "lse", "rp", "ci", "ws", "dq", "dk", "dv"):
+        assert call(**{name: None}) == -1, name
+    assert call(nnz=-1) == -1
+    for bad in (float("nan"), 0.0, -0.1, float("inf")):
+        assert call(sc=bad) == -1
+    assert call(wsb=need - 1) == -1
+    assert call(q=fake + 8) == -2
+    assert call(dv=fake + 7 * span + 8) == -2
+    assert call(dq=fake + 4096) == -1                 # output over an input
+    assert call(dk=fake + 5 * span + 64) == -1        # outputs over each other
+    L3 = V.veda_layout_init(5, 9, 20, 96, 128, [(8, 4, 4)])
+    assert call(layout=ctypes.byref(L3)) == -2
+    L2 = _layout()
+    L2.tile_off[1] += 1
+    assert call(layout=ctypes.byref(L2)) == -1
+
+
+def test_head_sq_error_rejections_and_workspace(lib):
+    L = _layout()
+    Lp = ctypes.byref(L)
+    fake = 1 << 20
+    span = 1 << 32
+    ws = ctypes.c_int64(0)
+    assert lib.veda_head_sq_error_workspace(Lp, ctypes.byref(ws)) == 0
+    need = ws.value
+    assert need > 0
+    assert lib.veda_head_sq_error_workspace(Lp, None) == -1
+    E = lib.veda_head_sq_error
+    assert E(Lp, None, fake + span, fake, None, fake, need, None) == -1
+    assert E(Lp, fake, None, fake, None, fake, need, None) == -1
+    assert E(Lp, fake, fake + span, None, None, fake, need, None) == -1
+    assert E(Lp, fake, fake + span, fake, None, None, need, None) == -1
+    assert E(Lp, fake, fake + span, fake, None, fake, need - 1, None) == -1
+    assert E(Lp, fake + 8, fake + span, fake, None, fake, need, None) == -2
+    assert E(Lp, fake, fake + span, fake, None, fake + 4, need, None) == -2
+    L6 = V.veda_layout_init(4, 8, 8, 100, 64, [(4, 4, 4)])   # head_dim/8 does not divide 256
+    ws6 = ctypes.c_int64(0)
+    assert lib.veda_head_sq_error_workspace(ctypes.byref(L6), ctypes.byref(ws6)) == 0
+    assert E(ctypes.byref(L6), fake, fake + span, fake, None, fake, ws6.value, None) == -2

@@ -207,3 +207,22 @@ def test_backward_large_heterogeneous_sampled():
         sci = np.array(sum(rows, []), dtype=np.int64)
         worst = max(worst, _check_head(r, h, do, grads, srp, sci, q_sel, k_sel))
     _say(f"  worst max-abs / max|ref| {worst:.3e}")
+
+
+@pytest.mark.parametrize("name,sparsity", [("ragged-small", 75), ("wan1.3b-480p-81f", 90)])
+def test_backward_tile_order_inputs_bit_identical(name, sparsity):
+    """veda_sparse_attn_bwd_tiles on the forward's tile-order Q and K gives
+    the same gradients, bit for bit, as veda_sparse_attn_bwd on the
+    token-order tensors."""
+    _say(f"backward tile-order inputs {name} {sparsity}%")
+    torch = need_gpu()
+    r = Run(name, sparsity=sparsity)
+    out = r.forward_fused()
+    rng = np.random.default_rng(23)
+    do = to_dev_bf16(bf16_round(rng.normal(size=(r.wl.q.shape[0], r.heads, r.d)).astype(np.float32)))
+    a = r.layer.backward(r.q, r.k, r.v, out, do, r.sm_scale, reuse_tiles=True)
+    a = [bf16_bits(t).copy() for t in a]
+    b = r.layer.backward(r.q, r.k, r.v, out, do, r.sm_scale, reuse_tiles=False)
+    torch.cuda.synchronize()
+    for x, t in zip(a, b):
+        assert np.array_equal(x, bf16_bits(t))

@@ -10,8 +10,8 @@ owns buffers and issues the calls in order (``layer``).
 from ._lib import (  # noqa: F401
     LIB_PATH, VEDA_BF16, VEDA_F32, VEDA_FWD, VEDA_FWD_T, VEDA_INV, VedaError, csr_nnz, lib,
     veda_distill_grad, veda_distill_grad_workspace, veda_head_sq_error,
-    veda_head_sq_error_workspace, veda_sparse_attn_bwd, veda_sparse_attn_bwd_workspace,
-    status_string, tiles_numel, tokens_numel, veda_keep_count, veda_layout, veda_layout_init,
+    veda_head_sq_error_workspace, veda_sparse_attn_bwd, veda_sparse_attn_bwd_tiles,
+    veda_sparse_attn_bwd_workspace, status_string, tiles_numel, tokens_numel, veda_keep_count, veda_layout, veda_layout_init,
     veda_oracle_maxpool_map, veda_oracle_maxpool_map_workspace, veda_select_tiles,
     veda_sparse_attn_fwd, veda_sparse_attn_fwd_tokens, veda_tile_permute, veda_tile_permute_pool,
     veda_tile_score, veda_tripool_score)

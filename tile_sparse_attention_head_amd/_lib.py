@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
         "veda_head_sq_error_workspace": (c_i32, [P, ctypes.POINTER(c_i64)]),
         "veda_sparse_attn_bwd": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
                                          c_f32, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]),
+        "veda_sparse_attn_bwd_tiles": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                               c_i64, c_f32, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]),
         "veda_sparse_attn_bwd_workspace": (c_i32, [P, c_i64, ctypes.POINTER(c_i64)]),
         "veda_status_string": (ctypes.c_char_p, [c_i32]),
         "veda_layout_sizeof": (c_i64, []),
@@ -424,3 +426,24 @@ def veda_sparse_attn_bwd(L: veda_layout, q, k, v, o, d_o, lse, row_ptr, col_idx,
     _check(lib().veda_sparse_attn_bwd(ctypes.byref(L), *ins, pl, prp, pci, int(nnz),
                                       float(sm_scale), pw, have, *outs, _stream(stream)),
            "veda_sparse_attn_bwd")
+
+
+def veda_sparse_attn_bwd_tiles(L: veda_layout, q_perm, k_perm, v, o, d_o, lse, row_ptr, col_idx,
+                               nnz: int, sm_scale: float, workspace, dq, dk, dv,
+                               stream=None) -> None:
+    """veda_sparse_attn_bwd with Q and K already in tile order (the forward's
+    gathers); the same results."""
+    torch = _torch()
+    bf = torch.bfloat16
+    n, nt = tokens_numel(L), tiles_numel(L)
+    ins = [_dev(q_perm, "q_perm", bf, nt), _dev(k_perm, "k_perm", bf, nt)]
+    ins += [_dev(t, name, bf, n) for t, name in ((v, "v"), (o, "o"), (d_o, "d_o"))]
+    pl = _dev(lse, "lse", torch.float32, L.total_tiles * L.tile_size)
+    prp = _dev(row_ptr, "row_ptr", torch.int32, L.total_tiles + 1)
+    pci = _dev(col_idx, "col_idx", torch.int32, int(nnz))
+    pw = _dev(workspace, "workspace", None, 0)
+    have = workspace.numel() * workspace.element_size()
+    outs = [_dev(t, name, bf, n) for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    _check(lib().veda_sparse_attn_bwd_tiles(ctypes.byref(L), *ins, pl, prp, pci, int(nnz),
+                                            float(sm_scale), pw, have, *outs, _stream(stream)),
+           "veda_sparse_attn_bwd_tiles")

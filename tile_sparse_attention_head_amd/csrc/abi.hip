@@ -148,6 +148,59 @@ int attn_args(const veda_layout* L, const void* q_perm, const void* k_perm, cons
   return VEDA_OK;
 }
 
+// Checks shared by the two backward entry points, plus the debug-mode CSR
+// validation (synchronous).  qk_bytes: the size of q and k as passed (token
+// or tile order).
+int bwd_args(const veda_layout* L, const void* q, const void* k, size_t qk_bytes, const void* v,
+             const void* o, const void* d_o, const float* lse, const int32_t* row_ptr,
+             const int32_t* col_idx, int64_t nnz, float sm_scale, void* workspace,
+             int64_t workspace_bytes, void* dq, void* dk, void* dv, void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || d_o == nullptr ||
+      lse == nullptr || row_ptr == nullptr || col_idx == nullptr || workspace == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return VEDA_ERR_INVALID_ARG;
+  if (nnz < 0 || nnz > INT32_MAX) return VEDA_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.f) || sm_scale == INFINITY) return VEDA_ERR_INVALID_ARG;
+  if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
+  for (const void* p : {q, k, v, o, d_o, (const void*)dq, (const void*)dk, (const void*)dv,
+                        (const void*)workspace})
+    if (!aligned16(p)) return VEDA_ERR_UNSUPPORTED;
+  const DevLayout dl = make_dev_layout(L);
+  if (workspace_bytes < attn_bwd_workspace_bytes(dl, nnz)) return VEDA_ERR_INVALID_ARG;
+  const size_t tok = (size_t)L->T * L->H * L->W * L->num_heads * L->head_dim * 2;
+  for (const void* out : {(const void*)dq, (const void*)dk, (const void*)dv}) {
+    for (const void* in : {v, o, d_o})
+      if (!disjoint(out, tok, in, tok)) return VEDA_ERR_INVALID_ARG;
+    for (const void* in : {q, k})
+      if (!disjoint(out, tok, in, qk_bytes)) return VEDA_ERR_INVALID_ARG;
+  }
+  if (!disjoint(dq, tok, dk, tok) || !disjoint(dq, tok, dv, tok) || !disjoint(dk, tok, dv, tok))
+    return VEDA_ERR_INVALID_ARG;
+  if (debug_sync()) {   // host-side CSR validation (synchronous, debug only)
+    const int64_t rows = L->tile_off[L->num_heads];
+    std::vector<int32_t> rp(rows + 1);
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return VEDA_ERR_LAUNCH;
+    if (hipMemcpy(rp.data(), row_ptr, (rows + 1) * sizeof(int32_t), hipMemcpyDeviceToHost) !=
+        hipSuccess)
+      return VEDA_ERR_LAUNCH;
+    if (rp[0] != 0 || rp[rows] != nnz) return VEDA_ERR_BAD_CSR;
+    for (int64_t r = 0; r < rows; ++r)
+      if (rp[r + 1] < rp[r]) return VEDA_ERR_BAD_CSR;
+    std::vector<int32_t> ci(nnz);
+    if (nnz > 0 && hipMemcpy(ci.data(), col_idx, nnz * sizeof(int32_t), hipMemcpyDeviceToHost) !=
+                       hipSuccess)
+      return VEDA_ERR_LAUNCH;
+    for (int h = 0; h < L->num_heads; ++h)
+      for (int64_t r = L->tile_off[h]; r < L->tile_off[h + 1]; ++r)
+        for (int32_t p = rp[r]; p < rp[r + 1]; ++p) {
+          if (ci[p] < 0 || ci[p] >= L->n_tiles[h]) return VEDA_ERR_BAD_CSR;
+          if (p > rp[r] && ci[p] < ci[p - 1]) return VEDA_ERR_BAD_CSR;
+        }
+  }
+  return VEDA_OK;
+}
+
 }  // namespace
 }  // namespace veda
 
@@ -297,53 +350,36 @@ int veda_sparse_attn_bwd_workspace(const veda_layout* L, int64_t nnz, int64_t* b
   return VEDA_OK;
 }
 
+
 int veda_sparse_attn_bwd(const veda_layout* L, const void* q, const void* k, const void* v,
                          const void* o, const void* d_o, const float* lse,
                          const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                          float sm_scale, void* workspace, int64_t workspace_bytes, void* dq,
                          void* dk, void* dv, void* stream) {
-  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || d_o == nullptr ||
-      lse == nullptr || row_ptr == nullptr || col_idx == nullptr || workspace == nullptr ||
-      dq == nullptr || dk == nullptr || dv == nullptr)
-    return VEDA_ERR_INVALID_ARG;
-  if (nnz < 0 || nnz > INT32_MAX) return VEDA_ERR_INVALID_ARG;
-  if (!(sm_scale > 0.f) || sm_scale == INFINITY) return VEDA_ERR_INVALID_ARG;
-  if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
-  for (const void* p : {q, k, v, o, d_o, (const void*)dq, (const void*)dk, (const void*)dv,
-                        (const void*)workspace})
-    if (!aligned16(p)) return VEDA_ERR_UNSUPPORTED;
-  const DevLayout dl = make_dev_layout(L);
-  if (workspace_bytes < attn_bwd_workspace_bytes(dl, nnz)) return VEDA_ERR_INVALID_ARG;
-  const size_t tok = (size_t)L->T * L->H * L->W * L->num_heads * L->head_dim * 2;
-  for (const void* out : {(const void*)dq, (const void*)dk, (const void*)dv})
-    for (const void* in : {q, k, v, o, d_o})
-      if (!disjoint(out, tok, in, tok)) return VEDA_ERR_INVALID_ARG;
-  if (!disjoint(dq, tok, dk, tok) || !disjoint(dq, tok, dv, tok) || !disjoint(dk, tok, dv, tok))
-    return VEDA_ERR_INVALID_ARG;
-  if (debug_sync()) {   // host-side CSR validation (synchronous, debug only)
-    const int64_t rows = L->tile_off[L->num_heads];
-    std::vector<int32_t> rp(rows + 1);
-    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return VEDA_ERR_LAUNCH;
-    if (hipMemcpy(rp.data(), row_ptr, (rows + 1) * sizeof(int32_t), hipMemcpyDeviceToHost) !=
-        hipSuccess)
-      return VEDA_ERR_LAUNCH;
-    if (rp[0] != 0 || rp[rows] != nnz) return VEDA_ERR_BAD_CSR;
-    for (int64_t r = 0; r < rows; ++r)
-      if (rp[r + 1] < rp[r]) return VEDA_ERR_BAD_CSR;
-    std::vector<int32_t> ci(nnz);
-    if (nnz > 0 && hipMemcpy(ci.data(), col_idx, nnz * sizeof(int32_t), hipMemcpyDeviceToHost) !=
-                       hipSuccess)
-      return VEDA_ERR_LAUNCH;
-    for (int h = 0; h < L->num_heads; ++h)
-      for (int64_t r = L->tile_off[h]; r < L->tile_off[h + 1]; ++r)
-        for (int32_t p = rp[r]; p < rp[r + 1]; ++p) {
-          if (ci[p] < 0 || ci[p] >= L->n_tiles[h]) return VEDA_ERR_BAD_CSR;
-          if (p > rp[r] && ci[p] < ci[p - 1]) return VEDA_ERR_BAD_CSR;
-        }
-  }
-  return finish(launch_sparse_attn_bwd(dl, q, k, v, o, d_o, lse, row_ptr, col_idx, nnz, sm_scale,
-                                       workspace, dq, dk, dv, (hipStream_t)stream),
+  const size_t tok = L ? (size_t)L->T * L->H * L->W * L->num_heads * L->head_dim * 2 : 0;
+  const int st = bwd_args(L, q, k, tok, v, o, d_o, lse, row_ptr, col_idx, nnz, sm_scale,
+                          workspace, workspace_bytes, dq, dk, dv, stream);
+  if (st != VEDA_OK) return st;
+  return finish(launch_sparse_attn_bwd(make_dev_layout(L), q, k, v, o, d_o, lse, row_ptr,
+                                       col_idx, nnz, sm_scale, workspace, dq, dk, dv, false,
+                                       (hipStream_t)stream),
+                stream);
+}
+
+int veda_sparse_attn_bwd_tiles(const veda_layout* L, const void* q_perm, const void* k_perm,
+                               const void* v, const void* o, const void* d_o, const float* lse,
+                               const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                               float sm_scale, void* workspace, int64_t workspace_bytes,
+                               void* dq, void* dk, void* dv, void* stream) {
+  const size_t tiles = L && layout_ok(L)
+                           ? (size_t)L->tile_off[L->num_heads] * L->tile_size * L->head_dim * 2
+                           : 0;
+  const int st = bwd_args(L, q_perm, k_perm, tiles, v, o, d_o, lse, row_ptr, col_idx, nnz,
+                          sm_scale, workspace, workspace_bytes, dq, dk, dv, stream);
+  if (st != VEDA_OK) return st;
+  return finish(launch_sparse_attn_bwd(make_dev_layout(L), q_perm, k_perm, v, o, d_o, lse,
+                                       row_ptr, col_idx, nnz, sm_scale, workspace, dq, dk, dv,
+                                       true, (hipStream_t)stream),
                 stream);
 }
 

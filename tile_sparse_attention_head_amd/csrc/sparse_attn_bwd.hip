@@ -762,15 +762,20 @@ int launch_sparse_attn_bwd(const DevLayout& L, const void* q, const void* k, con
                            const void* o, const void* d_o, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                            float sm_scale, void* workspace, void* dq, void* dk, void* dv,
-                           hipStream_t s) {
+                           bool qk_tiles, hipStream_t s) {
   const int64_t tiles = L.tile_off[L.heads];
   if (tiles == 0) return VEDA_OK;
   int64_t total = 0;
-  const BwdWs w = carve(L, nnz, workspace, &total);
-  const struct { const void* x; void* y; int dir; } perms[] = {
-      {q, w.qp, VEDA_FWD}, {k, w.kp, VEDA_FWD}, {v, w.vp, VEDA_FWD}};
-  for (const auto& p : perms)
-    if (launch_permute(L, VEDA_BF16, p.dir, p.x, p.y, s) != VEDA_OK) return VEDA_ERR_LAUNCH;
+  BwdWs w = carve(L, nnz, workspace, &total);
+  if (qk_tiles) {   // Q and K come in tile order (the forward's gathers)
+    w.qp = const_cast<void*>(q);
+    w.kp = const_cast<void*>(k);
+  } else {
+    if (launch_permute(L, VEDA_BF16, VEDA_FWD, q, w.qp, s) != VEDA_OK ||
+        launch_permute(L, VEDA_BF16, VEDA_FWD, k, w.kp, s) != VEDA_OK)
+      return VEDA_ERR_LAUNCH;
+  }
+  if (launch_permute(L, VEDA_BF16, VEDA_FWD, v, w.vp, s) != VEDA_OK) return VEDA_ERR_LAUNCH;
   hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, L,
                      (const __bf16*)o, (const __bf16*)d_o, lse, sm_scale, w.delta, w.lse2,
                      w.seed_s, w.seed_dp, (__bf16*)w.dop, w.cnt);

@@ -100,11 +100,12 @@ int launch_head_error(const DevLayout& L, const void* a, const void* b, double* 
 
 // Attention backward: workspace bytes for a CSR of nnz entries, and the launch.
 int64_t attn_bwd_workspace_bytes(const DevLayout& L, int64_t nnz);
+// qk_tiles: q and k are already in tile order (their gathers are skipped).
 int launch_sparse_attn_bwd(const DevLayout& L, const void* q, const void* k, const void* v,
                            const void* o, const void* d_o, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                            float sm_scale, void* workspace, void* dq, void* dk, void* dv,
-                           hipStream_t s);
+                           bool qk_tiles, hipStream_t s);
 
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? VEDA_OK : VEDA_ERR_LAUNCH;

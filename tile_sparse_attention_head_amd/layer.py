@@ -124,18 +124,27 @@ class TileSparseAttention:
         self.unpermute(out, stream)
         return out
 
-    def backward(self, q, k, v, out, d_out, sm_scale: float, grads=None, stream=None):
+    def backward(self, q, k, v, out, d_out, sm_scale: float, grads=None, stream=None,
+                 reuse_tiles: bool = True):
         """dQ, dK, dV (token order) of the last ``forward`` (its inputs q, k,
         v and output ``out``, its lse and CSR still in this layer) for the
-        output gradient ``d_out``."""
+        output gradient ``d_out``.  With ``reuse_tiles`` the tile-order Q and
+        K the forward gathered (still in this layer) are used instead of
+        gathering q and k again; the results are the same."""
         torch = self.torch
         if grads is None:
             grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         need = V.veda_sparse_attn_bwd_workspace(self.L, self.nnz)
         if getattr(self, "_bwd_ws", None) is None or self._bwd_ws.numel() < need:
             self._bwd_ws = torch.empty(max(16, need), dtype=torch.uint8, device=q.device)
-        V.veda_sparse_attn_bwd(self.L, q, k, v, out, d_out, self.lse, self.row_ptr, self.col_idx,
-                               self.nnz, sm_scale, self._bwd_ws, *grads, stream=stream)
+        if reuse_tiles:
+            V.veda_sparse_attn_bwd_tiles(self.L, self.q_perm, self.k_perm, v, out, d_out,
+                                         self.lse, self.row_ptr, self.col_idx, self.nnz,
+                                         sm_scale, self._bwd_ws, *grads, stream=stream)
+        else:
+            V.veda_sparse_attn_bwd(self.L, q, k, v, out, d_out, self.lse, self.row_ptr,
+                                   self.col_idx, self.nnz, sm_scale, self._bwd_ws, *grads,
+                                   stream=stream)
         return grads
 
     def maxpool_map(self, q_tiles, sm_scale: float, lse=None, out_map=None, stream=None):
