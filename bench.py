@@ -399,12 +399,14 @@ def sweep():
     return out
 
 
-def clock_power(launch, seconds: float = 1.5):
+def clock_power(launch, seconds: float = 3.0, samples: int = 3):
     """GPU clocks and socket power while `launch` (one kernel) runs back to
-    back for `seconds`: launches go out in batches of 20 (a synchronisation
-    after each keeps the queue short) while a thread runs `amd-smi` (a child
-    process) half way through.  None where amd-smi is missing; an error
-    record where its output cannot be read."""
+    back: launches go out in batches of 20 (a synchronisation after each
+    keeps the queue short) while a thread runs `amd-smi` (a child process)
+    `samples` times, the first 40 % of `seconds` in (its readings lag the
+    load by up to about a second); the launches go on until the last sample
+    is read.  Medians over the samples, and the samples.  None where amd-smi
+    is missing; an error record where its output cannot be read."""
     import shutil
     import subprocess
     import threading
@@ -412,15 +414,17 @@ def clock_power(launch, seconds: float = 1.5):
     exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
     if exe is None:
         return None
-    out = {}
+    outs, errs = [], []
 
     def sample():
-        time.sleep(seconds * 0.5)
-        try:
-            out["r"] = subprocess.run([exe, "metric", "-g", "0", "-c", "-p", "--json"],
-                                      capture_output=True, text=True, timeout=30)
-        except Exception as exc:
-            out["err"] = exc
+        time.sleep(seconds * 0.4)
+        for i in range(samples):
+            try:
+                outs.append(subprocess.run([exe, "metric", "-g", "0", "-c", "-p", "--json"],
+                                           capture_output=True, text=True, timeout=30).stdout)
+            except Exception as exc:
+                errs.append(exc)
+            time.sleep(seconds * 0.6 / samples)
 
     torch.cuda.synchronize()
     th = threading.Thread(target=sample)
@@ -432,19 +436,26 @@ def clock_power(launch, seconds: float = 1.5):
         torch.cuda.synchronize()
     th.join()
     try:
-        if "err" in out:
-            raise out["err"]
-        d = json.loads(out["r"].stdout)
-        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
-        clk = g["clock"]
-        gfx = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")
-               and isinstance(clk[k].get("clk"), dict)]
-        return {"socket_power_w": g["power"]["socket_power"]["value"], "gfx_mhz_per_xcd": gfx,
-                "gfx_mhz_median": float(np.median(gfx)) if gfx else None,
-                "max_gfx_mhz": next((clk[k]["max_clk"]["value"] for k in sorted(clk)
-                                     if k.startswith("gfx_")), None),
-                "sampled": "amd-smi metric -c -p, %.2f s into %.1f s of back-to-back launches"
-                           % (seconds * 0.5, seconds)}
+        if not outs:
+            raise errs[0] if errs else RuntimeError("no sample")
+        power, clocks = [], []
+        max_clk = None
+        for text in outs:
+            d = json.loads(text)
+            g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+            clk = g["clock"]
+            gfx = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")
+                   and isinstance(clk[k].get("clk"), dict)]
+            power.append(g["power"]["socket_power"]["value"])
+            clocks.append(float(np.median(gfx)) if gfx else None)
+            max_clk = max_clk or next((clk[k]["max_clk"]["value"] for k in sorted(clk)
+                                       if k.startswith("gfx_")), None)
+        return {"socket_power_w": float(np.median(power)),
+                "gfx_mhz_median": float(np.median([c for c in clocks if c is not None])),
+                "samples_power_w": power, "samples_gfx_mhz_median_over_xcds": clocks,
+                "max_gfx_mhz": max_clk,
+                "sampled": "amd-smi metric -c -p, %d samples from %.1f s into %.1f s of "
+                           "back-to-back launches" % (len(outs), seconds * 0.4, seconds)}
     except Exception as exc:   # the tool's output format is not ours to rely on
         return {"error": f"{type(exc).__name__}: {exc}"[:200]}
 
