@@ -27,6 +27,8 @@
  *  - Every argument is validated on the host before anything is enqueued.  An
  *    invalid argument returns a negative veda_status and enqueues nothing.
  *  - Calls keep no state between them and may be made from several threads.
+ *    No call enqueues a memset (the kernels clear their own counters), so a
+ *    sequence of calls can be captured in a HIP graph and replayed.
  *  - bf16 is the IEEE-754 binary32 high half (bfloat16); f32 is binary32.
  *
  * Token and tile order (the pages leave these open; the readings taken):
