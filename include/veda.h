@@ -55,6 +55,7 @@ extern "C" {
 #endif
 
 #define VEDA_MAX_HEADS 64
+#define VEDA_MAX_SUBSET (1 << 20) /* most query-tile subset entries of one map or distillation call */
 
 typedef enum veda_status {
   VEDA_OK = 0,
@@ -274,7 +275,8 @@ int veda_sparse_attn_bwd_workspace(const veda_layout* L, int64_t nnz, int64_t* b
  *  q_perm, k_perm  bf16, tile order
  *  sm_scale        finite and > 0 (else VEDA_ERR_INVALID_ARG)
  *  q_tiles         int32 [n_sub] global query-tile indices; an entry outside
- *                  [0, tile_off[num_heads]) gets a map row of zeros
+ *                  [0, tile_off[num_heads]) gets a map row of zeros;
+ *                  n_sub <= VEDA_MAX_SUBSET (else VEDA_ERR_UNSUPPORTED)
  *  workspace       device scratch of at least workspace_bytes >=
  *                  veda_oracle_maxpool_map_workspace(L, n_sub) bytes, 16-byte
  *                  aligned (smaller: VEDA_ERR_INVALID_ARG); owned by the
@@ -294,6 +296,7 @@ int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void
 /* Workspace bytes veda_oracle_maxpool_map needs for n_sub subset entries of
  * layout L (0 for n_sub = 0): n_sub*max_tiles*S*4 for the row maxima plus
  * n_sub*chunks*S*8 for per-chunk partial sums.  Host-only, no device work.
+ * n_sub above VEDA_MAX_SUBSET: VEDA_ERR_UNSUPPORTED.
  *  bytes  (host) output */
 int veda_oracle_maxpool_map_workspace(const veda_layout* L, int32_t n_sub, int64_t* bytes);
 
@@ -312,7 +315,8 @@ int veda_oracle_maxpool_map_workspace(const veda_layout* L, int32_t n_sub, int64
  *  map       f32 [n_sub][max_tiles]: veda_oracle_maxpool_map over the same
  *            q_tiles (a row whose map sums to 0 contributes nothing)
  *  q_tiles   int32 [n_sub] global query-tile indices; entries outside
- *            [0, tile_off[num_heads]) are ignored (and not counted in R)
+ *            [0, tile_off[num_heads]) are ignored (and not counted in R);
+ *            n_sub <= VEDA_MAX_SUBSET (else VEDA_ERR_UNSUPPORTED)
  *  desc      f32 [2][tile_off[num_heads]][3*head_dim] TripPool descriptors
  *  phi       f32 [2][tile_off[num_heads]][d_e] projections
  *  workspace device scratch of at least veda_distill_grad_workspace(L, n_sub,
@@ -328,7 +332,8 @@ int veda_distill_grad(const veda_layout* L, const float* scores, const float* ma
                       float* loss, float* grad_w_q, float* grad_w_k, float* grad_b_q,
                       float* grad_b_k, void* stream);
 
-/* Workspace bytes veda_distill_grad needs.  Host-only.
+/* Workspace bytes veda_distill_grad needs.  Host-only.  n_sub above
+ * VEDA_MAX_SUBSET: VEDA_ERR_UNSUPPORTED.
  *  bytes  (host) output */
 int veda_distill_grad_workspace(const veda_layout* L, int32_t n_sub, int32_t d_e,
                                 int64_t* bytes);

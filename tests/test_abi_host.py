@@ -183,6 +183,10 @@ def test_device_calls_reject_before_launch(lib):
     assert M(Lp, fake, fake, 0.1, fake, 3, None, big, fake, fake, None) == -1
     assert M(Lp, fake, fake, 0.1, fake, 3, fake, ws.value - 1, fake, fake, None) == -1
     assert M(Lp, fake, fake, 0.1, fake, 3, fake + 8, big, fake, fake, None) == -2
+    # more subset entries than VEDA_MAX_SUBSET (the launch grids' range)
+    assert M(Lp, fake, fake, 0.1, fake, (1 << 20) + 1, fake, big, fake, fake, None) == -2
+    assert lib.veda_oracle_maxpool_map_workspace(Lp, (1 << 20) + 1, ctypes.byref(ws)) == -2
+    assert lib.veda_oracle_maxpool_map_workspace(Lp, 1 << 20, ctypes.byref(ws)) == 0
 
 
 def test_distill_rejections_and_workspace(lib):
@@ -213,6 +217,8 @@ def test_distill_rejections_and_workspace(lib):
     assert call(ws=None) == -1
     assert call(wsb=need - 1) == -1
     assert call(ws=fake + 8) == -2
+    assert call(n=(1 << 20) + 1, wsb=1 << 46) == -2
+    assert lib.veda_distill_grad_workspace(Lp, (1 << 20) + 1, 128, ctypes.byref(ws)) == -2
     L3 = V.veda_layout_init(5, 9, 20, 96, 128, [(8, 4, 4)])
     ws3 = ctypes.c_int64(0)
     assert lib.veda_distill_grad_workspace(ctypes.byref(L3), 5, 128, ctypes.byref(ws3)) == 0

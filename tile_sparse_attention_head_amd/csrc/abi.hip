@@ -385,6 +385,7 @@ int veda_sparse_attn_bwd_tiles(const veda_layout* L, const void* q_perm, const v
 
 int veda_oracle_maxpool_map_workspace(const veda_layout* L, int32_t n_sub, int64_t* bytes) {
   if (L == nullptr || bytes == nullptr || !layout_ok(L) || n_sub < 0) return VEDA_ERR_INVALID_ARG;
+  if (n_sub > VEDA_MAX_SUBSET) return VEDA_ERR_UNSUPPORTED;
   *bytes = map_workspace_bytes(make_dev_layout(L), n_sub);
   return VEDA_OK;
 }
@@ -395,6 +396,7 @@ int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void
                             void* stream) {
   if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
   if (n_sub < 0) return VEDA_ERR_INVALID_ARG;
+  if (n_sub > VEDA_MAX_SUBSET) return VEDA_ERR_UNSUPPORTED;   // keeps both grids in range
   if (n_sub > 0 && (q_perm == nullptr || k_perm == nullptr || q_tiles == nullptr ||
                     lse == nullptr || map == nullptr || workspace == nullptr))
     return VEDA_ERR_INVALID_ARG;
@@ -413,6 +415,7 @@ int veda_distill_grad_workspace(const veda_layout* L, int32_t n_sub, int32_t d_e
                                 int64_t* bytes) {
   if (L == nullptr || bytes == nullptr || !layout_ok(L) || n_sub < 0 || d_e < 1)
     return VEDA_ERR_INVALID_ARG;
+  if (n_sub > VEDA_MAX_SUBSET) return VEDA_ERR_UNSUPPORTED;
   *bytes = distill_workspace_bytes(make_dev_layout(L), n_sub, d_e);
   return VEDA_OK;
 }
@@ -429,7 +432,7 @@ int veda_distill_grad(const veda_layout* L, const float* scores, const float* ma
     return VEDA_ERR_INVALID_ARG;
   if (n_sub > 0 && (scores == nullptr || map == nullptr || q_tiles == nullptr))
     return VEDA_ERR_INVALID_ARG;
-  if (d_e > 256) return VEDA_ERR_UNSUPPORTED;
+  if (d_e > 256 || n_sub > VEDA_MAX_SUBSET) return VEDA_ERR_UNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128) return VEDA_ERR_UNSUPPORTED;
   const DevLayout dl = make_dev_layout(L);
   if (workspace_bytes < distill_workspace_bytes(dl, n_sub, d_e)) return VEDA_ERR_INVALID_ARG;
