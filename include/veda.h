@@ -56,6 +56,14 @@ extern "C" {
 
 #define VEDA_MAX_HEADS 64
 #define VEDA_MAX_SUBSET (1 << 20) /* most query-tile subset entries of one map or distillation call */
+/* Most tiles one head may have in the calls that read K/V tiles through a
+ * buffer resource (attention forward and backward, the max-pooled map): a
+ * head's tile-order K or V must span at most 2^31 - 1 bytes, and the forward
+ * packs a tile index into 16 bits.  Larger: VEDA_ERR_UNSUPPORTED.
+ * veda_layout_init already keeps sum_h n_tiles[h]^2 (the CSR entry bound)
+ * within int32, so an accepted layout has at most 46340 tiles per head; the
+ * calls check this limit anyway. */
+#define VEDA_MAX_TILES_PER_HEAD 65535
 
 typedef enum veda_status {
   VEDA_OK = 0,
@@ -192,7 +200,8 @@ int veda_select_tiles(const veda_layout* L, const float* scores,
  *  sm_scale        finite and > 0 (else VEDA_ERR_INVALID_ARG)
  * A query row whose CSR row is empty gets O = 0 and lse = -inf.  Entries of
  * col_idx outside [0, n_tiles[hd]) are skipped.  Supported: (head_dim,
- * tile_size) in {(64,64), (128,128)}, 16-byte aligned tensors. */
+ * tile_size) in {(64,64), (128,128)}, 16-byte aligned tensors, max_tiles <=
+ * VEDA_MAX_TILES_PER_HEAD. */
 int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k_perm,
                          const void* vt_perm, const int32_t* row_ptr,
                          const int32_t* col_idx, float sm_scale, void* o_perm,
@@ -237,7 +246,8 @@ int veda_sparse_attn_fwd_tokens(const veda_layout* L, const void* q_perm, const 
  * is not sorted gives wrong gradients (never an out-of-bounds access); with
  * VEDA_DEBUG_SYNC=1 the CSR (monotone rows, in-range and ascending entries,
  * nnz) is checked and VEDA_ERR_BAD_CSR returned.  Supported: (head_dim,
- * tile_size) in {(64,64), (128,128)}, 16-byte aligned tensors. */
+ * tile_size) in {(64,64), (128,128)}, 16-byte aligned tensors, max_tiles <=
+ * VEDA_MAX_TILES_PER_HEAD. */
 int veda_sparse_attn_bwd(const veda_layout* L, const void* q, const void* k, const void* v,
                          const void* o, const void* d_o, const float* lse,
                          const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
@@ -260,7 +270,8 @@ int veda_sparse_attn_bwd_tiles(const veda_layout* L, const void* q_perm, const v
                                void* dq, void* dk, void* dv, void* stream);
 
 /* Workspace bytes veda_sparse_attn_bwd and veda_sparse_attn_bwd_tiles need
- * for a CSR of nnz entries.  Host-only.  bytes (host) output. */
+ * for a CSR of nnz entries.  Host-only.  bytes (host) output.  max_tiles
+ * above VEDA_MAX_TILES_PER_HEAD: VEDA_ERR_UNSUPPORTED. */
 int veda_sparse_attn_bwd_workspace(const veda_layout* L, int64_t nnz, int64_t* bytes);
 
 /* Max-pooled attention map, the distillation target (Veda §2.1 target
@@ -287,7 +298,8 @@ int veda_sparse_attn_bwd_workspace(const veda_layout* L, int64_t nnz, int64_t* b
  *  map             f32 [n_sub][max_tiles] (output)
  * Pass 1 also records, per query row and key tile, the largest logit, so
  * pass 2 reads n_sub*max_tiles*S floats instead of recomputing Q K^T.
- * Supported: (head_dim, tile_size) in {(64,64), (128,128)}. */
+ * Supported: (head_dim, tile_size) in {(64,64), (128,128)}, max_tiles <=
+ * VEDA_MAX_TILES_PER_HEAD. */
 int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void* k_perm,
                             float sm_scale, const int32_t* q_tiles, int32_t n_sub,
                             void* workspace, int64_t workspace_bytes, float* lse,
@@ -296,7 +308,8 @@ int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void
 /* Workspace bytes veda_oracle_maxpool_map needs for n_sub subset entries of
  * layout L (0 for n_sub = 0): n_sub*max_tiles*S*4 for the row maxima plus
  * n_sub*chunks*S*8 for per-chunk partial sums.  Host-only, no device work.
- * n_sub above VEDA_MAX_SUBSET: VEDA_ERR_UNSUPPORTED.
+ * n_sub above VEDA_MAX_SUBSET or max_tiles above VEDA_MAX_TILES_PER_HEAD:
+ * VEDA_ERR_UNSUPPORTED.
  *  bytes  (host) output */
 int veda_oracle_maxpool_map_workspace(const veda_layout* L, int32_t n_sub, int64_t* bytes);
 

@@ -40,15 +40,67 @@ def host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+_WL_CACHE = {}
+
+
+def cached_workload(name: str, seed: int = 0, T: int = None):
+    """workloads.make with the last full-size draw kept, so that tests of one
+    large layer at several sparsities draw its inputs once (one entry is kept,
+    which bounds host memory)."""
+    key = (name, seed, T)
+    if key not in _WL_CACHE:
+        _WL_CACHE.clear()
+        _WL_CACHE[key] = workloads.make(name, seed, T=T)
+    return _WL_CACHE[key]
+
+
+def check_attention(r, q_tiles_per_head, o_tok=None, att_max=2e-2, att_mean=2e-3, lse_tol=1e-4,
+                    say=None):
+    """GPU attention against oracle.sparse_attention on the GPU's own CSR, for
+    the query tiles ``q_tiles_per_head[h]`` of every head (None: all).  With
+    ``o_tok`` (the token-order output of the fused call) each query slot is
+    compared at its token's row; otherwise the tile-order o_perm is read.
+    lse (tile-slot order) is read from the layer.  Returns (worst max-abs,
+    mean of the per-head mean-abs, largest kept-row length seen)."""
+    L = r.L
+    o = None if o_tok is not None else bf16_f64(r.layer.o_perm).reshape(-1, r.d)
+    ot = None if o_tok is None else bf16_f64(o_tok)
+    lse = host(r.layer.lse)
+    worst, means, longest = 0.0, [], 0
+    for h in range(r.heads):
+        ht = r.tilings[h]
+        qp, kp, vp = r.head_perm(h)
+        rp, ci = r.csr_head(h)
+        tiles = None if q_tiles_per_head is None else q_tiles_per_head[h]
+        for i in (range(ht.n) if tiles is None else tiles):
+            longest = max(longest, int(rp[i + 1] - rp[i]))
+        ro, rl = oracle.sparse_attention(qp, kp, vp, ht.valid, r.S, rp, ci, r.sm_scale,
+                                         q_tiles=tiles)
+        sel = ~np.isnan(rl)
+        if ot is None:
+            go = o[r.rows(h)][sel]
+        else:
+            go = ot[ht.perm[sel], h, :]            # slot -> its token's row of head h
+        err = np.abs(go - ro[sel])
+        worst = max(worst, float(err.max()))
+        means.append(float(err.mean()))
+        assert err.max() <= att_max, (h, err.max())
+        assert err.mean() <= att_mean, (h, err.mean())
+        assert np.abs(lse[r.rows(h)][sel] - rl[sel]).max() <= lse_tol, h
+        if say is not None:
+            say(f"  head {h} {ht.shape}: max-abs {err.max():.2e}")
+    return worst, float(np.mean(means)), longest
+
+
 class Run:
     """A workload on the GPU plus its oracle-side view."""
 
     def __init__(self, name: str, seed: int = 0, sparsity: int = None, T: int = None,
-                 k_per_head=None):
+                 k_per_head=None, cache: bool = False):
         torch = need_gpu()
         import tile_sparse_attention_head_amd as V
         self.V = V
-        self.wl = workloads.make(name, seed, T=T)
+        self.wl = cached_workload(name, seed, T) if cache else workloads.make(name, seed, T=T)
         cfg = self.wl.config
         self.cfg = cfg
         self.T, self.H, self.W = self.wl.T, cfg.H, cfg.W

@@ -330,3 +330,29 @@ def test_head_sq_error_rejections_and_workspace(lib):
     ws6 = ctypes.c_int64(0)
     assert lib.veda_head_sq_error_workspace(ctypes.byref(L6), ctypes.byref(ws6)) == 0
     assert E(ctypes.byref(L6), fake, fake + span, fake, None, fake, ws6.value, None) == -2
+
+
+def test_tiles_per_head_limit(lib):
+    """The attention, backward and map calls read a head's K/V tiles through
+    a 32-bit buffer range and the forward packs tile indices into 16 bits
+    (VEDA_MAX_TILES_PER_HEAD = 65535).  veda_layout_init's own bound (sum of
+    n_h^2 within int32) stops at 46340 tiles per head, so the largest layout
+    it accepts passes the calls' check and the next one is refused by the
+    layout itself; a layout whose max_tiles was raised by hand is refused as
+    tampered."""
+    text = open(HEADER).read()
+    assert re.search(r"#define VEDA_MAX_TILES_PER_HEAD 65535\b", text)
+    # one head of (1,1,128) tiles over a T x 1 x 128 grid: n = T tiles
+    ok = V.veda_layout_init(46340, 1, 128, 128, 128, [(1, 1, 128)])
+    assert ok.max_tiles == 46340
+    with pytest.raises(Exception):
+        V.veda_layout_init(46341, 1, 128, 128, 128, [(1, 1, 128)])
+    ws = ctypes.c_int64(0)
+    assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(ok), 4, ctypes.byref(ws)) == 0
+    assert lib.veda_sparse_attn_bwd_workspace(ctypes.byref(ok), 100, ctypes.byref(ws)) == 0
+    bad = V.veda_layout_init(46340, 1, 128, 128, 128, [(1, 1, 128)])
+    bad.max_tiles = 70000
+    fake = 1 << 20
+    assert lib.veda_sparse_attn_fwd(ctypes.byref(bad), fake, fake, fake, fake, fake, 0.1, fake,
+                                    None, None) == -1
+    assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(bad), 4, ctypes.byref(ws)) == -1

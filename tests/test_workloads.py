@@ -50,3 +50,22 @@ def test_subset_draw():
     assert all(np.all(np.diff(s) > 0) for s in sub)
     again = workloads.draw_subset(wl, [20, 7, 1])
     assert all(np.array_equal(x, y) for x, y in zip(sub, again))
+
+
+def test_bf16_round_matches_exact_integer_rounding():
+    """The uint32 form gives the same bits as the rounding done in exact
+    (Python integer) arithmetic, over random values, both signs of zero,
+    infinities, NaN payloads near the top of the range, halfway cases, and a
+    chunked (multi-threaded) size."""
+    rng = np.random.default_rng(11)
+    special = np.array([0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000,
+                        0xFFFFFFFF, 0xFFFF8000, 0x7FFF8000, 0x3F808000, 0x3F818000,
+                        0x7F7FFFFF, 0xFF7FFFFF, 0x00008000, 0x00018000], dtype=np.uint32)
+    bits = np.concatenate([special, rng.integers(0, 2 ** 32, size=5000, dtype=np.uint32)])
+    want = np.array([((int(v) + 0x7FFF + ((int(v) >> 16) & 1)) >> 16) & 0xFFFF for v in bits],
+                    dtype=np.uint16)
+    assert np.array_equal(bf16_round(bits.view(np.float32)), want)
+    big = rng.standard_normal(3 * (1 << 22) + 17, dtype=np.float32)
+    b64 = big.view(np.uint32).astype(np.uint64)
+    ref = ((b64 + 0x7FFF + ((b64 >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(bf16_round(big), ref)

@@ -114,6 +114,13 @@ bool attn_shape_ok(const veda_layout* L) {
   return (L->head_dim == 128 && L->tile_size == 128) || (L->head_dim == 64 && L->tile_size == 64);
 }
 
+// The K/V tiles of one head are read through a buffer resource whose range
+// is a 32-bit byte count, and the forward packs a tile index into 16 bits.
+bool tiles_per_head_ok(const veda_layout* L) {
+  return L->max_tiles <= VEDA_MAX_TILES_PER_HEAD &&
+         (int64_t)L->max_tiles * L->tile_size * L->head_dim * 2 <= INT32_MAX;
+}
+
 // Checks shared by the two attention entry points, plus the debug-mode CSR
 // validation (synchronous).
 int attn_args(const veda_layout* L, const void* q_perm, const void* k_perm, const void* vt_perm,
@@ -124,7 +131,7 @@ int attn_args(const veda_layout* L, const void* q_perm, const void* k_perm, cons
       col_idx == nullptr || o == nullptr)
     return VEDA_ERR_INVALID_ARG;
   if (!(sm_scale > 0.f) || sm_scale == INFINITY) return VEDA_ERR_INVALID_ARG;
-  if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
+  if (!attn_shape_ok(L) || !tiles_per_head_ok(L)) return VEDA_ERR_UNSUPPORTED;
   if (!aligned16(q_perm) || !aligned16(k_perm) || !aligned16(vt_perm) || !aligned16(o))
     return VEDA_ERR_UNSUPPORTED;
   if (debug_sync()) {
@@ -162,7 +169,7 @@ int bwd_args(const veda_layout* L, const void* q, const void* k, size_t qk_bytes
     return VEDA_ERR_INVALID_ARG;
   if (nnz < 0 || nnz > INT32_MAX) return VEDA_ERR_INVALID_ARG;
   if (!(sm_scale > 0.f) || sm_scale == INFINITY) return VEDA_ERR_INVALID_ARG;
-  if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
+  if (!attn_shape_ok(L) || !tiles_per_head_ok(L)) return VEDA_ERR_UNSUPPORTED;
   for (const void* p : {q, k, v, o, d_o, (const void*)dq, (const void*)dk, (const void*)dv,
                         (const void*)workspace})
     if (!aligned16(p)) return VEDA_ERR_UNSUPPORTED;
@@ -346,6 +353,7 @@ int veda_sparse_attn_fwd_tokens(const veda_layout* L, const void* q_perm, const 
 int veda_sparse_attn_bwd_workspace(const veda_layout* L, int64_t nnz, int64_t* bytes) {
   if (L == nullptr || bytes == nullptr || !layout_ok(L) || nnz < 0 || nnz > INT32_MAX)
     return VEDA_ERR_INVALID_ARG;
+  if (!tiles_per_head_ok(L)) return VEDA_ERR_UNSUPPORTED;
   *bytes = attn_bwd_workspace_bytes(make_dev_layout(L), nnz);
   return VEDA_OK;
 }
@@ -385,7 +393,7 @@ int veda_sparse_attn_bwd_tiles(const veda_layout* L, const void* q_perm, const v
 
 int veda_oracle_maxpool_map_workspace(const veda_layout* L, int32_t n_sub, int64_t* bytes) {
   if (L == nullptr || bytes == nullptr || !layout_ok(L) || n_sub < 0) return VEDA_ERR_INVALID_ARG;
-  if (n_sub > VEDA_MAX_SUBSET) return VEDA_ERR_UNSUPPORTED;
+  if (n_sub > VEDA_MAX_SUBSET || !tiles_per_head_ok(L)) return VEDA_ERR_UNSUPPORTED;
   *bytes = map_workspace_bytes(make_dev_layout(L), n_sub);
   return VEDA_OK;
 }
@@ -401,7 +409,7 @@ int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void
                     lse == nullptr || map == nullptr || workspace == nullptr))
     return VEDA_ERR_INVALID_ARG;
   if (!(sm_scale > 0.f) || sm_scale == INFINITY) return VEDA_ERR_INVALID_ARG;
-  if (!attn_shape_ok(L)) return VEDA_ERR_UNSUPPORTED;
+  if (!attn_shape_ok(L) || !tiles_per_head_ok(L)) return VEDA_ERR_UNSUPPORTED;
   const DevLayout dl = make_dev_layout(L);
   if (n_sub > 0 && workspace_bytes < map_workspace_bytes(dl, n_sub)) return VEDA_ERR_INVALID_ARG;
   if (n_sub > 0 && (!aligned16(q_perm) || !aligned16(k_perm) || !aligned16(workspace)))

@@ -35,6 +35,7 @@ changing the token count (length sweep) keeps the per-head tile draw.
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence, Tuple
 
@@ -152,11 +153,33 @@ class Workload:
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bit pattern (uint16), round to nearest, ties to even."""
+    """fp32 -> bf16 bit pattern (uint16), round to nearest, ties to even:
+    bits 16..31 of ``b + 0x7FFF + bit16(b)`` for the fp32 bit pattern ``b``.
+    The sum is formed in uint32; it wraps past 2^32 only for NaN patterns,
+    and the wrap changes no bit below 32, so the kept half is the same as in
+    exact arithmetic.  Large arrays are done in chunks on a few threads (numpy
+    releases the GIL in these operations)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return b.astype(np.uint16)
+    b = x.reshape(-1).view(np.uint32)
+    out = np.empty(b.size, dtype=np.uint16)
+
+    def part(lo: int, hi: int) -> None:
+        src = b[lo:hi]
+        t = src >> 16
+        t &= 1
+        t += 0x7FFF
+        t += src
+        t >>= 16
+        out[lo:hi] = t
+
+    chunk = 1 << 22
+    if b.size <= chunk:
+        part(0, b.size)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            list(ex.map(lambda lo: part(lo, min(lo + chunk, b.size)), range(0, b.size, chunk)))
+    return out.reshape(x.shape)
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
