@@ -345,6 +345,28 @@ int veda_distill_grad(const veda_layout* L, const float* scores, const float* ma
                       float* loss, float* grad_w_q, float* grad_w_k, float* grad_b_q,
                       float* grad_b_k, void* stream);
 
+/* veda_distill_grad with no workspace argument and no allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight training or serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is a static device array inside the library, one per GPU,
+ * VEDA_DISTILL_STATIC_SCRATCH_BYTES bytes, held until the process ends; its
+ * address on a device is looked up (hipGetSymbolAddress) on the first call
+ * made with that device current, and `stream` must belong to the current
+ * device.  The call allocates nothing and calls no allocating routine.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (the kernels write every element they read): calls that overlap in
+ * time on one GPU -- on different streams, or from different threads --
+ * race, so order them on one stream.  A problem whose
+ * veda_distill_grad_workspace(L, n_sub, d_e) exceeds
+ * VEDA_DISTILL_STATIC_SCRATCH_BYTES returns VEDA_ERR_UNSUPPORTED before any
+ * device work; a failing address lookup returns VEDA_ERR_LAUNCH.  Every other
+ * argument, result and limit as veda_distill_grad, bit for bit. */
+#define VEDA_DISTILL_STATIC_SCRATCH_BYTES (64ll << 20)
+int veda_distill_grad_noalloc(const veda_layout* L, const float* scores, const float* map,
+                              const int32_t* q_tiles, int32_t n_sub, const float* desc,
+                              const float* phi, int32_t d_e, float* loss, float* grad_w_q,
+                              float* grad_w_k, float* grad_b_q, float* grad_b_k, void* stream);
+
 /* Workspace bytes veda_distill_grad needs.  Host-only.  n_sub above
  * VEDA_MAX_SUBSET: VEDA_ERR_UNSUPPORTED.
  *  bytes  (host) output */

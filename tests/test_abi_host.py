@@ -356,3 +356,46 @@ def test_tiles_per_head_limit(lib):
     assert lib.veda_sparse_attn_fwd(ctypes.byref(bad), fake, fake, fake, fake, fake, 0.1, fake,
                                     None, None) == -1
     assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(bad), 4, ctypes.byref(ws)) == -1
+
+
+def test_distill_noalloc_rejections(lib):
+    """The static-scratch distillation call validates like veda_distill_grad
+    and refuses, before any device work, a problem whose workspace would not
+    fit the library's scratch (VEDA_DISTILL_STATIC_SCRATCH_BYTES)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define VEDA_DISTILL_STATIC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", text)
+    assert m
+    cap = int(m.group(1)) << int(m.group(2))
+    L = _layout()
+    Lp = ctypes.byref(L)
+    fake = 1 << 20
+    N = lib.veda_distill_grad_noalloc
+    ok = dict(sc=fake, mp=fake, qt=fake, n=5, desc=fake, phi=fake, de=128, loss=fake, gq=fake,
+              gk=fake)
+
+    def call(layout=Lp, **kw):
+        a = dict(ok, **kw)
+        return N(layout, a["sc"], a["mp"], a["qt"], a["n"], a["desc"], a["phi"], a["de"],
+                 a["loss"], a["gq"], a["gk"], None, None, None)
+
+    assert call(n=-1) == -1
+    assert call(de=0) == -1
+    assert call(de=300) == -2
+    for name in ("desc", "phi", "loss", "gq", "gk", "mp", "sc", "qt"):
+        assert call(**{name: None}) == -1, name
+    assert call(n=(1 << 20) + 1) == -2
+    L2 = _layout()
+    L2.tile_off[1] += 1
+    assert call(layout=ctypes.byref(L2)) == -1
+    # the 720P 241-frame layer: 1920 tiles per head; enough subset rows to
+    # overflow the scratch, and the workspace query agrees on the size
+    big = V.veda_layout_init(61, 45, 80, 128, 128, [(4, 4, 8)] * 24)
+    n_over = cap // (4 * big.max_tiles) + 1
+    ws = ctypes.c_int64(0)
+    assert lib.veda_distill_grad_workspace(ctypes.byref(big), n_over, 128, ctypes.byref(ws)) == 0
+    assert ws.value > cap
+    assert call(layout=ctypes.byref(big), n=n_over) == -2
+    # the largest subset at this layer that the benchmark uses (10 % of every head) fits
+    n_bench = 24 * 192
+    assert lib.veda_distill_grad_workspace(ctypes.byref(big), n_bench, 128, ctypes.byref(ws)) == 0
+    assert ws.value <= cap

@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
         "veda_distill_grad": (c_i32, [P, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_i64,
                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
         "veda_distill_grad_workspace": (c_i32, [P, c_i32, c_i32, ctypes.POINTER(c_i64)]),
+        "veda_distill_grad_noalloc": (c_i32, [P, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32,
+                                              c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
         "veda_head_sq_error": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp]),
         "veda_head_sq_error_workspace": (c_i32, [P, ctypes.POINTER(c_i64)]),
         "veda_sparse_attn_bwd": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
@@ -377,6 +379,31 @@ def veda_distill_grad(L: veda_layout, scores, out_map, q_tiles, desc, phi, d_e: 
     _check(lib().veda_distill_grad(ctypes.byref(L), ps, pm, pq, n_sub, pd, pp, int(d_e), pw, have,
                                    pl, gq, gk, bq, bk, _stream(stream)),
            "veda_distill_grad")
+
+
+def veda_distill_grad_noalloc(L: veda_layout, scores, out_map, q_tiles, desc, phi, d_e: int,
+                              loss, grad_w_q, grad_w_k, grad_b_q=None, grad_b_k=None,
+                              stream=None) -> None:
+    """veda_distill_grad in the library's static per-GPU scratch: no
+    workspace argument, nothing allocated; calls overlapping on one GPU race."""
+    torch = _torch()
+    f32 = torch.float32
+    n_sub = int(q_tiles.numel())
+    d = L.head_dim
+    H = L.num_heads
+    ps = _dev(scores, "scores", f32, L.total_scores)
+    pm = _dev(out_map, "map", f32, n_sub * L.max_tiles)
+    pq = _dev(q_tiles, "q_tiles", torch.int32, n_sub)
+    pd = _dev(desc, "desc", f32, 2 * L.total_tiles * 3 * d)
+    pp = _dev(phi, "phi", f32, 2 * L.total_tiles * int(d_e))
+    pl = _dev(loss, "loss", f32, 1)
+    gq = _dev(grad_w_q, "grad_w_q", f32, H * int(d_e) * 3 * d)
+    gk = _dev(grad_w_k, "grad_w_k", f32, H * int(d_e) * 3 * d)
+    bq = _dev(grad_b_q, "grad_b_q", f32, H * int(d_e), True)
+    bk = _dev(grad_b_k, "grad_b_k", f32, H * int(d_e), True)
+    _check(lib().veda_distill_grad_noalloc(ctypes.byref(L), ps, pm, pq, n_sub, pd, pp, int(d_e),
+                                           pl, gq, gk, bq, bk, _stream(stream)),
+           "veda_distill_grad_noalloc")
 
 
 def veda_head_sq_error_workspace(L: veda_layout) -> int:

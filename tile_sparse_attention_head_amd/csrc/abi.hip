@@ -208,6 +208,22 @@ int bwd_args(const veda_layout* L, const void* q, const void* k, size_t qk_bytes
   return VEDA_OK;
 }
 
+// Checks shared by the two distillation entry points (all but the workspace).
+int distill_args(const veda_layout* L, const float* scores, const float* map,
+                 const int32_t* q_tiles, int32_t n_sub, const float* desc, const float* phi,
+                 int32_t d_e, const float* loss, const float* grad_w_q, const float* grad_w_k) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (n_sub < 0 || d_e < 1) return VEDA_ERR_INVALID_ARG;
+  if (desc == nullptr || phi == nullptr || loss == nullptr || grad_w_q == nullptr ||
+      grad_w_k == nullptr)
+    return VEDA_ERR_INVALID_ARG;
+  if (n_sub > 0 && (scores == nullptr || map == nullptr || q_tiles == nullptr))
+    return VEDA_ERR_INVALID_ARG;
+  if (d_e > 256 || n_sub > VEDA_MAX_SUBSET) return VEDA_ERR_UNSUPPORTED;
+  if (L->head_dim != 64 && L->head_dim != 128) return VEDA_ERR_UNSUPPORTED;
+  return VEDA_OK;
+}
+
 }  // namespace
 }  // namespace veda
 
@@ -433,19 +449,32 @@ int veda_distill_grad(const veda_layout* L, const float* scores, const float* ma
                       int32_t d_e, void* workspace, int64_t workspace_bytes, float* loss,
                       float* grad_w_q, float* grad_w_k, float* grad_b_q, float* grad_b_k,
                       void* stream) {
-  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
-  if (n_sub < 0 || d_e < 1) return VEDA_ERR_INVALID_ARG;
-  if (desc == nullptr || phi == nullptr || workspace == nullptr || loss == nullptr ||
-      grad_w_q == nullptr || grad_w_k == nullptr)
-    return VEDA_ERR_INVALID_ARG;
-  if (n_sub > 0 && (scores == nullptr || map == nullptr || q_tiles == nullptr))
-    return VEDA_ERR_INVALID_ARG;
-  if (d_e > 256 || n_sub > VEDA_MAX_SUBSET) return VEDA_ERR_UNSUPPORTED;
-  if (L->head_dim != 64 && L->head_dim != 128) return VEDA_ERR_UNSUPPORTED;
+  const int st = distill_args(L, scores, map, q_tiles, n_sub, desc, phi, d_e, loss, grad_w_q,
+                              grad_w_k);
+  if (st != VEDA_OK) return st;
+  if (workspace == nullptr) return VEDA_ERR_INVALID_ARG;
   const DevLayout dl = make_dev_layout(L);
   if (workspace_bytes < distill_workspace_bytes(dl, n_sub, d_e)) return VEDA_ERR_INVALID_ARG;
   if (!aligned16(workspace)) return VEDA_ERR_UNSUPPORTED;
   return finish(launch_distill(dl, scores, map, q_tiles, n_sub, desc, phi, d_e, workspace, loss,
+                               grad_w_q, grad_w_k, grad_b_q, grad_b_k, (hipStream_t)stream),
+                stream);
+}
+
+int veda_distill_grad_noalloc(const veda_layout* L, const float* scores, const float* map,
+                              const int32_t* q_tiles, int32_t n_sub, const float* desc,
+                              const float* phi, int32_t d_e, float* loss, float* grad_w_q,
+                              float* grad_w_k, float* grad_b_q, float* grad_b_k, void* stream) {
+  const int st = distill_args(L, scores, map, q_tiles, n_sub, desc, phi, d_e, loss, grad_w_q,
+                              grad_w_k);
+  if (st != VEDA_OK) return st;
+  const DevLayout dl = make_dev_layout(L);
+  if (distill_workspace_bytes(dl, n_sub, d_e) > VEDA_DISTILL_STATIC_SCRATCH_BYTES)
+    return VEDA_ERR_UNSUPPORTED;
+  void* scratch_ptr = nullptr;
+  const int ss = distill_static_scratch(&scratch_ptr);
+  if (ss != VEDA_OK) return ss;
+  return finish(launch_distill(dl, scores, map, q_tiles, n_sub, desc, phi, d_e, scratch_ptr, loss,
                                grad_w_q, grad_w_k, grad_b_q, grad_b_k, (hipStream_t)stream),
                 stream);
 }

@@ -15,6 +15,8 @@
 // deterministic.  The work is small next to the map that produces the
 // reference (a few matrix products of n_h x d_e x 3d per head), and the
 // kernels are plain LDS-tiled vector code.
+#include <mutex>
+
 #include "veda_internal.hpp"
 
 namespace veda {
@@ -322,6 +324,33 @@ int64_t distill_workspace_bytes(const DevLayout& L, int64_t n_sub, int d_e) {
   int64_t total = 0;
   carve(L, n_sub, d_e, nullptr, &total);
   return total;
+}
+
+// Scratch of veda_distill_grad_noalloc: a device array of the library, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it names a stand-in, not device
+// memory): the address each device holds it at is looked up once per device
+// with that device current and kept in `g_scratch`.
+static __device__ __align__(256) unsigned char scratch[VEDA_DISTILL_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+int distill_static_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VEDA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return VEDA_ERR_LAUNCH;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return VEDA_OK;
 }
 
 int launch_distill(const DevLayout& L, const float* scores, const float* map,

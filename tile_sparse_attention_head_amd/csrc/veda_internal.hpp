@@ -93,6 +93,11 @@ int launch_distill(const DevLayout& L, const float* scores, const float* map,
                    int d_e, void* workspace, float* loss, float* dwq, float* dwk, float* dbq,
                    float* dbk, hipStream_t s);
 
+// Device address, on the current device, of the library's static scratch for
+// veda_distill_grad_noalloc (VEDA_DISTILL_STATIC_SCRATCH_BYTES); looked up on
+// the first call per device.  VEDA_OK, or VEDA_ERR_LAUNCH if HIP refuses.
+int distill_static_scratch(void** ptr);
+
 // Per-head squared error of two token-order outputs (tiling search).
 int64_t head_error_workspace_bytes(const DevLayout& L);
 int launch_head_error(const DevLayout& L, const void* a, const void* b, double* err, double* ref,
