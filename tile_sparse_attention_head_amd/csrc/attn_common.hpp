@@ -96,6 +96,27 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t G) {
   return xcd * per + (xcd < rem ? xcd : rem) + b / X;
 }
 
+// Lockstep XCD order over the tiles of a layer.  Every head's tiles are cut
+// into 8 contiguous chunks, chunk x going to XCD x (the hardware places
+// workgroup b on XCD b % 8); XCD x walks chunk x of head 0, then chunk x of
+// head 1, and so on.  All XCDs therefore work inside the same head at the
+// same time, so the key/value tiles in flight are those of about one head
+// (which the memory-side cache holds), while each XCD's query tiles are a
+// contiguous, spatially compact run of that head.  Returns the global tile
+// of workgroup b, or -1 past the end of its XCD's run (the grid is 8 times
+// the longest run; see lockstep_grid).
+__device__ __forceinline__ int64_t lockstep_tile(const DevLayout& L, int64_t b) {
+  const int x = (int)(b & 7);
+  int64_t i = b >> 3;
+  for (int h = 0; h < L.heads; ++h) {
+    const int64_t n = L.tile_off[h + 1] - L.tile_off[h];
+    const int64_t lo = n * x / 8, len = n * (x + 1) / 8 - lo;
+    if (i < len) return L.tile_off[h] + lo + i;
+    i -= len;
+  }
+  return -1;
+}
+
 // A step buffer in LDS: R rows of CPR 16-byte chunks, each row followed by
 // one 16-byte pad, so that 16 lanes reading one chunk column of 16
 // consecutive rows hit 16 distinct bank groups (row stride (CPR+1)*16 bytes

@@ -2,7 +2,9 @@
 // the Veda pages describe: at 95 % sparsity each query tile keeps about 5 %
 // of the key tiles, chosen by the estimator's scores).
 //
-// One workgroup per query-tile row.  Scores are mapped to order-preserving
+// Rows of up to 2048 columns go to a kernel with one wave per row and the
+// keys in registers (see select_wave_kernel); longer rows to one workgroup
+// per query-tile row.  Scores are mapped to order-preserving
 // 32-bit keys (NaN -> 0, below every number; -0.0 folded onto +0.0) and kept
 // in LDS.  A most-significant-digit-first radix select (four 8-bit rounds,
 // LDS histograms) finds the k-th largest key K* and how many of the keys equal
@@ -133,6 +135,121 @@ __global__ __launch_bounds__(kThreads) void select_kernel(DevLayout L, SelectArg
   }
 }
 
+// One wave per row, for rows of at most 64*KPL columns: lane l holds the keys
+// of columns l, l + 64, ..., l + 64*(KPL-1) in registers (key 0 past the row's
+// end).  The k-th largest key K* is found bit by bit from the top: t is the
+// largest value with at least k keys >= t, and each candidate t | bit is
+// counted over the wave with one compare and a ballot population count, no
+// LDS and no barrier.  Once the upper 16 bits of K* are known, only keys
+// sharing them can decide the lower bits; when at most 64 do, they are
+// compacted into the wave's LDS slots (one per lane) and the last 16 rounds
+// count those alone.  The final pass walks the columns in index order, keeps
+// every key > K* and the lowest-index keys == K*, and writes each kept column
+// at the position the ballot prefix gives it: ascending, deterministic, and
+// the same result as the workgroup kernel.
+constexpr int kWaves = 4;
+
+template <int KPL>
+__global__ __launch_bounds__(64 * kWaves) void select_wave_kernel(DevLayout L, SelectArgs sa,
+                                                                  const float* __restrict__ scores,
+                                                                  int32_t* __restrict__ row_ptr,
+                                                                  int32_t* __restrict__ col_idx) {
+  __shared__ uint32_t cand_lds[kWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r = (int64_t)blockIdx.x * kWaves + wave;
+  if (r >= L.tile_off[L.heads]) return;
+  const int h = head_of_tile(L, r);
+  const int i = (int)(r - L.tile_off[h]);
+  const int n = (int)(L.tile_off[h + 1] - L.tile_off[h]);
+  const int k = sa.k[h];
+  const int64_t start = sa.nnz_off[h] + (int64_t)i * k;
+  if (lane == 0) {
+    row_ptr[r] = (int32_t)start;
+    if (r + 1 == L.tile_off[L.heads]) row_ptr[r + 1] = (int32_t)sa.nnz_off[L.heads];
+  }
+  const float* row = scores + L.score_off[h] + (int64_t)i * n;
+  uint32_t key[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int c = 64 * j + lane;
+    key[j] = c < n ? order_key(row[c]) : 0u;
+  }
+  // count of keys >= v over the wave (padding keys are 0: they count only
+  // for v = 0, where every real key counts too and n >= k already)
+  auto count_ge = [&](uint32_t v) {
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(key[j] >= v));
+    return cnt;
+  };
+  uint32_t t = 0u;
+#pragma unroll 1
+  for (int b = 31; b >= 16; --b) {
+    const uint32_t cand = t | (1u << b);
+    if (count_ge(cand) >= k) t = cand;
+  }
+  // keys above the 16-bit prefix always count; keys sharing it are the
+  // candidates for the low bits
+  const uint32_t hi = t >> 16;
+  int above = 0, m = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    above += __popcll(__ballot((key[j] >> 16) > hi));
+    m += __popcll(__ballot((key[j] >> 16) == hi));
+  }
+  if (m <= 64) {
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const bool is_c = (key[j] >> 16) == hi;
+      const uint64_t bal = __ballot(is_c);
+      if (is_c) cand_lds[wave][base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = key[j];
+      base += __popcll(bal);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    const uint32_t mine = lane < m ? cand_lds[wave][lane] : 0u;
+    const bool live = lane < m;
+#pragma unroll 1
+    for (int b = 15; b >= 0; --b) {
+      const uint32_t cand = t | (1u << b);
+      if (above + __popcll(__ballot(live && mine >= cand)) >= k) t = cand;
+    }
+  } else {
+#pragma unroll 1
+    for (int b = 15; b >= 0; --b) {
+      const uint32_t cand = t | (1u << b);
+      if (count_ge(cand) >= k) t = cand;
+    }
+  }
+  // t = K*, the k-th largest key; keep every key > K* and the first `need`
+  // keys == K* in index order
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) gt += __popcll(__ballot(64 * j + lane < n && key[j] > t));
+  const int need = k - gt;
+  int32_t* out = col_idx + start;
+  int pos = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int c = 64 * j + lane;
+    const bool real = c < n;
+    const bool eq = real && key[j] == t;
+    const uint64_t beq = __ballot(eq);
+    const int eq_rank = eq_seen + (int)__builtin_amdgcn_mbcnt_hi(
+                                      (uint32_t)(beq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)beq, 0u));
+    const bool take = (real && key[j] > t) || (eq && eq_rank < need);
+    const uint64_t bt = __ballot(take);
+    if (take)
+      out[pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u))] = c;
+    pos += __popcll(bt);
+    eq_seen += __popcll(beq);
+  }
+}
+
 }  // namespace
 
 int launch_select(const DevLayout& L, const float* scores, const int32_t* k_host,
@@ -145,8 +262,19 @@ int launch_select(const DevLayout& L, const float* scores, const int32_t* k_host
   }
   const unsigned rows = (unsigned)L.tile_off[L.heads];
   if (rows == 0) return VEDA_OK;
-  hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(kThreads),
-                     (size_t)L.max_tiles * sizeof(uint32_t), s, L, sa, scores, row_ptr, col_idx);
+  const unsigned wgs = (rows + kWaves - 1) / kWaves;
+  if (L.max_tiles <= 512)
+    hipLaunchKernelGGL(select_wave_kernel<8>, dim3(wgs), dim3(64 * kWaves), 0, s, L, sa, scores,
+                       row_ptr, col_idx);
+  else if (L.max_tiles <= 1024)
+    hipLaunchKernelGGL(select_wave_kernel<16>, dim3(wgs), dim3(64 * kWaves), 0, s, L, sa, scores,
+                       row_ptr, col_idx);
+  else if (L.max_tiles <= 2048)
+    hipLaunchKernelGGL(select_wave_kernel<32>, dim3(wgs), dim3(64 * kWaves), 0, s, L, sa, scores,
+                       row_ptr, col_idx);
+  else
+    hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(kThreads),
+                       (size_t)L.max_tiles * sizeof(uint32_t), s, L, sa, scores, row_ptr, col_idx);
   return launch_status();
 }
 

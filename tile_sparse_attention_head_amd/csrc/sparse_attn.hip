@@ -33,9 +33,17 @@
 // outside [0, n_tiles) becomes a tile whose keys are all masked, which leaves
 // the result exactly as if it were skipped.
 //
-// Workgroups are ordered XCD-aware and head-major, so the query tiles running
-// together on one XCD are spatial neighbours whose kept key tiles overlap in
-// that XCD's L2.
+// Workgroups take their query tiles in an XCD-aware order.  With heads of at
+// least kLockstepTiles tiles, in lockstep: all XCDs work in the same head at
+// once, so the key/value tiles in flight are about one head's, which the
+// memory-side cache holds, and the query tiles running together on one XCD
+// are a contiguous run of that head (neighbours whose kept key tiles overlap
+// in its L2).  With smaller heads, one eighth of a head is shorter than the
+// workgroups an XCD runs at once, and each XCD takes a contiguous eighth of
+// the layer instead.
+#include <algorithm>
+#include <climits>
+
 #include "attn_common.hpp"
 
 namespace veda {
@@ -44,6 +52,9 @@ namespace {
 using namespace attn;
 
 constexpr float kLazyRescale = 8.0f;   // log2 of the largest unnormalised p
+// Lockstep XCD order from this many tiles per head on: 8 XCDs x 64 resident
+// workgroups (two per CU on 32 CUs).
+constexpr int kLockstepTiles = 512;
 
 template <int D, int S>
 struct Pipe {
@@ -66,7 +77,7 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ vt, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, float scale_log2, __bf16* __restrict__ o,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, int lockstep) {
   using P = Pipe<D, S>;
   using KB = typename P::KBuf;
   using VB = typename P::VBuf;
@@ -80,7 +91,8 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char v1[VB::BYTES];
   __shared__ BiasTable<SPT, 9> btab;
 
-  const int64_t g = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t g = lockstep ? lockstep_tile(L, blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+  if (g < 0) return;   // past the end of this XCD's run
   const int h = head_of_tile(L, g);
   const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
   const int64_t head_base = L.tile_off[h];
@@ -351,15 +363,19 @@ template <bool TOK>
 void launch_attn(const DevLayout& L, const void* q, const void* k, const void* vt,
                  const int32_t* row_ptr, const int32_t* col_idx, float scale_log2, void* o,
                  float* lse, hipStream_t s) {
-  const unsigned G = (unsigned)L.tile_off[L.heads];
+  int min_tiles = INT32_MAX;
+  for (int h = 0; h < L.heads; ++h)
+    min_tiles = std::min<int>(min_tiles, (int)(L.tile_off[h + 1] - L.tile_off[h]));
+  const int lockstep = min_tiles >= kLockstepTiles;
+  const unsigned G = (unsigned)(lockstep ? lockstep_grid(L) : L.tile_off[L.heads]);
   if (L.d == 128) {
     hipLaunchKernelGGL((sparse_attn_fwd_kernel<128, 128, TOK>), dim3(G), dim3(256), 0, s,
                        L, (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, row_ptr, col_idx,
-                       scale_log2, (__bf16*)o, lse);
+                       scale_log2, (__bf16*)o, lse, lockstep);
   } else {
     hipLaunchKernelGGL((sparse_attn_fwd_kernel<64, 64, TOK>), dim3(G), dim3(128), 0, s, L,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, row_ptr, col_idx,
-                       scale_log2, (__bf16*)o, lse);
+                       scale_log2, (__bf16*)o, lse, lockstep);
   }
 }
 }  // namespace

@@ -63,6 +63,22 @@ __device__ __forceinline__ TileExtent tile_extent(const DevLayout& L, int h, int
   return e;
 }
 
+// Workgroups of a launch in lockstep XCD order (attn::lockstep_tile): 8 times
+// the longest of the 8 per-XCD runs, each the sum over heads of one eighth of
+// the head's tiles.
+inline int64_t lockstep_grid(const DevLayout& L) {
+  int64_t longest = 0;
+  for (int x = 0; x < 8; ++x) {
+    int64_t run = 0;
+    for (int h = 0; h < L.heads; ++h) {
+      const int64_t n = L.tile_off[h + 1] - L.tile_off[h];
+      run += n * (x + 1) / 8 - n * x / 8;
+    }
+    if (run > longest) longest = run;
+  }
+  return 8 * longest;
+}
+
 // Launchers (each returns a veda_status; arguments already validated).
 int launch_permute(const DevLayout& L, int dtype, int dir, const void* x, void* y,
                    hipStream_t s);
