@@ -164,13 +164,18 @@ def test_dense_full_size_sampled_against_token_order_dense_attention():
 
 @pytest.mark.parametrize("n_shape,pct,ties", [(((61, 45, 80), (4, 4, 8)), 95, False),
                                               (((61, 45, 80), (1, 8, 16)), 90, True),
+                                              (((61, 45, 80), (4, 4, 8)), 90, "flat"),
+                                              (((31, 45, 80), (1, 8, 16)), 95, "flat"),
                                               (((64, 64, 256), (1, 8, 16)), 95, False),
                                               (((64, 64, 256), (1, 8, 16)), 90, True)])
 def test_select_bit_exact_large_rows(n_shape, pct, ties):
-    """Random f32 score matrices of one head with 1830 / 1920 / 8192 key
-    tiles per row (8192 is the largest the selection call accepts), k at 5 %
-    and 10 %; with ties the values come from a six-value set with +-0, and
-    NaN is planted on a lattice.  Every row against oracle.select_topk."""
+    """Random f32 score matrices of one head with 930 / 1830 / 1920 / 8192
+    key tiles per row (8192 is the largest the selection call accepts), k at
+    5 % and 10 %; with ties the values come from a six-value set with +-0, and
+    NaN is planted on a lattice; "flat" rows are mostly one value with a few
+    Gaussian entries, so that most keys tie at the k-th place (more than 512
+    keys reach the wave kernel's pre-filter threshold, which sends the row to
+    its search over all keys).  Every row against oracle.select_topk."""
     grid, shape = n_shape
     _say(f"select large rows {grid} {shape} {pct}% ties={ties}")
     torch = need_gpu()
@@ -179,8 +184,14 @@ def test_select_bit_exact_large_rows(n_shape, pct, ties):
     L = V.veda_layout_init(*grid, 128, 128, [shape])
     n = L.n(0)
     k = V.veda_keep_count(n, pct)
-    s = random_scores(n, n, seed=300 + n + pct, ties=ties)
-    if ties:
+    if ties == "flat":
+        s = np.full((n, n), 0.5, dtype=np.float32)
+        rng = np.random.default_rng(400 + n)
+        mask = rng.random((n, n)) < 0.02
+        s[mask] = rng.standard_normal(int(mask.sum())).astype(np.float32)
+    else:
+        s = random_scores(n, n, seed=300 + n + pct, ties=bool(ties))
+    if ties is True:
         s[::7, ::11] = np.nan
     rp = torch.empty(n + 1, dtype=torch.int32, device="cuda")
     ci = torch.empty(n * k, dtype=torch.int32, device="cuda")

@@ -140,21 +140,41 @@ __global__ __launch_bounds__(kThreads) void select_kernel(DevLayout L, SelectArg
 // end).  The k-th largest key K* is found bit by bit from the top: t is the
 // largest value with at least k keys >= t, and each candidate t | bit is
 // counted over the wave with one compare and a ballot population count, no
-// LDS and no barrier.  Once the upper 16 bits of K* are known, only keys
-// sharing them can decide the lower bits; when at most 64 do, they are
-// compacted into the wave's LDS slots (one per lane) and the last 16 rounds
-// count those alone.  The final pass walks the columns in index order, keeps
-// every key > K* and the lowest-index keys == K*, and writes each kept column
-// at the position the ballot prefix gives it: ascending, deterministic, and
-// the same result as the workgroup kernel.
+// barrier.
+//
+// Pre-filter (k <= 256, rows up to 1024 columns; with 32 keys per lane the
+// extra registers cost more occupancy than the filter saves): with
+// r = ceil(k / 64), every lane's r-th largest
+// key is >= tau0, their minimum over the wave, so at least 64 r >= k keys are
+// >= tau0 and K* >= tau0; K* <= the row's largest key, so K* shares their
+// common upper bits.  Only the real keys >= tau0 (a few per lane, compacted
+// into the wave's LDS) are counted, from the first bit where tau0 and the
+// largest key differ: below tau0 both the full and the candidate counts reach
+// k, above it they are equal, so the search ends at the same K*.  Rows where
+// more than kCand keys pass the filter (heavy ties) take the plain search
+// over all keys, which after the upper 16 bits counts only the keys sharing
+// them when at most 64 do.
+//
+// The final pass walks the columns in index order, keeps every key > K* and
+// the lowest-index keys == K*, and writes each kept column at the position the
+// ballot prefix gives it: ascending, deterministic, and the same result as the
+// workgroup kernel.
 constexpr int kWaves = 4;
+constexpr int kCand = 512;   // pre-filter candidates kept in LDS per wave
+
+__device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
+}
+__device__ __forceinline__ uint32_t lane_prefix(uint64_t bal) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
 
 template <int KPL>
 __global__ __launch_bounds__(64 * kWaves) void select_wave_kernel(DevLayout L, SelectArgs sa,
                                                                   const float* __restrict__ scores,
                                                                   int32_t* __restrict__ row_ptr,
                                                                   int32_t* __restrict__ col_idx) {
-  __shared__ uint32_t cand_lds[kWaves][64];
+  __shared__ uint32_t cand_lds[kWaves][kCand];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t r = (int64_t)blockIdx.x * kWaves + wave;
@@ -175,53 +195,110 @@ __global__ __launch_bounds__(64 * kWaves) void select_wave_kernel(DevLayout L, S
     const int c = 64 * j + lane;
     key[j] = c < n ? order_key(row[c]) : 0u;
   }
-  // count of keys >= v over the wave (padding keys are 0: they count only
-  // for v = 0, where every real key counts too and n >= k already)
-  auto count_ge = [&](uint32_t v) {
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(key[j] >= v));
-    return cnt;
-  };
+  uint32_t* cl = cand_lds[wave];
   uint32_t t = 0u;
-#pragma unroll 1
-  for (int b = 31; b >= 16; --b) {
-    const uint32_t cand = t | (1u << b);
-    if (count_ge(cand) >= k) t = cand;
-  }
-  // keys above the 16-bit prefix always count; keys sharing it are the
-  // candidates for the low bits
-  const uint32_t hi = t >> 16;
-  int above = 0, m = 0;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    above += __popcll(__ballot((key[j] >> 16) > hi));
-    m += __popcll(__ballot((key[j] >> 16) == hi));
-  }
-  if (m <= 64) {
-    int base = 0;
+  bool found = false;
+  const int rr = (k + 63) / 64;
+  if (KPL <= 16 && rr <= 4) {
+    // this lane's largest and r-th largest key
+    uint32_t m1 = 0u, m2 = 0u, m3 = 0u, m4 = 0u;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      const bool is_c = (key[j] >> 16) == hi;
-      const uint64_t bal = __ballot(is_c);
-      if (is_c) cand_lds[wave][base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = key[j];
-      base += __popcll(bal);
+      const uint32_t x = key[j];
+      m4 = med3u(m3, m4, x);
+      m3 = med3u(m2, m3, x);
+      m2 = med3u(m1, m2, x);
+      m1 = max(m1, x);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    const uint32_t mine = lane < m ? cand_lds[wave][lane] : 0u;
-    const bool live = lane < m;
-#pragma unroll 1
-    for (int b = 15; b >= 0; --b) {
-      const uint32_t cand = t | (1u << b);
-      if (above + __popcll(__ballot(live && mine >= cand)) >= k) t = cand;
+    uint32_t tau = rr == 1 ? m1 : rr == 2 ? m2 : rr == 3 ? m3 : m4, top_key = m1;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      tau = min(tau, (uint32_t)__shfl_xor((int)tau, o, 64));
+      top_key = max(top_key, (uint32_t)__shfl_xor((int)top_key, o, 64));
     }
-  } else {
+    int m = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) m += __popcll(__ballot(64 * j + lane < n && key[j] >= tau));
+    if (m <= kCand) {
+      int base = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const bool is_c = 64 * j + lane < n && key[j] >= tau;
+        const uint64_t bal = __ballot(is_c);
+        if (is_c) cl[base + lane_prefix(bal)] = key[j];
+        base += __popcll(bal);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      constexpr int CM = kCand / 64;
+      uint32_t cv[CM];
+#pragma unroll
+      for (int j = 0; j < CM; ++j) cv[j] = 64 * j + lane < m ? cl[64 * j + lane] : 0u;
+      const int cw = (m + 63) / 64;   // candidate slots in use per lane
+      const uint32_t diff = tau ^ top_key;
+      const int top = diff ? 31 - __builtin_clz(diff) : -1;
+      t = top < 0 ? tau : (top == 31 ? 0u : tau & ~((2u << top) - 1u));
 #pragma unroll 1
-    for (int b = 15; b >= 0; --b) {
+      for (int b = top; b >= 0; --b) {
+        const uint32_t cand = t | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < CM; ++j)
+          if (j < cw) cnt += __popcll(__ballot(cv[j] >= cand));
+        if (cnt >= k) t = cand;
+      }
+      found = true;
+    }
+  }
+  if (!found) {
+    // count of keys >= v over the wave (padding keys are 0: they count only
+    // for v = 0, where every real key counts too and n >= k already)
+    auto count_ge = [&](uint32_t v) {
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(key[j] >= v));
+      return cnt;
+    };
+#pragma unroll 1
+    for (int b = 31; b >= 16; --b) {
       const uint32_t cand = t | (1u << b);
       if (count_ge(cand) >= k) t = cand;
+    }
+    // keys above the 16-bit prefix always count; keys sharing it are the
+    // candidates for the low bits
+    const uint32_t hi = t >> 16;
+    int above = 0, m = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      above += __popcll(__ballot((key[j] >> 16) > hi));
+      m += __popcll(__ballot((key[j] >> 16) == hi));
+    }
+    if (m <= 64) {
+      int base = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const bool is_c = (key[j] >> 16) == hi;
+        const uint64_t bal = __ballot(is_c);
+        if (is_c) cl[base + lane_prefix(bal)] = key[j];
+        base += __popcll(bal);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint32_t mine = lane < m ? cl[lane] : 0u;
+      const bool live = lane < m;
+#pragma unroll 1
+      for (int b = 15; b >= 0; --b) {
+        const uint32_t cand = t | (1u << b);
+        if (above + __popcll(__ballot(live && mine >= cand)) >= k) t = cand;
+      }
+    } else {
+#pragma unroll 1
+      for (int b = 15; b >= 0; --b) {
+        const uint32_t cand = t | (1u << b);
+        if (count_ge(cand) >= k) t = cand;
+      }
     }
   }
   // t = K*, the k-th largest key; keep every key > K* and the first `need`
@@ -238,13 +315,10 @@ __global__ __launch_bounds__(64 * kWaves) void select_wave_kernel(DevLayout L, S
     const bool real = c < n;
     const bool eq = real && key[j] == t;
     const uint64_t beq = __ballot(eq);
-    const int eq_rank = eq_seen + (int)__builtin_amdgcn_mbcnt_hi(
-                                      (uint32_t)(beq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)beq, 0u));
+    const int eq_rank = eq_seen + (int)lane_prefix(beq);
     const bool take = (real && key[j] > t) || (eq && eq_rank < need);
     const uint64_t bt = __ballot(take);
-    if (take)
-      out[pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u))] = c;
+    if (take) out[pos + lane_prefix(bt)] = c;
     pos += __popcll(bt);
     eq_seen += __popcll(beq);
   }
