@@ -1,7 +1,11 @@
 """Benchmark of the tile-sparse attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--sparsity S] [--no-cpu-baseline] [--no-context]
+                    [--sparsity S] [--warm] [--no-cpu-baseline] [--no-context]
+
+Default workload: the 720P 241-frame layer (61x45x80 latent, 219,600 tokens,
+24 heads with per-head tile shapes drawn from the seed) at 95 % tile
+sparsity, the largest single-GPU configuration of the metric.
 
 One step is one pass of every stage of the path over one synthetic layer
 whose inputs are already resident in HBM, through the layer's fused calls:
@@ -10,35 +14,40 @@ whose inputs are already resident in HBM, through the layer's fused calls:
   forward-transposed) -> veda_tile_score -> veda_select_tiles ->
   veda_sparse_attn_fwd_tokens (O written in token order) ->
   veda_oracle_maxpool_map (the distillation target on the workload's seeded
-  query-tile subset)
+  10 % query-tile subset)
 
-The context runs also time the same layer one method step per call
-(veda_tile_permute, veda_tripool_score, veda_select_tiles,
-veda_sparse_attn_fwd, inverse veda_tile_permute), the layer at 95 % and 0 %
-sparsity, with cold caches, the distillation step, the attention backward and
-the tiling search, and record the GPU clocks and socket power (amd-smi) while
-the attention kernel runs back to back.
-
-W untimed steps run first, then exactly K steps are timed between two device
-synchronisations.  Every stage is also bracketed by HIP events on the stream
-the kernels run on, which gives the per-layer latency (all stages but the
-map), the map's latency and the attention kernel's average launch duration.
+Timing.  W untimed steps run first, then exactly K steps are timed between two
+device synchronisations.  By default caches are cold: a 512 MiB buffer is
+overwritten before every step (inside the timed region), which evicts the L2s
+and the 256 MiB MALL; ``--warm`` drops the overwrite.  Every stage is also
+bracketed by HIP events on the stream the kernels run on; stage times are
+medians over the K steps (p10/p50/p90 beside them).
 
 Printed: one JSON line.  ``value`` is the effective throughput of the step in
 TFLOP/s: the matrix work the tile kernels compute (4*S^2*d per kept
 (query tile, key tile) pair of the attention, plus 2*S^2*d per (subset query
 tile, key tile) pair of the map -- its one Q K^T product; the second pass
-reads the row maxima the first one stored) divided by the step time.
+reads the row maxima the first one stored) divided by the wall time per step.
 ``roofline`` is for the stage that takes the longest (the dominant kernel;
 with the context runs it also carries the clock measured under that kernel
-and its fraction of the peak at that clock);
-``kernels`` gives the same record for every stage: matrix-bound kernels in
-TFLOP/s against the bf16 peak, data-movement kernels in GB/s of algorithmic
-bytes against the HBM peak, with ``traffic`` the HBM bytes per launch read
-from the committed rocprofv3 counter summaries under profiles/ (null when the
-kernel's sources changed since).  ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the same workload.  With --gpus above 1 the benchmark refuses: this path runs on one
-GPU (heads shard across GPUs without any exchange inside the path).
+and its fraction of the peak at that clock); ``kernels`` gives the same
+record for every stage: matrix-bound kernels in TFLOP/s against the bf16
+peak, data-movement kernels in GB/s of algorithmic bytes against the HBM
+peak, with ``traffic`` the HBM bytes per launch read from the committed
+rocprofv3 counter summaries under profiles/ (null when the kernel's sources
+changed since).  ``cpu_baseline`` times the CPU oracle on a seeded sample of
+the same layer (2 heads x 32 query tiles plus 4 map tiles per head) and
+extrapolates it to the layer.
+
+Context runs (``context``, none of it in ``value``): the same steps with warm
+caches; the same layer at 0 % sparsity (dense attention, the same kernel) and
+the speed-up over it; the layer one call per method step; the distillation
+step and the attention backward; GPU clocks and socket power (amd-smi) while
+the attention and the map kernels run back to back; the Wan-1.3B-like and
+Waver-12B-like layers at 90 % and 95 %; and the head-aware tiling search on
+the Wan-1.3B-like layer.  With --gpus above 1 the benchmark refuses: this path
+runs on one GPU (heads shard across GPUs without any exchange inside the
+path).
 """
 from __future__ import annotations
 
@@ -67,10 +76,11 @@ KERNEL_SOURCES = {
     "permute_fwd_pool_kernel": ("permute.hip", "veda_internal.hpp"),
     "project_kernel": ("tripool.hip", "veda_internal.hpp"),
     "score_kernel": ("tripool.hip", "veda_internal.hpp"),
-    "permute_fwd_t_kernel": ("permute.hip", "veda_internal.hpp"),
+    "permute_fwd_t_bf16_kernel": ("permute.hip", "veda_internal.hpp"),
     "permute_inv_kernel": ("permute.hip", "veda_internal.hpp"),
     "tripool_pool_kernel": ("tripool.hip", "veda_internal.hpp"),
     "select_kernel": ("select.hip", "veda_internal.hpp"),
+    "select_wave_kernel": ("select.hip", "veda_internal.hpp"),
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -227,27 +237,29 @@ class Bench:
         desc = L.total_tiles * 3 * d * 4                # one side's descriptors, f32
         d_e = self.layer.d_e
         proj = 2 * desc + 2 * L.num_heads * d_e * 3 * d * 4 + 2 * L.total_tiles * d_e * 4
+        # rows of up to 2048 key tiles: one wave per row; longer: a workgroup per row
+        sel = "select_wave_kernel" if L.max_tiles <= 2048 else "select_kernel"
         if self.fused:
             return {
                 "permute_pool_q": ("hbm", tok + til + desc, "permute_fwd_pool_kernel"),
                 "permute_pool_k": ("hbm", tok + til + desc, "permute_fwd_pool_kernel"),
-                "permute_vt": ("hbm", tok + til, "permute_fwd_t_kernel"),
+                "permute_vt": ("hbm", tok + til, "permute_fwd_t_bf16_kernel"),
                 # projection (descriptors + weights in, phi out) and score
                 # (phi in, score matrix out)
                 "tile_score": ("hbm", proj + 2 * L.total_tiles * d_e * 4 + 4 * L.total_scores,
                                "project_kernel"),
                 "select": ("hbm", 4 * L.total_scores + 4 * nnz + 4 * (L.total_tiles + 1),
-                           "select_kernel"),
+                           sel),
                 "sparse_attn": ("mfma", self.flops_c, "sparse_attn_fwd_kernel"),
                 "map": ("mfma", self.flops_d, "map_stats_kernel"),
             }
         return {
             "permute_q": ("hbm", tok + til, "permute_fwd_kernel"),
             "permute_k": ("hbm", tok + til, "permute_fwd_kernel"),
-            "permute_vt": ("hbm", tok + til, "permute_fwd_t_kernel"),
+            "permute_vt": ("hbm", tok + til, "permute_fwd_t_bf16_kernel"),
             "tripool_score": ("hbm", 2 * tok + 4 * L.total_scores, "tripool_pool_kernel"),
             "select": ("hbm", 4 * L.total_scores + 4 * nnz + 4 * (L.total_tiles + 1),
-                       "select_kernel"),
+                       sel),
             "sparse_attn": ("mfma", self.flops_c, "sparse_attn_fwd_kernel"),
             "permute_o": ("hbm", 2 * tok, "permute_inv_kernel"),
             "map": ("mfma", self.flops_d, "map_stats_kernel"),
@@ -322,11 +334,18 @@ class Bench:
         return wall, per.mean(axis=0), per
 
 
-def cpu_baseline(wl, sparsity: int, budget_s: float = 12.0):
-    """The oracle (as it stands) on whole heads of the same workload, head by
-    head until ``budget_s`` has passed: gather Q/K/V, TripPool + projection +
-    scores, top-k, sparse attention of every query tile, inverse scatter, and
-    the max-pooled map on the head's query-tile subset."""
+def cpu_baseline(wl, sparsity: int, n_heads: int = 2, n_qtiles: int = 32, n_map: int = 4,
+                 seed: int = 0):
+    """The oracle (as it stands) on a seeded sample of the same layer, each
+    part timed and extrapolated linearly to the whole layer.  For each of
+    ``n_heads`` seeded heads: the per-head parts (gather of Q, K, V; TripPool,
+    projection and scores of every tile; the inverse scatter of O), then the
+    top-k and sparse attention of ``n_qtiles`` seeded query tiles, and the
+    max-pooled map of ``n_map`` of the head's seeded subset tiles.  The layer
+    estimate is heads x (per-head parts) + query tiles x (per-query-tile part)
+    + subset tiles x (per-subset-tile part); ``value`` is the layer's FLOPs
+    counted as for the GPU (4 S^2 d per kept pair, 2 S^2 d per map pair: one
+    Q K^T product) over that estimate."""
     import oracle
     import workloads
     from workloads import bf16_to_f64
@@ -334,34 +353,59 @@ def cpu_baseline(wl, sparsity: int, budget_s: float = 12.0):
     T, H, W, S, d = wl.T, cfg.H, cfg.W, cfg.tile_size, cfg.head_dim
     tilings = [oracle.HeadTiling(T, H, W, s) for s in wl.tile_shapes]
     subset = workloads.draw_subset(wl, [t.n for t in tilings])
-    flops, heads = 0.0, 0
-    t0 = time.perf_counter()
-    for h in range(cfg.heads):
+    rng = np.random.default_rng(seed)
+    heads = sorted(int(x) for x in rng.choice(cfg.heads, size=min(n_heads, cfg.heads), replace=False))
+    t_head, t_rows, t_map, rows_done, map_done = 0.0, 0.0, 0.0, 0, 0
+    t_all = time.perf_counter()
+    for h in heads:
         ht = tilings[h]
+        kk = oracle.keep_count(ht.n, sparsity)
+        t0 = time.perf_counter()
         q, k, v = (bf16_to_f64(a[:, h, :]) for a in (wl.q, wl.k, wl.v))
         qp, kp, vp = (oracle.gather(a, T, H, W, ht.shape) for a in (q, k, v))
         w = wl.w[h].astype(np.float64)
-        s = oracle.tile_scores(oracle.project(oracle.tripool(qp, ht.valid, S), w),
-                               oracle.project(oracle.tripool(kp, ht.valid, S), w))
-        kk = oracle.keep_count(ht.n, sparsity)
-        rp, ci = oracle.select_topk(s, kk)
-        o, _ = oracle.sparse_attention(qp, kp, vp, ht.valid, S, rp, ci, cfg.sm_scale)
+        sc = oracle.tile_scores(oracle.project(oracle.tripool(qp, ht.valid, S), w),
+                                oracle.project(oracle.tripool(kp, ht.valid, S), w))
+        t1 = time.perf_counter()
+        rows = np.sort(rng.choice(ht.n, size=min(n_qtiles, ht.n), replace=False))
+        _, ci = oracle.select_topk(sc[rows], kk)
+        counts = np.zeros(ht.n, dtype=np.int64)
+        counts[rows] = kk
+        rp = np.concatenate([[0], np.cumsum(counts)])
+        o, _ = oracle.sparse_attention(qp, kp, vp, ht.valid, S, rp, ci, cfg.sm_scale, q_tiles=rows)
+        t2 = time.perf_counter()
         oracle.scatter(np.nan_to_num(o), T, H, W, ht.shape)
-        oracle.maxpool_map(qp, kp, ht.valid, S, subset[h], cfg.sm_scale)
-        flops += 4.0 * S * S * d * ht.n * kk + 2 * 2.0 * S * S * d * len(subset[h]) * ht.n
-        heads += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+        t3 = time.perf_counter()
+        sub = subset[h][np.sort(rng.choice(len(subset[h]), size=min(n_map, len(subset[h])),
+                                           replace=False))]
+        oracle.maxpool_map(qp, kp, ht.valid, S, sub, cfg.sm_scale)
+        t4 = time.perf_counter()
+        t_head += (t1 - t0) + (t3 - t2)
+        t_rows += t2 - t1
+        t_map += t4 - t3
+        rows_done += len(rows)
+        map_done += len(sub)
+    measured = time.perf_counter() - t_all
+    n_tiles = sum(t.n for t in tilings)
+    n_sub = sum(len(x) for x in subset)
+    est = (t_head / len(heads) * cfg.heads + t_rows / rows_done * n_tiles
+           + t_map / map_done * n_sub)
+    flops = sum(4.0 * S * S * d * t.n * oracle.keep_count(t.n, sparsity) for t in tilings)
+    flops += sum(2.0 * S * S * d * len(subset[h]) * tilings[h].n for h in range(cfg.heads))
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{heads} of {cfg.heads} heads, whole path per head (gather, TripPool/score, "
-                      f"top-k, sparse attention of all query tiles, scatter, map on the head's "
-                      f"{cfg.map_subset_pct}% query-tile subset), {dt:.1f} s, fp64 numpy"}
+    return {"value": flops / est / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "extrapolated": True, "layer_s_extrapolated": est, "sample_s": measured,
+            "sample": f"heads {heads} of {cfg.heads}: per head the gather of Q/K/V, TripPool + "
+                      f"projection + scores of all tiles and the inverse scatter; top-k and "
+                      f"sparse attention of {n_qtiles} seeded query tiles per head; the max-pooled "
+                      f"map of {n_map} of the head's seeded {cfg.map_subset_pct}% subset tiles; "
+                      f"fp64 numpy, {measured:.1f} s, extrapolated linearly to all {cfg.heads} "
+                      f"heads, {n_tiles} query tiles and {n_sub} subset tiles; FLOPs counted as "
+                      f"for the GPU (map: one Q K^T product)"}
 
 
 def sweep():
@@ -460,16 +504,53 @@ def clock_power(launch, seconds: float = 3.0, samples: int = 3):
         return {"error": f"{type(exc).__name__}: {exc}"[:200]}
 
 
+def _say(msg: str) -> None:
+    """Progress on stderr (the JSON line alone goes to stdout)."""
+    print(msg, file=sys.stderr, flush=True)
+
+
+def stage_record(b, per):
+    """Median / p10 / p90 over the timed steps of every stage and of the layer
+    (all stages but the map), from the per-step event times ``per``."""
+    med = {n: float(np.median(per[:, i])) for i, n in enumerate(b.stages)}
+    pct = {n: [float(x) for x in np.percentile(per[:, i], [10, 50, 90])]
+           for i, n in enumerate(b.stages)}
+    layer = per[:, [i for i, n in enumerate(b.stages) if n != "map"]].sum(axis=1)
+    pct["layer"] = [float(x) for x in np.percentile(layer, [10, 50, 90])]
+    pct["step"] = [float(x) for x in np.percentile(per.sum(axis=1), [10, 50, 90])]
+    return med, pct
+
+
+def layer_summary(b, med, wall_ms):
+    """The metric's figures for one timed run of a Bench."""
+    attn = med["sparse_attn"]
+    layer_ms = sum(med[n] for n in b.stages if n != "map")
+    out = {"step_ms_wall": wall_ms, "ms_per_layer": layer_ms,
+           "attn_ms": attn, "attn_tflops": b.flops_c / (attn * 1e-3) / 1e12,
+           "attn_frac_peak": b.flops_c / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "layer_tflops_effective": b.flops_c / (layer_ms * 1e-3) / 1e12,
+           "kept_pairs": b.pairs, "kept_tiles_per_row": sorted(set(b.layer.k_per_head))}
+    if "map" in med and b.flops_d > 0 and med["map"] > 0:
+        out.update({"map_ms": med["map"], "map_tflops": b.flops_d / (med["map"] * 1e-3) / 1e12,
+                    "map_frac_peak": b.flops_d / (med["map"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                    "map_subset_tiles": int(sum(b.n_sub)),
+                    "step_tflops_effective": (b.flops_c + b.flops_d) / (wall_ms * 1e-3) / 1e12})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wan1.3b-480p-81f")
-    ap.add_argument("--sparsity", type=int, default=90)
+    ap.add_argument("--workload", default="long-720p-241f")
+    ap.add_argument("--sparsity", type=int, default=95)
+    ap.add_argument("--warm", action="store_true",
+                    help="time the headline steps with warm caches (no 512 MiB overwrite "
+                         "before each step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
-                    help="skip the 95 %% and 0 %% (dense) context runs")
+                    help="skip every context run (warm cache, 0 %% dense, other layers, ...)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one torch copy of this many MiB (counter calibration)")
     ap.add_argument("--backward", action="store_true",
@@ -500,24 +581,25 @@ def main():
         print(json.dumps({"workload": args.workload, "sparsity_pct": args.sparsity,
                           "backward_ms": ms, "kept_pairs": bb.pairs,
                           "tflops": bb.backward_flops() / (ms * 1e-3) / 1e12,
-                          "frac_peak": bb.backward_flops() / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                          "forward_attn_ms_for_reference": None}))
+                          "frac_peak": bb.backward_flops() / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}))
         return
 
+    t_start = time.perf_counter()
+    _say(f"bench: drawing {args.workload}")
     b = Bench(args.workload, args.sparsity)
-    wall_ms, stage_ms, per = b.run(args.steps, args.warmup)
-    pct = {n: [float(x) for x in np.percentile(per[:, i], [10, 50, 90])]
-           for i, n in enumerate(b.stages)}
-    layer_steps = per[:, [i for i, n in enumerate(b.stages) if n != "map"]].sum(axis=1)
-    pct["layer"] = [float(x) for x in np.percentile(layer_steps, [10, 50, 90])]
+    cfg, L = b.cfg, b.L
+    # cold caches (the primary timing): a 512 MiB buffer is overwritten before
+    # every step, which evicts the L2s and the 256 MiB MALL; the overwrite runs
+    # inside the timed region, so the wall time per step includes it
+    flush = None if args.warm else torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32,
+                                               device="cuda")
+    _say(f"bench: {args.steps} timed steps ({'warm' if args.warm else 'cold'} caches)")
+    wall_ms, _, per = b.run(args.steps, args.warmup, flush=flush)
+    st, pct = stage_record(b, per)
     valid_c = b.valid_flops_c()
-    names = b.stages
-    st = dict(zip(names, [float(x) for x in stage_ms]))
-    layer_ms = sum(st[n] for n in names if n != "map")
-    attn_ms = st["sparse_attn"]
+    layer_ms = sum(st[n] for n in b.stages if n != "map")
     total_flops = b.flops_c + b.flops_d
     value = total_flops / (wall_ms * 1e-3) / 1e12
-    cfg, L = b.cfg, b.L
 
     kernels = {}
     for name, (bound, work, kname) in b.kernel_work().items():
@@ -534,96 +616,107 @@ def main():
     dominant = max(kernels, key=lambda n: kernels[n]["avg_launch_ms"])
     roofline = dict(kernels[dominant])
     roofline["stage"] = dominant
+    roofline["timing"] = "median event-timed launch over the timed steps, " + (
+        "warm caches" if args.warm else "cold caches")
 
     context = {}
     if not args.no_context:
-        # the distillation step on this step's map and scores: KL rows, then
-        # the projection gradients (2 S = phi phi^T backward products and the
-        # 3d x d_e weight gradients per head)
+        _say("bench: warm-cache steps")
+        w_ms, _, wper = b.run(args.steps, 2)
+        wmed, wpct = stage_record(b, wper)
+        context["warm_cache"] = dict(layer_summary(b, wmed, w_ms), stage_ms=wmed,
+                                     stage_ms_p10_p50_p90=wpct)
+        if flush is None:
+            flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        # the same kernel with every tile kept (0 % sparsity: dense attention)
+        _say("bench: 0 % (dense) on the same layer")
+        c = Bench(args.workload, 0, wl=b.wl)
+        c_ms, _, cper = c.run(3, 1, with_map=False, flush=flush)
+        cmed, _ = stage_record(c, cper)
+        context["sparsity_0"] = layer_summary(c, cmed, c_ms)
+        context["attn_speedup_vs_dense"] = cmed["sparse_attn"] / st["sparse_attn"]
+        context["density"] = b.pairs / c.pairs
+        del c
+        torch.cuda.empty_cache()
+        # one call per method step (tile-order O, then the inverse permutation)
+        _say("bench: one call per method step")
+        u = Bench(args.workload, args.sparsity, wl=b.wl, fused=False)
+        u_ms, _, uper = u.run(max(5, args.steps // 4), 2, flush=flush)
+        umed, _ = stage_record(u, uper)
+        context["unfused"] = {"ms_per_layer": sum(umed[n] for n in u.stages if n != "map"),
+                              "stage_ms": {n: umed[n] for n in u.stages if n != "map"}}
+        del u
+        torch.cuda.empty_cache()
+        # the distillation step and the attention backward of this layer
+        _say("bench: distillation step and attention backward")
         dms = b.time_distill()
         n_sub = int(sum(b.n_sub))
         de = b.layer.d_e
-        flops = (2.0 * 2 * de * sum(b.n_sub[h] * L.n(h) for h in range(L.num_heads))
-                 + 2.0 * 3 * cfg.head_dim * de * (n_sub + L.total_tiles))
-        context["distill"] = {"ms": dms, "subset_tiles": n_sub, "gflop": flops / 1e9,
-                              "tflops": flops / (dms * 1e-3) / 1e12}
-        # attention backward of this step's forward
+        dfl = (2.0 * 2 * de * sum(b.n_sub[h] * L.n(h) for h in range(L.num_heads))
+               + 2.0 * 3 * cfg.head_dim * de * (n_sub + L.total_tiles))
+        context["distill"] = {"ms": dms, "subset_tiles": n_sub, "gflop": dfl / 1e9,
+                              "tflops": dfl / (dms * 1e-3) / 1e12}
         bms = b.time_backward()
         context["backward"] = {
             "ms": bms, "tflops": b.backward_flops() / (bms * 1e-3) / 1e12,
             "frac_peak": b.backward_flops() / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "flops_per_pair": "10 S^2 d (S recomputed once, dP, dQ, dK, dV)"}
-        # head-aware tiling search over the four 128-slot shapes on this layer:
-        # full attention once, then the fused layer and the per-head error for
-        # each shape.  Wall time of the second of two calls (buffers allocated
-        # per candidate included); the first call also pays the allocator's
-        # first requests for these sizes
-        import tile_sparse_attention_head_amd as V
-        search_ms = []
-        for _ in range(2):
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            chosen, errs, ref = V.search_tile_shapes(b.wl.T, cfg.H, cfg.W, cfg.head_dim,
-                                                     cfg.tile_size, b.q, b.k, b.v, b.w, b.w,
-                                                     cfg.sm_scale, args.sparsity)
-            torch.cuda.synchronize()
-            search_ms.append((time.perf_counter() - t0) * 1e3)
-        rel = (errs / ref).sqrt().cpu().numpy()
-        context["tiling_search"] = {
-            "ms": search_ms[1], "first_call_ms": search_ms[0],
-            "candidates": [list(c) for c in V.tiling_search.SHAPES_128],
-            "chosen": [list(c) for c in chosen],
-            "rel_error_per_candidate_median_over_heads": [float(np.median(r)) for r in rel]}
         torch.cuda.empty_cache()
-        for s in (95, 0):
-            if s == args.sparsity:
-                continue
-            # the same step as the headline run (map included), so the
-            # stages see the same cache and clock conditions
-            c = Bench(args.workload, s)
-            w2, sm2, _ = c.run(max(10, args.steps // 2), 3)
-            d2 = dict(zip(names, [float(x) for x in sm2]))
-            a_ms = d2["sparse_attn"]
-            context[f"sparsity_{s}"] = {
-                "ms_per_layer": sum(d2[n] for n in names if n != "map"),
-                "attn_ms": a_ms, "attn_tflops": c.flops_c / (a_ms * 1e-3) / 1e12,
-                "attn_frac_peak": c.flops_c / (a_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                "kept_pairs": c.pairs}
-            del c
-            torch.cuda.empty_cache()
-        if "sparsity_0" in context:
-            context["attn_speedup_vs_dense"] = context["sparsity_0"]["attn_ms"] / attn_ms
-            context["density"] = b.pairs / context["sparsity_0"]["kept_pairs"]
-        # the same layer one method step per call (tile-order O, then the
-        # inverse permutation): what the fused calls save
-        u = Bench(args.workload, args.sparsity, fused=False)
-        _, smu, _ = u.run(max(10, args.steps // 2), 3)
-        du = dict(zip(u.stages, [float(x) for x in smu]))
-        context["unfused"] = {"ms_per_layer": sum(du[n] for n in u.stages if n != "map"),
-                              "stage_ms": {n: du[n] for n in u.stages if n != "map"}}
-        del u
-        torch.cuda.empty_cache()
-        # cold caches: a 512 MiB buffer is overwritten before every step, which
-        # evicts L2 and MALL (256 MiB) between steps
-        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
-        _, smc, _ = b.run(max(3, args.steps // 2), 1, flush=flush)
-        dc = dict(zip(names, [float(x) for x in smc]))
-        context["cold_cache"] = {"ms_per_layer": sum(dc[n] for n in names if n != "map"),
-                                 "attn_ms": dc["sparse_attn"], "map_ms": dc["map"]}
-        del flush
-        torch.cuda.empty_cache()
-        # the clock the attention kernel runs at, and the power it draws
+        # clocks and power while the attention kernel, then the map, run back to back
+        _say("bench: clocks and power")
         context["clock_power_under_attention"] = clock_power(
             lambda: b.layer.attend_tokens(b.cfg.sm_scale, b.out, with_lse=True))
         context["clock_power_under_map"] = clock_power(
             lambda: b.layer.maxpool_map(b.q_tiles, b.cfg.sm_scale, b.map_lse, b.map_out))
-        # the attention kernel's fraction of the MFMA peak at the clock the
-        # power limit leaves it (the published peak assumes 2.4 GHz)
-        cp = context["clock_power_under_attention"]
+        cp = context["clock_power_under_attention"] if dominant == "sparse_attn" else \
+            context["clock_power_under_map"]
         if roofline.get("unit") == "TFLOP/s" and isinstance(cp, dict) and cp.get("gfx_mhz_median"):
             roofline["measured_clock_mhz"] = cp["gfx_mhz_median"]
             roofline["frac_at_measured_clock"] = (
                 roofline["achieved"] / (roofline["peak"] * cp["gfx_mhz_median"] / 2400.0))
+        # the other layers of the metric, same step, cold caches
+        others = {}
+        for name, sp in (("wan1.3b-480p-81f", 90), ("wan1.3b-480p-81f", 95),
+                         ("waver12b-720p-121f", 90), ("waver12b-720p-121f", 95)):
+            if name == args.workload and sp == args.sparsity:
+                continue
+            _say(f"bench: context layer {name} at {sp} %")
+            wl = others.get(name, {}).get("_wl")
+            o = Bench(name, sp, wl=wl)
+            o_ms, _, oper = o.run(10, 3, flush=flush)
+            omed, _ = stage_record(o, oper)
+            rec = others.setdefault(name, {"_wl": o.wl})
+            rec[f"sparsity_{sp}"] = dict(layer_summary(o, omed, o_ms), stage_ms=omed)
+            if name == "wan1.3b-480p-81f" and sp == 90:
+                # head-aware tiling search over the four 128-slot shapes on this
+                # layer (second of two calls; the first also pays the
+                # allocator's first requests for these sizes)
+                import tile_sparse_attention_head_amd as V
+                search_ms = []
+                for _ in range(2):
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    chosen, errs, ref = V.search_tile_shapes(
+                        o.wl.T, o.cfg.H, o.cfg.W, o.cfg.head_dim, o.cfg.tile_size, o.q, o.k, o.v,
+                        o.w, o.w, o.cfg.sm_scale, sp)
+                    torch.cuda.synchronize()
+                    search_ms.append((time.perf_counter() - t0) * 1e3)
+                rel = (errs / ref).sqrt().cpu().numpy()
+                context["tiling_search"] = {
+                    "workload": name, "sparsity_pct": sp, "ms": search_ms[1],
+                    "first_call_ms": search_ms[0],
+                    "candidates": [list(x) for x in V.tiling_search.SHAPES_128],
+                    "chosen": [list(x) for x in chosen],
+                    "rel_error_per_candidate_median_over_heads": [float(np.median(r)) for r in rel]}
+            del o
+            torch.cuda.empty_cache()
+        for rec in others.values():
+            rec.pop("_wl", None)
+        context["other_layers"] = others
+        context["context_s"] = time.perf_counter() - t_start
+    if flush is not None:
+        del flush
+        torch.cuda.empty_cache()
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1024 * 1024 // 4
@@ -633,6 +726,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    if not args.no_cpu_baseline:
+        _say("bench: CPU oracle sample")
     cpu = None if args.no_cpu_baseline else cpu_baseline(b.wl, args.sparsity)
 
     line = {
@@ -646,14 +741,19 @@ def main():
             "tokens": L.tokens, "heads": L.num_heads, "head_dim": cfg.head_dim,
             "tile_size": cfg.tile_size, "tile_shapes": sorted(set(b.wl.tile_shapes)),
             "sparsity_pct": args.sparsity, "kept_tiles_per_row": sorted(set(b.layer.k_per_head)),
-            "map_subset_tiles": int(sum(b.n_sub)), "parallelism": "single GPU"},
+            "map_subset_tiles": int(sum(b.n_sub)), "parallelism": "single GPU",
+            "timing": ("warm caches" if args.warm else
+                       "cold caches: a 512 MiB buffer is overwritten before every step (inside "
+                       "the timed region)") +
+                      "; value = (4 S^2 d per kept pair + 2 S^2 d per map pair) / ms_per_step; "
+                      "stage times are medians of HIP events on the kernels' stream"},
         "ms_per_layer": layer_ms,
         "layer_tflops_effective": b.flops_c / (layer_ms * 1e-3) / 1e12,
         "stage_ms": st,
         "stage_ms_p10_p50_p90": pct,
         "attn_valid_tokens": {
             "flops": valid_c, "padding_fraction": 1.0 - valid_c / b.flops_c,
-            "tflops": valid_c / (attn_ms * 1e-3) / 1e12},
+            "tflops": valid_c / (st["sparse_attn"] * 1e-3) / 1e12},
         "roofline": roofline,
         "kernels": kernels,
         "context": context,
