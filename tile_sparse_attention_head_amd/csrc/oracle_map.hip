@@ -24,6 +24,8 @@
 // queries, K copied HBM -> LDS in 64-key steps two steps ahead, and per step
 // one hand-laid block interleaving the MFMAs of QK(s+1) with the statistics
 // of step s.  Padding keys are masked by seeding the accumulator with -inf.
+#include <type_traits>
+
 #include "attn_common.hpp"
 
 namespace veda {
@@ -230,25 +232,48 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
   if (hf == 0) ml[((int64_t)sub * chunks + c) * S + qslot] = make_float2(m_run, l_tot);
 }
 
-// Pass 2.  Workgroup (subset entry, block of 32 key tiles), 4 waves.  Lane l
-// of every wave holds query slots 2l, 2l+1 (S = 128) or l (S = 64): merges
-// the chunk partials into lse2, then wave w takes key tiles jb + w, jb + w +
-// 4, ... of the block and reduces max over real slots of exp2(rowmax - lse2)
-// across the wave.  Block 0 also writes lse.
-constexpr int kReduceTiles = 32;
+// Maximum of v over the 64 lanes of the wave, in every lane: within each
+// quad and row of 16 by DPP (swap neighbours, swap pairs, rotate by 4 and 8),
+// then across rows by exchanging with lane l ^ 16 and l ^ 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_max_all(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x124>(v));   // row_ror:4
+  v = fmaxf(v, dpp_f32<0x128>(v));   // row_ror:8
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  return swap32_max(v);
+}
+
+// Pass 2.  Workgroup (subset entry, block of tb key tiles), 4 waves.  Lane l
+// of every wave holds query slots 2l, 2l+1 (S = 128) or l (S = 64): it merges
+// the chunk partials of its slots into lse2 once, then wave w takes key tiles
+// jb + w, jb + w + 4, ... of the block, kAhead at a time.  Per key tile the
+// wave reads the tile's S row maxima (one 4*QPL-byte load per lane), takes
+// the largest rowmax - lse2 over the tile's real rows with a wave reduction
+// (the kAhead reductions interleaved), and writes exp2 of it: exp2 is
+// monotone, so this is the largest probability of the block.  Block 0 also
+// writes lse.
+constexpr int kAhead = 8;
 constexpr int kMaxChunks = 16;   // map_chunks() never returns more
 
 template <int S>
 __global__ __launch_bounds__(256) void map_reduce_kernel(
-    DevLayout L, const int32_t* __restrict__ q_tiles, int chunks,
+    DevLayout L, const int32_t* __restrict__ q_tiles, int chunks, int tb,
     const float* __restrict__ rowmax, const float2* __restrict__ ml, float* __restrict__ lse,
     float* __restrict__ map) {
   constexpr int QPL = S / 64;   // query slots per lane
+  using Vec = typename std::conditional<QPL == 2, float2, float>::type;
   const int sub = blockIdx.y;
-  const int jb = blockIdx.x * kReduceTiles;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int jb = blockIdx.x * tb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* mrow = map + (int64_t)sub * L.max_tiles;
-  const int jend = min(jb + kReduceTiles, (int)L.max_tiles);
+  const int jend = min(jb + tb, (int)L.max_tiles);
   const int64_t g = q_tiles[sub];
   if (g < 0 || g >= L.tile_off[L.heads]) {
     for (int j = jb + tid; j < jend; j += 256) mrow[j] = 0.f;
@@ -257,9 +282,10 @@ __global__ __launch_bounds__(256) void map_reduce_kernel(
   const int h = head_of_tile(L, g);
   const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
   const TileExtent eq = tile_extent(L, h, (int)(g - L.tile_off[h]));
+  for (int j = max(jb, n_h) + tid; j < jend; j += 256) mrow[j] = 0.f;   // beyond the head
 
-  // every load of the workgroup goes out first: the chunk partials of this
-  // lane's slots and the row maxima of its key tiles
+  // lse2 of this lane's slots; -inf for a padding slot, so that it never
+  // wins.  Every partial is loaded first (predicated, all in flight at once).
   float2 part[QPL][kMaxChunks];
 #pragma unroll
   for (int u = 0; u < QPL; ++u)
@@ -267,21 +293,10 @@ __global__ __launch_bounds__(256) void map_reduce_kernel(
     for (int c = 0; c < kMaxChunks; ++c)
       part[u][c] = c < chunks ? ml[((int64_t)sub * chunks + c) * S + QPL * lane + u]
                               : make_float2(-INFINITY, 0.f);
-  const float* rm = rowmax + (int64_t)sub * L.max_tiles * S + QPL * lane;
-  constexpr int PER_WAVE = kReduceTiles / 4;
-  float x[PER_WAVE][QPL];
-#pragma unroll
-  for (int t = 0; t < PER_WAVE; ++t) {
-    const int j = jb + wave + 4 * t;
-#pragma unroll
-    for (int u = 0; u < QPL; ++u) x[t][u] = j < n_h ? rm[(int64_t)j * S + u] : 0.f;
-  }
-  float lse2[QPL];
-  bool real[QPL];
+  float neg_lse[QPL];
 #pragma unroll
   for (int u = 0; u < QPL; ++u) {
     const int qs = QPL * lane + u;
-    real[u] = eq.slot_real(qs);
     float M = -INFINITY;
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, part[u][c].x);
@@ -291,19 +306,36 @@ __global__ __launch_bounds__(256) void map_reduce_kernel(
       for (int c = 0; c < kMaxChunks; ++c)
         if (part[u][c].y > 0.f) Ls += part[u][c].y * exp2_(part[u][c].x - M);
     }
-    lse2[u] = Ls > 0.f ? M + __log2f(Ls) : -INFINITY;
-    if (blockIdx.x == 0 && wave == 0) lse[(int64_t)sub * S + qs] = lse2[u] * 0.69314718055994531f;
+    const float lse2 = Ls > 0.f ? M + __log2f(Ls) : -INFINITY;
+    if (blockIdx.x == 0 && wave == 0) lse[(int64_t)sub * S + qs] = lse2 * 0.69314718055994531f;
+    // a real row always has a real key, so lse2 is finite for it
+    neg_lse[u] = eq.slot_real(qs) && lse2 != -INFINITY ? -lse2 : -INFINITY;
   }
+  const float* rm = rowmax + (int64_t)sub * L.max_tiles * S + QPL * lane;
+  const int jlast = min(jend, n_h);
+  // tiles jb + wave + 4t of this block that lie in the head
+  const int nt = jlast > jb + wave ? (jlast - (jb + wave) + 3) / 4 : 0;
+  for (int t0 = 0; t0 < nt; t0 += kAhead) {
+    Vec x[kAhead];
 #pragma unroll
-  for (int t = 0; t < PER_WAVE; ++t) {
-    const int j = jb + wave + 4 * t;
-    float v = 0.f;
+    for (int a = 0; a < kAhead; ++a) {
+      const int j = jb + wave + 4 * min(t0 + a, nt - 1);   // past the end: re-read the last
+      x[a] = *reinterpret_cast<const Vec*>(rm + (int64_t)j * S);
+    }
+    float v[kAhead];
 #pragma unroll
-    for (int u = 0; u < QPL; ++u)
-      if (j < n_h && real[u] && lse2[u] != -INFINITY) v = fmaxf(v, exp2_(x[t][u] - lse2[u]));
+    for (int a = 0; a < kAhead; ++a) {
+      if constexpr (QPL == 2) v[a] = fmaxf(x[a].x + neg_lse[0], x[a].y + neg_lse[1]);
+      else v[a] = x[a] + neg_lse[0];
+    }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    if (lane == 0 && j < jend) mrow[j] = v;
+    for (int a = 0; a < kAhead; ++a) v[a] = wave_max_all(v[a]);
+    if (lane < kAhead) {
+      float w = v[0];
+#pragma unroll
+      for (int a = 1; a < kAhead; ++a) w = lane == a ? v[a] : w;
+      if (t0 + lane < nt) mrow[jb + wave + 4 * (t0 + lane)] = w == -INFINITY ? 0.f : exp2_(w);
+    }
   }
 }
 
@@ -365,17 +397,20 @@ int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm
   const int64_t rm = ((n_sub * (int64_t)L.max_tiles * L.S * 4) + 255) / 256 * 256;
   float2* ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(workspace) + rm);
   const unsigned grid1 = (unsigned)(n_sub * chunks);
-  const dim3 grid2((unsigned)((L.max_tiles + kReduceTiles - 1) / kReduceTiles), (unsigned)n_sub);
+  // pass 2: blocks of 32..256 key tiles, about 4096 workgroups in all
+  int64_t tb = ((int64_t)L.max_tiles * n_sub / 4096 + 31) / 32 * 32;
+  tb = tb < 32 ? 32 : (tb > 256 ? 256 : tb);
+  const dim3 grid2((unsigned)((L.max_tiles + tb - 1) / tb), (unsigned)n_sub);
   if (L.d == 128) {
     hipLaunchKernelGGL((map_stats_kernel<128, 128>), dim3(grid1), dim3(256), 0, s, L,
                        (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, chunks, rowmax, ml);
     hipLaunchKernelGGL((map_reduce_kernel<128>), grid2, dim3(256), 0, s, L, q_tiles, chunks,
-                       rowmax, ml, lse, map);
+                       (int)tb, rowmax, ml, lse, map);
   } else {
     hipLaunchKernelGGL((map_stats_kernel<64, 64>), dim3(grid1), dim3(128), 0, s, L,
                        (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, chunks, rowmax, ml);
     hipLaunchKernelGGL((map_reduce_kernel<64>), grid2, dim3(256), 0, s, L, q_tiles, chunks,
-                       rowmax, ml, lse, map);
+                       (int)tb, rowmax, ml, lse, map);
   }
   return launch_status();
 }
