@@ -90,9 +90,24 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
   uint32_t koff[KB::PER_WAVE];
   KB::offsets(koff, wave, lane);
   auto k_off = [&](int t) { return (uint32_t)((j0 + t / SPT) * TILE + (t % SPT) * P::KSTEP); };
-  int qcut = 0;   // cut of the tile whose logits are computed next
+  // Grid coordinates and cut of the key tile whose logits are computed next.
+  // Steps visit the chunk's tiles in index order, so the coordinates advance
+  // one tile at a time (no division per tile); a tile's cut marks the axes
+  // along which it is the last, partial tile of the grid.
+  const int nH = L.grid[h][1], nW = L.grid[h][2], nT = L.grid[h][0];
+  const bool part_t = L.T % L.shape[h][0] != 0, part_h = L.H % L.shape[h][1] != 0,
+             part_w = L.W % L.shape[h][2] != 0;
+  int kw = j0 % nW, kh = (j0 / nW) % nH, kt = j0 / (nW * nH);
+  int qcut = 0;
   auto bias_of = [&](int t) -> const f32x4* {
-    if (t % SPT == 0) qcut = cut_of(tile_extent(L, h, j0 + t / SPT));
+    if (t % SPT == 0) {
+      if (t > 0 && ++kw == nW) {
+        kw = 0;
+        if (++kh == nH) { kh = 0; ++kt; }
+      }
+      qcut = (part_t && kt == nT - 1 ? 4 : 0) | (part_h && kh == nH - 1 ? 2 : 0) |
+             (part_w && kw == nW - 1 ? 1 : 0);
+    }
     return &btab.v[qcut][t % SPT][0][hf][0];
   };
 
