@@ -169,11 +169,16 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     // copy is in flight at this point).
     if ((s + 2) / SPT - wbase >= 64) load_window((s + 2) / SPT - 2);
     const int es = entry(s);
-    const uint32_t kgs = s + 2 < N ? k_off(entry(s + 2), s + 2) : k_off(es, s);
+    // step s+2, or s itself when there is none (its K rounds then re-copy K(s)
+    // into its own, no longer read, slot); a scalar select, not a branch
+    const int t2 = s + 2 < N ? s + 2 : s;
+    const int e2 = entry(t2);
+    const uint32_t kgs = k_off(e2, t2);
     const uint32_t vgs = v_off(es, s);
     // mask rows of step s+2, loaded into the logits registers of step s once
-    // its softmax has read them (the last slots below)
-    const f32x4* bias2 = bias_of(s + 2 < N ? entry(s + 2) : 0, s + 2);
+    // its softmax has read them (the last slots below); with no step s+2 they
+    // are valid rows that nothing reads
+    const f32x4* bias2 = bias_of(e2, s + 2);
     unsigned char* kdst = PAR ? k1 : k0;
     unsigned char* vdst = PAR ? v1 : v0;
     constexpr int RW = KB::PER_WAVE + VB::PER_WAVE;
@@ -258,7 +263,10 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
           psum1 += e[el0 + 1];
           pcur[2 * b + (ii >> 3)][ii & 7] = (__bf16)e[el0];
           pcur[2 * b + (ii >> 3)][(ii & 7) + 1] = (__bf16)e[el0 + 1];
-          asm volatile("" : "+v"(psum0), "+v"(psum1));
+          // the bf16 conversion stays in this slot: left to itself the
+          // compiler sinks it to the next step, whose PV reads it, where it
+          // runs before the first product with nothing to overlap
+          asm volatile("" : "+v"(psum0), "+v"(psum1), "+v"(pcur[2 * b + (ii >> 3)]));
         }
       });
       if constexpr (i == 5 + (15 * (NSLOT - 7)) / 16 + 1) load_bias(scur, bias2);
