@@ -36,8 +36,8 @@ peak, data-movement kernels in GB/s of algorithmic bytes against the HBM
 peak, with ``traffic`` the HBM bytes per launch read from the committed
 rocprofv3 counter summaries under profiles/ (null when the kernel's sources
 changed since).  ``cpu_baseline`` times the CPU oracle on a seeded sample of
-the same layer (2 heads x 32 query tiles plus 4 map tiles per head) and
-extrapolates it to the layer.
+the same layer (4 heads x 32 query tiles plus 8 map tiles per head, about
+10 s of CPU work) and extrapolates it to the layer.
 
 Context runs (``context``, none of it in ``value``): the same steps with warm
 caches; the same layer at 0 % sparsity (dense attention, the same kernel) and
@@ -334,7 +334,7 @@ class Bench:
         return wall, per.mean(axis=0), per
 
 
-def cpu_baseline(wl, sparsity: int, n_heads: int = 2, n_qtiles: int = 32, n_map: int = 4,
+def cpu_baseline(wl, sparsity: int, n_heads: int = 4, n_qtiles: int = 32, n_map: int = 8,
                  seed: int = 0):
     """The oracle (as it stands) on a seeded sample of the same layer, each
     part timed and extrapolated linearly to the whole layer.  For each of
