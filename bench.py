@@ -43,8 +43,9 @@ Context runs (``context``, none of it in ``value``): the same steps with warm
 caches; the same layer at 0 % sparsity (dense attention, the same kernel) and
 the speed-up over it; the layer one call per method step; the distillation
 step and the attention backward; GPU clocks and socket power (amd-smi) while
-the attention and the map kernels run back to back; the Wan-1.3B-like and
-Waver-12B-like layers at 90 % and 95 %; and the head-aware tiling search on
+the attention and the map kernels run back to back; the tiny layer at 50 %,
+the Wan-1.3B-like and Waver-12B-like layers at 90 % and 95 % and the
+Wan-14B-like layer at 95 %; and the head-aware tiling search on
 the Wan-1.3B-like layer.  With --gpus above 1 the benchmark refuses: this path
 runs on one GPU (heads shard across GPUs without any exchange inside the
 path).
@@ -676,8 +677,9 @@ def main():
                 roofline["achieved"] / (roofline["peak"] * cp["gfx_mhz_median"] / 2400.0))
         # the other layers of the metric, same step, cold caches
         others = {}
-        for name, sp in (("wan1.3b-480p-81f", 90), ("wan1.3b-480p-81f", 95),
-                         ("waver12b-720p-121f", 90), ("waver12b-720p-121f", 95)):
+        for name, sp in (("tiny", 50), ("wan1.3b-480p-81f", 90), ("wan1.3b-480p-81f", 95),
+                         ("wan14b-720p-81f", 95), ("waver12b-720p-121f", 90),
+                         ("waver12b-720p-121f", 95)):
             if name == args.workload and sp == args.sparsity:
                 continue
             _say(f"bench: context layer {name} at {sp} %")
