@@ -24,9 +24,12 @@
 // consecutive LDS, and each lane picks the HBM chunk that must land at its
 // LDS position.  Rows are padded by 16 bytes (see StepBuf).
 //
-// Padding key slots of boundary tiles are masked by seeding the S^T
-// accumulator with 0 or -inf per key slot (see BiasTable), so masking costs
-// no vector instruction.
+// Padding key slots of boundary tiles are masked with a row of 0 / -inf per
+// key slot (see BiasTable).  Only boundary tiles need it: a full tile's
+// products start from an inline zero accumulator and read no mask row, so
+// the LDS carries operands alone on most steps.  The map seeds the
+// accumulator of a boundary tile with its mask row (no vector instruction);
+// the attention kernel adds it to the logits of a boundary step.
 #pragma once
 
 #include <type_traits>
@@ -220,6 +223,21 @@ __device__ __forceinline__ void load_bias(f32x16 (&acc)[2], const f32x4* bp) {
       acc[b][4 * c + 1] = x[1];
       acc[b][4 * c + 2] = x[2];
       acc[b][4 * c + 3] = x[3];
+    }
+}
+
+// Add the mask rows bp to a step's two S^T accumulators (logits computed
+// from a zero start).
+__device__ __forceinline__ void add_bias(f32x16 (&acc)[2], const f32x4* bp) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 x = bp[b * 8 + c];
+      acc[b][4 * c + 0] += x[0];
+      acc[b][4 * c + 1] += x[1];
+      acc[b][4 * c + 2] += x[2];
+      acc[b][4 * c + 3] += x[3];
     }
 }
 

@@ -99,7 +99,8 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
              part_w = L.W % L.shape[h][2] != 0;
   int kw = j0 % nW, kh = (j0 / nW) % nH, kt = j0 / (nW * nH);
   int qcut = 0;
-  auto bias_of = [&](int t) -> const f32x4* {
+  // cut of the tile of step t (called once per step, in order)
+  auto cut_at = [&](int t) -> int {
     if (t % SPT == 0) {
       if (t > 0 && ++kw == nW) {
         kw = 0;
@@ -108,8 +109,9 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
       qcut = (part_t && kt == nT - 1 ? 4 : 0) | (part_h && kh == nH - 1 ? 2 : 0) |
              (part_w && kw == nW - 1 ? 1 : 0);
     }
-    return &btab.v[qcut][t % SPT][0][hf][0];
+    return qcut;
   };
+  auto bias_of = [&](int t) -> const f32x4* { return &btab.v[qcut][t % SPT][0][hf][0]; };
 
   float m_run = -INFINITY, l_run = 0.f, tmax = -INFINITY;
   float* rm_row = rowmax + ((int64_t)sub * L.max_tiles + j0) * S + qslot;
@@ -117,15 +119,19 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
 
   // One step s: statistics of step s and, in the same hand-laid block,
   // S^T(s+1) = K(s+1) Q^T, with the copy of K(s+2) spread over the slots.
-  auto step = [&](auto has_qk, auto par, int s) {
+  // ZS: the tile of step s+1 has no padding key, so its mask rows are all
+  // zero; its products then start from an inline zero accumulator instead of
+  // reading the rows from LDS.
+  auto step = [&](auto has_qk, auto par, auto zero_seed, int s) __attribute__((always_inline)) {
     constexpr bool QK = decltype(has_qk)::value;
     constexpr int PAR = decltype(par)::value;
+    constexpr bool ZS = decltype(zero_seed)::value;
     f32x16 (&scur)[2] = PAR ? sB : sA;
     f32x16 (&snext)[2] = PAR ? sA : sB;
     const unsigned char* ksrc = PAR ? k0 : k1;
     unsigned char* kdst = PAR ? k1 : k0;
 
-    if constexpr (QK) load_bias(snext, bias_of(s + 1));
+    if constexpr (QK && !ZS) load_bias(snext, bias_of(s + 1));
     // K(s+2) over K(s); with no step s+2 the rounds re-copy K(s) into its
     // own, no longer read, slot
     const uint32_t kgs = s + 2 < N ? k_off(s + 2) : k_off(s);
@@ -156,7 +162,10 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
       });
       if constexpr (QK) {
         if constexpr (i + LA < NSLOT) opnd[(i + LA) % (LA + 1)] = operand(i + LA);
-        snext[i & 1] = mfma32(opnd[i % (LA + 1)], qr[i >> 1], snext[i & 1]);
+        if constexpr (ZS && i < 2)
+          snext[i & 1] = mfma32(opnd[i % (LA + 1)], qr[i >> 1], f32x16{});
+        else
+          snext[i & 1] = mfma32(opnd[i % (LA + 1)], qr[i >> 1], snext[i & 1]);
       }
       // statistics of step s: row maximum in slots 0..4, then the elements
       if constexpr (i < 4) {
@@ -218,12 +227,18 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
   using F = std::false_type;
   using Z = std::integral_constant<int, 0>;
   using O1 = std::integral_constant<int, 1>;
+  // a step with products, in the variant its next tile's cut asks for
+  auto qk_step = [&](auto par, int s) __attribute__((always_inline)) {
+    if (cut_at(s + 1) == 0) step(T{}, par, T{}, s);
+    else step(T{}, par, F{}, s);
+  };
   if (N > 0) {
     KB::copy(krs, k_off(0), k0, koff, wave);
     if (N > 1) KB::copy(krs, k_off(1), k1, koff, wave);
     build_bias_table<SPT>(btab, L, h, tid, 2 * S);
     wait_all();
     __syncthreads();
+    cut_at(0);
     load_bias(sA, bias_of(0));
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -233,15 +248,15 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // k0 free
     int s = 0;
     for (; s + 1 <= N - 2; s += 2) {
-      step(T{}, Z{}, s);
-      step(T{}, O1{}, s + 1);
+      qk_step(Z{}, s);
+      qk_step(O1{}, s + 1);
     }
     if (s <= N - 2) {
-      step(T{}, Z{}, s);
+      qk_step(Z{}, s);
       ++s;
     }
-    if (s & 1) step(F{}, O1{}, s);
-    else step(F{}, Z{}, s);
+    if (s & 1) step(F{}, O1{}, F{}, s);
+    else step(F{}, Z{}, F{}, s);
   }
   const float l_tot = swap32_sum(l_run);
   if (hf == 0) ml[((int64_t)sub * chunks + c) * S + qslot] = make_float2(m_run, l_tot);

@@ -21,10 +21,11 @@
 // V^T slots and the mask table take 74 KiB, so two workgroups share a CU and
 // the two waves on a SIMD come from different, unsynchronised workgroups.
 //
-// Per logit: padding keys of boundary tiles start their accumulation at -inf
-// (the S^T accumulator is seeded from a per-workgroup mask table), online
-// softmax in base 2 with sm_scale*log2(e) folded into one FMA, P rounded to
-// bf16, f32 accumulation.  The running maximum is raised only when a new
+// Per logit: the products start from zero, and the padding keys of a
+// boundary tile (or of an entry outside the head) get -inf added from a
+// per-workgroup mask table before the softmax, in a uniform branch that full
+// tiles skip; online softmax in base 2 with sm_scale*log2(e) folded into one
+// FMA, P rounded to bf16, f32 accumulation.  The running maximum is raised only when a new
 // logit exceeds it by more than 2^8, so the accumulator is rescaled rarely;
 // the result is the same softmax (numerator and denominator share one
 // reference).  The CSR row sits in one register, 64 entries at a time (lane
@@ -175,16 +176,15 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     const int e2 = entry(t2);
     const uint32_t kgs = k_off(e2, t2);
     const uint32_t vgs = v_off(es, s);
-    // mask rows of step s+2, loaded into the logits registers of step s once
-    // its softmax has read them (the last slots below); with no step s+2 they
-    // are valid rows that nothing reads
-    const f32x4* bias2 = bias_of(e2, s + 2);
     unsigned char* kdst = PAR ? k1 : k0;
     unsigned char* vdst = PAR ? v1 : v0;
     constexpr int RW = KB::PER_WAVE + VB::PER_WAVE;
     // the addresses come from scalar loads: have them land before the slots,
     // whose LDS waits then count the operand reads alone
     asm volatile("" :: "s"(kgs), "s"(vgs));
+    // padding keys of step s's tile (rare: boundary tiles and entries outside
+    // the head) get their mask rows added to the logits before the softmax
+    if (es >> 16) add_bias(scur, bias_of(es, s));
 
     constexpr int LA = 3;          // operand reads run LA slots ahead of their MFMA
     constexpr int NSLOT = D / 4;   // D/8 QK and D/8 PV products
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
       if constexpr (has_mfma(i)) {
         constexpr int j = i >> 1;
         if constexpr (i & 1) oacc[j % DB] = mfma32(opnd[i % (LA + 1)], pprev[j / DB], oacc[j % DB]);
-        else snext[j & 1] = mfma32(opnd[i % (LA + 1)], qr[j >> 1], snext[j & 1]);
+        else snext[j & 1] = mfma32(opnd[i % (LA + 1)], qr[j >> 1], j < 2 ? f32x16{} : snext[j & 1]);
       }
       // softmax(s): row maximum in slots 0..4, then the elements
       if constexpr (i < 4) {
@@ -269,7 +269,6 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
           asm volatile("" : "+v"(psum0), "+v"(psum1), "+v"(pcur[2 * b + (ii >> 3)]));
         }
       });
-      if constexpr (i == 5 + (15 * (NSLOT - 7)) / 16 + 1) load_bias(scur, bias2);
       __builtin_amdgcn_sched_barrier(0);
     });
 
@@ -298,13 +297,11 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     build_bias_table<SPT, 9>(btab, L, h, tid, 2 * S);
     wait_all();
     __syncthreads();
-    // logits of step 0; mask rows of step 1 (later ones come from the slots)
-    load_bias(sA, bias_of(entry(0), 0));
-    if (N > 1) load_bias(sB, bias_of(entry(1), 1));
+    // logits of step 0 (its mask rows are added by the step)
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      sA[0] = mfma32(KB::read(k0, n, 2 * s + hf), qr[s], sA[0]);
-      sA[1] = mfma32(KB::read(k0, 32 + n, 2 * s + hf), qr[s], sA[1]);
+      sA[0] = mfma32(KB::read(k0, n, 2 * s + hf), qr[s], s == 0 ? f32x16{} : sA[0]);
+      sA[1] = mfma32(KB::read(k0, 32 + n, 2 * s + hf), qr[s], s == 0 ? f32x16{} : sA[1]);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // k0 free
     if (N == 1) {
