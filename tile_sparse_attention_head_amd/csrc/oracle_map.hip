@@ -34,6 +34,9 @@ namespace {
 using namespace attn;
 
 constexpr float kLazyRescale = 8.0f;   // log2 of the largest unnormalised term
+// Running reference of a row that has seen no real key: finite, so that its
+// negation enters the exp2 argument with no test, and far below any logit.
+constexpr float kNoRef = -3.0e38f;
 
 template <int D, int S>
 struct MapPipe {
@@ -51,8 +54,8 @@ struct MapPipe {
 // padding query slot q of the tile:
 //   rowmax[sub][j][q] = sm_scale*log2(e) * max over real keys of tile j of q.k
 //   ml[sub][c][q]     = (m, l) with sum over the chunk's real keys of
-//                       exp2(sm_scale*log2(e) q.k) = l * 2^m  (m = -inf, l = 0
-//                       for an empty chunk)
+//                       exp2(sm_scale*log2(e) q.k) = l * 2^m  (l = 0 for a
+//                       chunk with no real key)
 template <int D, int S>
 __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
@@ -113,7 +116,8 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
   };
   auto bias_of = [&](int t) -> const f32x4* { return &btab.v[qcut][t % SPT][0][hf][0]; };
 
-  float m_run = -INFINITY, l_run = 0.f, tmax = -INFINITY;
+  // m_thr = m_run + kLazyRescale, updated with m_run
+  float m_run = kNoRef, m_thr = kNoRef + kLazyRescale, l_run = 0.f, tmax = -INFINITY;
   float* rm_row = rowmax + ((int64_t)sub * L.max_tiles + j0) * S + qslot;
   f32x16 sA[2], sB[2];
 
@@ -183,9 +187,9 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
       }
       if constexpr (i == 4) {
         const float m_cand = fmaxf(m_run, mxs);
-        raise = m_cand > m_run + kLazyRescale;
+        raise = m_cand > m_thr;
         m_new = raise ? m_cand : m_run;
-        neg_m = m_new == -INFINITY ? 0.f : -m_new;
+        neg_m = -m_new;
         asm volatile("" : "+v"(neg_m));
       }
       // element pairs: FMA in slot fs(k), exp in fs(k)+1, sum in fs(k)+2
@@ -212,7 +216,12 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
       __builtin_amdgcn_sched_barrier(0);
     });
 
-    if (raise) l_run *= exp2_(m_run - m_new);
+    // the sum to the new reference: rare after a row's first real key, so
+    // the exponential is skipped unless some lane raised
+    if (__builtin_expect(__any(raise), 0)) {
+      l_run *= raise ? exp2_(m_run - m_new) : 1.f;
+      m_thr = m_new + kLazyRescale;
+    }
     m_run = m_new;
     l_run += psum0 + psum1;
     // largest logit of the tile, once its last step is in

@@ -53,6 +53,9 @@ namespace {
 using namespace attn;
 
 constexpr float kLazyRescale = 8.0f;   // log2 of the largest unnormalised p
+// Running reference of a row that has seen no real key: finite, so that its
+// negation enters the exp2 argument with no test, and far below any logit.
+constexpr float kNoRef = -3.0e38f;
 // Lockstep XCD order from this many tiles per head on: 8 XCDs x 64 resident
 // workgroups (two per CU on 32 CUs).
 constexpr int kLockstepTiles = 512;
@@ -142,7 +145,8 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     return &btab.v[e >> 16][t % SPT][0][hf][0];
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_thr = m_run + kLazyRescale, updated with m_run
+  float m_run = kNoRef, m_thr = kNoRef + kLazyRescale, l_run = 0.f;
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
@@ -236,9 +240,9 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
       }
       if constexpr (i == 4) {
         const float m_cand = fmaxf(m_run, mxs * scale_log2);
-        raise = m_cand > m_run + kLazyRescale;
+        raise = m_cand > m_thr;
         m_new = raise ? m_cand : m_run;
-        neg_m = m_new == -INFINITY ? 0.f : -m_new;
+        neg_m = -m_new;
         asm volatile("" : "+v"(neg_m));
       }
       // element pairs get their FMAs in slot fs(k), exps in fs(k)+1, sums and
@@ -278,6 +282,7 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m_thr = m_new + kLazyRescale;
     }
     m_run = m_new;
     l_run += psum0 + psum1;
