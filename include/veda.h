@@ -390,6 +390,23 @@ int veda_head_sq_error(const veda_layout* L, const void* a, const void* b, doubl
  *  bytes  (host) output */
 int veda_head_sq_error_workspace(const veda_layout* L, int64_t* bytes);
 
+/* The decision of the head-aware tiling search (Veda §2.2: per head, the
+ * candidate tile shape whose sparse-attention output is closest to the
+ * full-attention output on calibration inputs).
+ *  err     f64 [n_cand][num_heads] (device, 8-byte aligned): row c holds the
+ *          per-head errors of candidate c (e.g. veda_head_sq_error's err)
+ *  choice  int32 [num_heads] (device, 4-byte aligned, output): per head the
+ *          candidate index picked by the scan best = 0; for c = 1 ..
+ *          n_cand - 1: if err[c][h] < err[best][h] then best = c.  Equal
+ *          errors keep the earlier candidate; a NaN error never replaces an
+ *          earlier candidate, and a NaN error of candidate 0 is never replaced.
+ * n_cand in 1..VEDA_MAX_CANDIDATES, num_heads in 1..VEDA_MAX_HEADS, else
+ * VEDA_ERR_INVALID_ARG before any device work.  Stream-ordered, no workspace,
+ * deterministic. */
+#define VEDA_MAX_CANDIDATES 64
+int veda_head_choose(const double* err, int32_t n_cand, int32_t num_heads, int32_t* choice,
+                     void* stream);
+
 /* Static text for a veda_status value. */
 const char* veda_status_string(int status);
 

@@ -64,6 +64,7 @@ int distill_static_scratch(void** ptr) {
   return VEDA_OK;
 }
 int64_t head_error_workspace_bytes(const DevLayout& L) { return (int64_t)L.heads * 64 * 16; }
+int launch_head_choose(const double*, int, int, int32_t*, hipStream_t) { return ++g_launches, VEDA_OK; }
 int launch_head_error(const DevLayout&, const void*, const void*, double*, double*, void*, hipStream_t) {
   return ++g_launches, VEDA_OK;
 }
@@ -221,6 +222,19 @@ int main() {
   EXPECT_CALL(veda_head_sq_error(&L, P(1), P(2), static_cast<double*>(P(3)), nullptr, P(4), ws, nullptr),
               VEDA_OK, 1);
   EXPECT_CALL(veda_head_sq_error(&L, P(1), P(2), static_cast<double*>(P(3)), nullptr, P(4), ws - 1, nullptr),
+              VEDA_ERR_INVALID_ARG, 0);
+
+  double* de = static_cast<double*>(P(3));
+  int32_t* dc = I(4);
+  EXPECT_CALL(veda_head_choose(de, 4, 24, dc, nullptr), VEDA_OK, 1);
+  EXPECT_CALL(veda_head_choose(de, VEDA_MAX_CANDIDATES, VEDA_MAX_HEADS, dc, nullptr), VEDA_OK, 1);
+  EXPECT_CALL(veda_head_choose(nullptr, 4, 24, dc, nullptr), VEDA_ERR_INVALID_ARG, 0);
+  EXPECT_CALL(veda_head_choose(de, 4, 24, nullptr, nullptr), VEDA_ERR_INVALID_ARG, 0);
+  EXPECT_CALL(veda_head_choose(de, 0, 24, dc, nullptr), VEDA_ERR_INVALID_ARG, 0);
+  EXPECT_CALL(veda_head_choose(de, VEDA_MAX_CANDIDATES + 1, 24, dc, nullptr), VEDA_ERR_INVALID_ARG, 0);
+  EXPECT_CALL(veda_head_choose(de, 4, 0, dc, nullptr), VEDA_ERR_INVALID_ARG, 0);
+  EXPECT_CALL(veda_head_choose(de, 4, VEDA_MAX_HEADS + 1, dc, nullptr), VEDA_ERR_INVALID_ARG, 0);
+  EXPECT_CALL(veda_head_choose(reinterpret_cast<double*>(reinterpret_cast<char*>(de) + 4), 4, 24, dc, nullptr),
               VEDA_ERR_INVALID_ARG, 0);
 
   for (int s : {0, -1, -2, -3, -4, 77}) CHECK(std::strlen(veda_status_string(s)) > 0);

@@ -332,6 +332,22 @@ def test_head_sq_error_rejections_and_workspace(lib):
     assert E(ctypes.byref(L6), fake, fake + span, fake, None, fake, ws6.value, None) == -2
 
 
+def test_head_choose_rejections(lib):
+    """veda_head_choose refuses bad counts, null or misaligned pointers before
+    any device work (no GPU call is made here)."""
+    C = lib.veda_head_choose
+    fake = 1 << 20
+    assert C(None, 4, 24, fake, None) == -1
+    assert C(fake, 4, 24, None, None) == -1
+    assert C(fake, 0, 24, fake, None) == -1
+    assert C(fake, 65, 24, fake, None) == -1
+    assert C(fake, -1, 24, fake, None) == -1
+    assert C(fake, 4, 0, fake, None) == -1
+    assert C(fake, 4, 65, fake, None) == -1
+    assert C(fake + 4, 4, 24, fake, None) == -1
+    assert C(fake, 4, 24, fake + 2, None) == -1
+
+
 def test_tiles_per_head_limit(lib):
     """The attention, backward and map calls read a head's K/V tiles through
     a 32-bit buffer range and the forward packs tile indices into 16 bits

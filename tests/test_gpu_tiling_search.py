@@ -8,7 +8,9 @@
   agrees with the oracle's search (oracle.search_head) within the bf16
   output rounding of the two attention runs;
 * the search on the Wan-1.3B-like benchmark layer: every error is the host
-  f64 sum over the GPU's outputs, and the chosen shapes are their argmins.
+  f64 sum over the GPU's outputs, and the chosen shapes are their argmins;
+* veda_head_choose, the search's decision, against the first argmin on
+  tied errors and against its documented scan with NaN errors.
 """
 import numpy as np
 import pytest
@@ -112,3 +114,31 @@ def test_search_bench_layer_errors_are_host_sums():
     torch.cuda.synchronize()
     np.testing.assert_allclose(e[2], ((of - os_) ** 2).sum(axis=(0, 2)), rtol=1e-10)
     np.testing.assert_allclose(host(ref), (of ** 2).sum(axis=(0, 2)), rtol=1e-10)
+
+
+@pytest.mark.parametrize("n_cand,heads", [(4, 24), (1, 3), (64, 64), (7, 40)])
+def test_head_choose_matches_first_argmin(n_cand, heads):
+    """veda_head_choose against the oracle search's rule (np.argmin: the first
+    smallest error) on finite errors drawn from a few values, so that many
+    heads tie; then with NaN planted, against the documented scan (a NaN never
+    replaces an earlier candidate; a NaN candidate 0 stays)."""
+    _say(f"head_choose {n_cand}x{heads}")
+    torch = need_gpu()
+    import tile_sparse_attention_head_amd as V
+    rng = np.random.default_rng(100 * n_cand + heads)
+    e = rng.choice(np.array([0.5, 0.25, 1.0, 0.25, 3.0, 1e-300, 0.0]), size=(n_cand, heads))
+    choice = torch.empty(heads, dtype=torch.int32, device="cuda")
+    V.veda_head_choose(torch.from_numpy(e).cuda(), choice)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(choice), np.argmin(e, axis=0))
+    e[rng.random(e.shape) < 0.2] = np.nan
+    V.veda_head_choose(torch.from_numpy(e).cuda(), choice)
+    torch.cuda.synchronize()
+    want = []
+    for h in range(heads):
+        best = 0
+        for c in range(1, n_cand):
+            if e[c, h] < e[best, h]:
+                best = c
+        want.append(best)
+    assert np.array_equal(host(choice), np.array(want))

@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
                                               c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
         "veda_head_sq_error": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp]),
         "veda_head_sq_error_workspace": (c_i32, [P, ctypes.POINTER(c_i64)]),
+        "veda_head_choose": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
         "veda_sparse_attn_bwd": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
                                          c_f32, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]),
         "veda_sparse_attn_bwd_tiles": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -426,6 +427,18 @@ def veda_head_sq_error(L: veda_layout, a, b, err, workspace, ref=None, stream=No
     have = workspace.numel() * workspace.element_size()
     _check(lib().veda_head_sq_error(ctypes.byref(L), pa, pb, pe, pr, pw, have, _stream(stream)),
            "veda_head_sq_error")
+
+
+def veda_head_choose(err, choice, stream=None) -> None:
+    """choice[h] = the candidate c with the smallest err[c][h] (the first of
+    equal ones); err f64 [n_cand][heads], choice int32 [heads], on the GPU."""
+    torch = _torch()
+    if err is None or err.dim() != 2:
+        raise ValueError("err must be a 2-D [n_cand][heads] tensor")
+    n_cand, heads = int(err.shape[0]), int(err.shape[1])
+    pe = _dev(err, "err", torch.float64, n_cand * heads)
+    pc = _dev(choice, "choice", torch.int32, heads)
+    _check(lib().veda_head_choose(pe, n_cand, heads, pc, _stream(stream)), "veda_head_choose")
 
 
 def veda_sparse_attn_bwd_workspace(L: veda_layout, nnz: int) -> int:

@@ -498,6 +498,15 @@ int veda_head_sq_error(const veda_layout* L, const void* a, const void* b, doubl
   return finish(launch_head_error(dl, a, b, err, ref, workspace, (hipStream_t)stream), stream);
 }
 
+int veda_head_choose(const double* err, int32_t n_cand, int32_t num_heads, int32_t* choice,
+                     void* stream) {
+  if (err == nullptr || choice == nullptr) return VEDA_ERR_INVALID_ARG;
+  if (n_cand < 1 || n_cand > VEDA_MAX_CANDIDATES || num_heads < 1 || num_heads > VEDA_MAX_HEADS)
+    return VEDA_ERR_INVALID_ARG;
+  if (((uintptr_t)err & 7u) != 0 || ((uintptr_t)choice & 3u) != 0) return VEDA_ERR_INVALID_ARG;
+  return finish(launch_head_choose(err, n_cand, num_heads, choice, (hipStream_t)stream), stream);
+}
+
 int64_t veda_layout_sizeof(void) { return (int64_t)sizeof(veda_layout); }
 
 const char* veda_status_string(int status) {

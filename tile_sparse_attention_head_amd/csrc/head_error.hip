@@ -83,7 +83,32 @@ __global__ __launch_bounds__(64) void head_error_final_kernel(const double* __re
   if (ref != nullptr) ref[h] = r;
 }
 
+// The tiling search's choice: one lane per head scans the candidates in
+// order and keeps the first strictly smaller error.
+__global__ __launch_bounds__(64) void head_choose_kernel(const double* __restrict__ err,
+                                                         int n_cand, int heads,
+                                                         int32_t* __restrict__ choice) {
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  if (h >= heads) return;
+  int best = 0;
+  double be = err[h];
+  for (int c = 1; c < n_cand; ++c) {
+    const double e = err[(int64_t)c * heads + h];
+    if (e < be) {
+      be = e;
+      best = c;
+    }
+  }
+  choice[h] = best;
+}
+
 }  // namespace
+
+int launch_head_choose(const double* err, int n_cand, int heads, int32_t* choice, hipStream_t s) {
+  hipLaunchKernelGGL(head_choose_kernel, dim3((heads + 63) / 64), dim3(64), 0, s, err, n_cand, heads,
+                     choice);
+  return launch_status();
+}
 
 int64_t head_error_workspace_bytes(const DevLayout& L) {
   return (int64_t)L.heads * kChunksX * 2 * 8;

@@ -118,6 +118,7 @@ int distill_static_scratch(void** ptr);
 int64_t head_error_workspace_bytes(const DevLayout& L);
 int launch_head_error(const DevLayout& L, const void* a, const void* b, double* err, double* ref,
                       void* workspace, hipStream_t s);
+int launch_head_choose(const double* err, int n_cand, int heads, int32_t* choice, hipStream_t s);
 
 // Attention backward: workspace bytes for a CSR of nnz entries, and the launch.
 int64_t attn_bwd_workspace_bytes(const DevLayout& L, int64_t nnz);

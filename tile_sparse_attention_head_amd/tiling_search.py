@@ -10,8 +10,8 @@ the HIP kernels:
      tokens whatever the tiling;
   2. for each candidate shape (all heads at once): the fused layer at the
      requested sparsity, then veda_head_sq_error against step 1;
-  3. per head, the candidate with the smallest squared error (equal errors
-     prefer the earlier candidate).
+  3. veda_head_choose: per head, the candidate with the smallest squared
+     error (equal errors prefer the earlier candidate).
 """
 from __future__ import annotations
 
@@ -52,12 +52,8 @@ def search_tile_shapes(T: int, H: int, W: int, head_dim: int, tile_size: int, q,
         V.veda_head_sq_error(ly.L, full, out, errs[c], ws, ref=ref if c == 0 else None,
                              stream=stream)
         del ly
-    e = errs.cpu()
-    chosen: List[Tuple[int, int, int]] = []
-    for h in range(heads):
-        best = 0
-        for c in range(1, len(candidates)):
-            if float(e[c, h]) < float(e[best, h]):
-                best = c
-        chosen.append(tuple(candidates[best]))
+    choice = torch.empty(heads, dtype=torch.int32, device=dev)
+    V.veda_head_choose(errs, choice, stream=stream)
+    # the chosen shapes are host parameters of the layers built from them
+    chosen: List[Tuple[int, int, int]] = [tuple(candidates[int(c)]) for c in choice.cpu()]
     return chosen, errs, ref
