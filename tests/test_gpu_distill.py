@@ -3,7 +3,7 @@
 The GPU computes the estimator forward (fused gather + TripPool, projection
 and score), the max-pooled map of a subset of query tiles, then the row-wise
 KL loss and the projection gradients.  The oracle (oracle.distill_head, fp64)
-gets the GPU's own descriptors and map, so the step is judged on its own.
+gets the GPU's own descriptors and map, so the step is checked on its own.
 
 Bars, from f32 arithmetic: the loss within 1e-5 relative; each head's weight
 and bias gradients within 1e-5 of the largest term magnitude that feeds them

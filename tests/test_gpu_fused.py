@@ -10,7 +10,7 @@
   veda_sparse_attn_fwd followed by the inverse permutation.
 
 The bit-identity checks compare the two GPU paths on the same inputs; the
-oracle checks judge the fused calls on their own.
+oracle checks test the fused calls on their own.
 """
 import numpy as np
 import pytest

@@ -7,7 +7,7 @@ f32 tile scores; attention outputs (bf16) max-abs <= 2e-2 and mean-abs <=
 2e-3, log-sum-exp |d| <= 1e-4; the max-pooled map relative 1e-3 with an
 absolute floor of 1e-7.  The oracle always gets the GPU's own inputs to the
 stage under test (e.g. the GPU's f32 score matrix for top-k, the GPU's CSR
-for attention), so each stage is judged on its own.
+for attention), so each stage is checked on its own.
 """
 import numpy as np
 import pytest
