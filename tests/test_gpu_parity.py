@@ -342,15 +342,17 @@ def test_attention_properties_full_size():
         assert np.all(np.abs(o[r.rows(h)][ht.valid] - 1.0) <= 1e-2)
 
 
-def test_attention_edge_csr():
-    """Hand-made CSR: an empty row (O = 0, lse = -inf), out-of-range entries
-    (skipped), a repeated tile, a single kept tile."""
-    _say("attention edge csr")
+@pytest.mark.parametrize("row0", [[], [-5, 4, 100]])
+def test_attention_edge_csr(row0):
+    """Hand-made CSR: an empty row, or a row of out-of-range entries only
+    (every step fully masked; O = 0, lse = -inf either way), out-of-range
+    entries among real ones (skipped), a repeated tile, a single kept tile."""
+    _say(f"attention edge csr row0={row0}")
     torch = need_gpu()
     r = Run("tiny")
     V, L = r.V, r.L
     r.layer.permute_inputs(r.q, r.k, r.v)
-    rows = [[], [3, -1, 7, 0], [2, 2], [1]]
+    rows = [list(row0), [3, -1, 7, 0], [2, 2], [1]]
     rp = np.cumsum([0] + [len(x) for x in rows]).astype(np.int32)
     ci = np.array(sum(rows, []), dtype=np.int32)
     V.veda_sparse_attn_fwd(L, r.layer.q_perm, r.layer.k_perm, r.layer.vt_perm,
