@@ -14,7 +14,9 @@ layer).  These tests compare exactly those cases with the oracle
   configuration (fused calls, O written in token order), sampled query tiles
   of every head including its last (boundary) tile;
 * the Wan-1.3B-like layer at 0 % against dense attention in token order;
-* top-k selection bit-exact at 1830-1920 and 8192 key tiles per row.
+* top-k selection bit-exact at 1830-1920 and 8192 key tiles per row;
+* the max-pooled map of the 720P 241-frame layer's whole 10 % subset,
+  sampled per tile shape against the oracle.
 
 Bars as in the other parity tests: bf16 O max-abs <= 2e-2, mean-abs <= 2e-3,
 lse <= 1e-4; selection bit-exact.
@@ -133,6 +135,51 @@ def test_attention_full_size_layer_sampled(name, sparsity, T):
             assert np.array_equal(rp, ref_rp) and np.array_equal(ci, ref_ci), h
             _say(f"  select head {h}: n = {r.L.n(h)}, k = {k} bit-exact")
     del r, out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(420)
+def test_maxpool_map_720p_sampled():
+    """The max-pooled map at the 720P 241-frame layer in the benchmark's
+    launch shape: the whole seeded 10 % subset (4527 subset tiles, one chunk
+    per tile) over the tile-order Q and K that the fused layer left.  The last
+    subset tile of the first head of each tile shape against
+    oracle.maxpool_map over all of the head's 1830-1920 key tiles (map entries
+    within 1e-3 relative, lse within 1e-4; zeros past the head)."""
+    _say("map 720p 241f 10% sampled")
+    torch = need_gpu()
+    import workloads
+    r = Run("long-720p-241f", sparsity=95, cache=True)
+    r.forward_fused()
+    L = r.L
+    subset = workloads.draw_subset(r.wl, [L.n(h) for h in range(r.heads)])
+    flat = np.concatenate([int(L.tile_off[h]) + s for h, s in enumerate(subset)]).astype(np.int32)
+    assert flat.size > 4000
+    lse, mp = r.layer.maxpool_map(torch.from_numpy(flat).cuda(), r.sm_scale)
+    torch.cuda.synchronize()
+    lse = host(lse).reshape(-1, r.S)
+    mp = host(mp).reshape(-1, L.max_tiles)
+    starts = np.concatenate([[0], np.cumsum([len(s) for s in subset])])
+    first = {}
+    for h in range(r.heads):
+        first.setdefault(r.wl.tile_shapes[h], h)
+    assert len(first) > 1
+    for h in first.values():
+        ht = r.tilings[h]
+        i = len(subset[h]) - 1
+        qp, kp, _ = r.head_perm(h)
+        rl, rm = oracle.maxpool_map(qp, kp, ht.valid, r.S, subset[h][i:i + 1], r.sm_scale)
+        row = starts[h] + i
+        got = mp[row]
+        assert np.all(got[ht.n:] == 0), h
+        rel = np.abs(got[:ht.n] - rm[0]) / np.maximum(rm[0], 1e-30)
+        assert np.all(np.abs(got[:ht.n] - rm[0]) <= np.maximum(1e-3 * rm[0], 1e-7)), (h, rel.max())
+        sel = ~np.isnan(rl)
+        dl = np.abs(lse[row][sel] - rl[sel]).max()
+        assert dl <= LSE_TOL, (h, dl)
+        _say(f"  head {h} {r.wl.tile_shapes[h]}: subset tile {int(subset[h][i])} of {ht.n}, "
+             f"map rel err {rel.max():.2e}, lse err {dl:.2e}")
+    del r
     torch.cuda.empty_cache()
 
 
