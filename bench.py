@@ -648,6 +648,41 @@ def main():
                               "stage_ms": {n: umed[n] for n in u.stages if n != "map"}}
         del u
         torch.cuda.empty_cache()
+        # the score product fused with the selection (the score matrix never
+        # stored) against the two calls, on this step's descriptors
+        _say("bench: scores and selection in one call")
+        ly = b.layer
+
+        def two_calls():
+            ly.score_from_desc(b.w, b.w)
+            ly.select()
+
+        def one_call():
+            ly.score_select_from_desc(b.w, b.w)
+
+        def timed(fn, reps=20):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        try:
+            t2 = timed(two_calls)
+            ci2 = ly.col_idx.clone()
+            t1 = timed(one_call)
+            same = bool(torch.equal(ci2, ly.col_idx))
+            context["score_select"] = {"two_calls_ms": t2, "one_call_ms": t1,
+                                       "csr_bit_identical": same,
+                                       "score_matrix_bytes_not_stored": 4 * L.total_scores}
+            two_calls()   # leave the layer's scores and CSR as the step wrote them
+        except Exception as exc:   # outside the fused call's supported sizes
+            context["score_select"] = {"skipped": str(exc)}
+        torch.cuda.synchronize()
         # the distillation step and the attention backward of this layer
         _say("bench: distillation step and attention backward")
         dms = b.time_distill()

@@ -165,7 +165,9 @@ int veda_tile_permute_pool(const veda_layout* L, int32_t dtype, const void* x, v
  * descriptors already computed (by veda_tile_permute_pool or
  * veda_tripool_score):
  *  desc    f32 [2][tile_off[num_heads]][3*head_dim]: side 0 Q, side 1 K
- *  w_q, w_k, b_q, b_k, d_e, phi, scores  as in veda_tripool_score
+ *  w_q, w_k, b_q, b_k, d_e, phi  as in veda_tripool_score
+ *  scores  as in veda_tripool_score, or NULL: the projection alone (phi for
+ *          veda_score_select)
  * Same kernels and results as veda_tripool_score.  Supported: head_dim in
  * {64, 128}, 1 <= d_e <= 256. */
 int veda_tile_score(const veda_layout* L, const float* desc, const float* w_q,
@@ -185,6 +187,23 @@ int veda_tile_score(const veda_layout* L, const float* desc, const float* w_q,
 int veda_select_tiles(const veda_layout* L, const float* scores,
                       const int32_t* k_per_head, int32_t* row_ptr,
                       int32_t* col_idx, void* stream);
+
+/* The tile-score product fused with the tile selection (Veda §2.1 scores,
+ * <phi_Q,i, phi_K,j>; lay summary and §5: keep the top fraction of tiles):
+ * the CSR that veda_tile_score followed by veda_select_tiles writes, with the
+ * n_tiles x n_tiles score matrix of each head never stored.
+ *  phi         f32 [2][tile_off[num_heads]][d_e] as veda_tile_score writes it
+ *              (scores may be NULL there), 16-byte aligned
+ *  d_e         64 or 128
+ *  k_per_head, row_ptr, col_idx  as in veda_select_tiles
+ * Each score is the same f32 value veda_tile_score writes (the same product
+ * order), so row_ptr and col_idx are bit-identical to the two-call path, and
+ * deterministic.  Arguments outside veda_select_tiles' rules:
+ * VEDA_ERR_INVALID_ARG.  Supported: d_e in {64, 128}, phi 16-byte aligned,
+ * max_tiles <= 2048 (VEDA_ERR_UNSUPPORTED otherwise). */
+int veda_score_select(const veda_layout* L, const float* phi, int32_t d_e,
+                      const int32_t* k_per_head, int32_t* row_ptr, int32_t* col_idx,
+                      void* stream);
 
 /* Tile-skipping attention forward (Veda §2.3).  For every query tile of every
  * head, softmax(sm_scale * Q K^T) V over the real key slots of the key tiles

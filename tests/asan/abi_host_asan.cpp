@@ -65,6 +65,10 @@ int distill_static_scratch(void** ptr) {
 }
 int64_t head_error_workspace_bytes(const DevLayout& L) { return (int64_t)L.heads * 64 * 16; }
 int launch_head_choose(const double*, int, int, int32_t*, hipStream_t) { return ++g_launches, VEDA_OK; }
+int launch_score_select(const DevLayout&, const float*, int, const int32_t*, int32_t*, int32_t*, hipStream_t) {
+  return ++g_launches, VEDA_OK;
+}
+int score_select_max_cols() { return 2048; }
 int launch_head_error(const DevLayout&, const void*, const void*, double*, double*, void*, hipStream_t) {
   return ++g_launches, VEDA_OK;
 }
@@ -171,6 +175,26 @@ int main() {
   EXPECT_CALL(veda_select_tiles(&L, F(1), kbad, I(2), I(3), nullptr), VEDA_ERR_INVALID_ARG, 0);
   kbad[2] = 1921;
   EXPECT_CALL(veda_select_tiles(&L, F(1), kbad, I(2), I(3), nullptr), VEDA_ERR_INVALID_ARG, 0);
+
+  // projection only, then the fused score + selection
+  EXPECT_CALL(veda_tile_score(&L, F(1), F(2), F(2), nullptr, nullptr, 128, F(3), nullptr, nullptr), VEDA_OK, 1);
+  EXPECT_CALL(veda_score_select(&L, F(3), 128, kh, I(2), I(3), nullptr), VEDA_OK, 1);
+  EXPECT_CALL(veda_score_select(&L, F(3), 64, kh, I(2), I(3), nullptr), VEDA_OK, 1);
+  EXPECT_CALL(veda_score_select(&L, F(3), 96, kh, I(2), I(3), nullptr), VEDA_ERR_UNSUPPORTED, 0);
+  EXPECT_CALL(veda_score_select(&L, reinterpret_cast<float*>(reinterpret_cast<char*>(F(3)) + 4), 128, kh,
+                                I(2), I(3), nullptr), VEDA_ERR_UNSUPPORTED, 0);
+  EXPECT_CALL(veda_score_select(&L, F(3), 0, kh, I(2), I(3), nullptr), VEDA_ERR_INVALID_ARG, 0);
+  EXPECT_CALL(veda_score_select(&L, nullptr, 128, kh, I(2), I(3), nullptr), VEDA_ERR_INVALID_ARG, 0);
+  EXPECT_CALL(veda_score_select(&L, F(3), 128, kh, I(2), nullptr, nullptr), VEDA_ERR_INVALID_ARG, 0);
+  EXPECT_CALL(veda_score_select(&L, F(3), 128, kbad, I(2), I(3), nullptr), VEDA_ERR_INVALID_ARG, 0);
+  {
+    const int wide[1][3] = {{1, 8, 16}};
+    veda_layout Lw = make_layout(64, 64, 256, 128, 128, 1, wide);   // 8192 tiles in the head
+    CHECK(veda_layout_init(&Lw) == VEDA_OK && Lw.max_tiles == 8192);
+    int32_t kw[1] = {410};
+    EXPECT_CALL(veda_score_select(&Lw, F(3), 128, kw, I(2), I(3), nullptr), VEDA_ERR_UNSUPPORTED, 0);
+    EXPECT_CALL(veda_select_tiles(&Lw, F(1), kw, I(2), I(3), nullptr), VEDA_OK, 1);
+  }
 
   EXPECT_CALL(veda_sparse_attn_fwd(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(6), F(7), nullptr), VEDA_OK, 1);
   EXPECT_CALL(veda_sparse_attn_fwd_tokens(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(6), nullptr, nullptr),

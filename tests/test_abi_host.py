@@ -332,6 +332,29 @@ def test_head_sq_error_rejections_and_workspace(lib):
     assert E(ctypes.byref(L6), fake, fake + span, fake, None, fake, ws6.value, None) == -2
 
 
+def test_score_select_rejections(lib):
+    """veda_score_select refuses bad arguments before any device work (no
+    GPU call is made here): k out of range, d_e outside {64, 128}, a
+    misaligned phi, rows longer than 2048 tiles."""
+    L = _layout()
+    Lp = ctypes.byref(L)
+    S = lib.veda_score_select
+    fake = 1 << 20
+    H = L.num_heads
+    good = (ctypes.c_int32 * H)(*[1] * H)
+    bad = (ctypes.c_int32 * H)(*([0] + [1] * (H - 1)))
+    assert S(Lp, None, 128, good, fake, fake, None) == -1
+    assert S(Lp, fake, 128, None, fake, fake, None) == -1
+    assert S(Lp, fake, 128, good, None, fake, None) == -1
+    assert S(Lp, fake, 128, good, fake, None, None) == -1
+    assert S(Lp, fake, 0, good, fake, fake, None) == -1
+    assert S(Lp, fake, 128, bad, fake, fake, None) == -1
+    assert S(Lp, fake, 96, good, fake, fake, None) == -2
+    assert S(Lp, fake + 4, 128, good, fake, fake, None) == -2
+    Lw = V.veda_layout_init(64, 64, 256, 128, 128, [(1, 8, 16)])   # 8192 tiles per head
+    assert S(ctypes.byref(Lw), fake, 128, (ctypes.c_int32 * 1)(410), fake, fake, None) == -2
+
+
 def test_head_choose_rejections(lib):
     """veda_head_choose refuses bad counts, null or misaligned pointers before
     any device work (no GPU call is made here)."""

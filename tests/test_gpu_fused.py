@@ -7,7 +7,9 @@
 * veda_tile_score: projection and scores from those descriptors;
 * veda_sparse_attn_fwd_tokens: O written straight to token order, against the
   oracle (same bars as the tile-order call) and bit-identical to
-  veda_sparse_attn_fwd followed by the inverse permutation.
+  veda_sparse_attn_fwd followed by the inverse permutation;
+* veda_score_select: the CSR bit-identical to veda_tile_score followed by
+  veda_select_tiles on the same phi, with and without exact ties.
 
 The bit-identity checks compare the two GPU paths on the same inputs; the
 oracle checks test the fused calls on their own.
@@ -241,3 +243,71 @@ def test_attention_tokens_edge_csr():
     sel = ~np.isnan(rl)
     assert np.abs(og[sel] - ro[sel]).max() <= ATT_MAX
     assert np.abs(lse[sel] - rl[sel]).max() <= LSE_TOL
+
+
+@pytest.mark.timeout(420)
+@pytest.mark.parametrize("name,sparsity,tie", [("tiny", 50, False), ("ragged-small", 75, False),
+                                               ("ragged-d64", 60, False),
+                                               ("wan1.3b-480p-81f", 90, False),
+                                               ("wan1.3b-480p-81f", 95, True),
+                                               ("waver12b-720p-121f", 95, False),
+                                               ("long-720p-241f", 95, False),
+                                               ("long-720p-241f", 95, True)])
+def test_score_select_bit_identical_to_two_calls(name, sparsity, tie):
+    """veda_score_select (scores never stored) against veda_tile_score +
+    veda_select_tiles on the same phi: row_ptr and col_idx bit-identical, at
+    4-1920 key tiles per row (all three register widths of the selection).
+    With tie, phi_K rows are copied within runs of four tiles, so every row
+    holds many exactly equal scores and the lowest index must win."""
+    _say(f"score_select {name} s={sparsity} tie={tie}")
+    torch = need_gpu()
+    r = Run(name, sparsity=sparsity, cache=name.startswith("long"))
+    V, L, ly = r.V, r.L, r.layer
+    ly.permute_pool_inputs(r.q, r.k, r.v)
+    V.veda_tile_score(L, ly.desc, r.w, r.w, ly.phi, None)
+    if tie:
+        de = ly.d_e
+        tot = L.total_tiles
+        pk = ly.phi[tot * de:].view(tot, de)
+        for h in range(r.heads):
+            a, b = int(L.tile_off[h]), int(L.tile_off[h + 1])
+            src = torch.arange(a, b, device="cuda") // 4 * 4
+            pk[a:b] = pk[src]
+    # reference: the standalone score kernel, from the same phi, then select
+    ref_scores = torch.full((L.total_scores,), float("nan"), dtype=torch.float32, device="cuda")
+    _score_only(r, ly.phi, ref_scores)
+    rp_ref = torch.full((L.total_tiles + 1,), -7, dtype=torch.int32, device="cuda")
+    ci_ref = torch.full((max(1, ly.nnz),), -7, dtype=torch.int32, device="cuda")
+    V.veda_select_tiles(L, ref_scores, ly.k_per_head, rp_ref, ci_ref)
+    ly.row_ptr.fill_(-9)
+    ly.col_idx.fill_(-9)
+    V.veda_score_select(L, ly.phi, ly.d_e, ly.k_per_head, ly.row_ptr, ly.col_idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ly.row_ptr), host(rp_ref))
+    assert np.array_equal(host(ly.col_idx)[:ly.nnz], host(ci_ref)[:ly.nnz])
+    if tie:
+        s = host(ref_scores)
+        a, n = int(L.score_off[0]), L.n(0)
+        row = s[a:a + n]
+        assert len(np.unique(row)) <= (n + 3) // 4   # the copies tie exactly
+    _say(f"  {L.total_tiles} rows, nnz {ly.nnz}, max {L.max_tiles} tiles per row: bit-identical")
+    del r
+    torch.cuda.empty_cache()
+
+
+def _score_only(r, phi, scores):
+    """The score product of veda_tile_score from a given phi: its projection
+    is run with an identity weight on descriptors that hold phi itself."""
+    torch = need_gpu()
+    V, L, ly = r.V, r.L, r.layer
+    d, de, tot = L.head_dim, ly.d_e, L.total_tiles
+    # desc rows [phi | 0 | 0] and W = [I | 0 | 0] reproduce phi exactly (each
+    # output is one product by 1 plus exact zeros)
+    desc = torch.zeros(2, tot, 3 * d, dtype=torch.float32, device="cuda")
+    desc[:, :, :de] = phi.view(2, tot, de)
+    w = torch.zeros(L.num_heads, de, 3 * d, dtype=torch.float32, device="cuda")
+    w[:, torch.arange(de), torch.arange(de)] = 1.0
+    phi2 = torch.empty_like(phi)
+    V.veda_tile_score(L, desc.view(-1), w, w, phi2, scores)
+    torch.cuda.synchronize()
+    assert torch.equal(phi2, phi)

@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
         "veda_tile_permute_pool": (c_i32, [P, c_i32, c_vp, c_vp, c_vp, c_vp]),
         "veda_tile_score": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
         "veda_select_tiles": (c_i32, [P, c_vp, ctypes.POINTER(c_i32), c_vp, c_vp, c_vp]),
+        "veda_score_select": (c_i32, [P, c_vp, c_i32, ctypes.POINTER(c_i32), c_vp, c_vp, c_vp]),
         "veda_sparse_attn_fwd": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_vp, c_vp,
                                          c_vp]),
         "veda_sparse_attn_fwd_tokens": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_vp,
@@ -247,7 +248,8 @@ def veda_tile_permute_pool(L: veda_layout, x, y, desc, stream=None) -> None:
 
 def veda_tile_score(L: veda_layout, desc, w_q, w_k, phi, scores, b_q=None, b_k=None,
                     stream=None) -> None:
-    """Projection and tile scores from descriptors desc [2][tiles][3*head_dim]."""
+    """Projection and tile scores from descriptors desc [2][tiles][3*head_dim];
+    scores None: the projection only (veda_score_select takes phi from there)."""
     torch = _torch()
     f32 = torch.float32
     H, d = L.num_heads, L.head_dim
@@ -258,7 +260,7 @@ def veda_tile_score(L: veda_layout, desc, w_q, w_k, phi, scores, b_q=None, b_k=N
             _dev(w_q, "w_q", f32, H * d_e * 3 * d), _dev(w_k, "w_k", f32, H * d_e * 3 * d),
             _dev(b_q, "b_q", f32, H * d_e, True), _dev(b_k, "b_k", f32, H * d_e, True)]
     outs = [_dev(phi, "phi", f32, 2 * L.total_tiles * d_e),
-            _dev(scores, "scores", f32, L.total_scores)]
+            _dev(scores, "scores", f32, L.total_scores, True)]
     _check(lib().veda_tile_score(ctypes.byref(L), *args, d_e, *outs, _stream(stream)),
            "veda_tile_score")
 
@@ -278,6 +280,22 @@ def veda_select_tiles(L: veda_layout, scores, k_per_head: Sequence[int], row_ptr
     pci = _dev(col_idx, "col_idx", torch.int32, csr_nnz(L, k_per_head))
     _check(lib().veda_select_tiles(ctypes.byref(L), ps, kh, prp, pci, _stream(stream)),
            "veda_select_tiles")
+
+
+def veda_score_select(L: veda_layout, phi, d_e: int, k_per_head: Sequence[int], row_ptr,
+                      col_idx, stream=None) -> None:
+    """The tile scores of phi [2][tiles][d_e] and their row-wise top-k as CSR,
+    with the score matrix never stored (same CSR as veda_tile_score followed
+    by veda_select_tiles)."""
+    torch = _torch()
+    if len(k_per_head) != L.num_heads:
+        raise ValueError("k_per_head needs one entry per head")
+    kh = (c_i32 * L.num_heads)(*[int(v) for v in k_per_head])
+    pp = _dev(phi, "phi", torch.float32, 2 * L.total_tiles * int(d_e))
+    prp = _dev(row_ptr, "row_ptr", torch.int32, L.total_tiles + 1)
+    pci = _dev(col_idx, "col_idx", torch.int32, csr_nnz(L, k_per_head))
+    _check(lib().veda_score_select(ctypes.byref(L), pp, int(d_e), kh, prp, pci, _stream(stream)),
+           "veda_score_select")
 
 
 def veda_sparse_attn_fwd(L: veda_layout, q_perm, k_perm, vt_perm, row_ptr, col_idx,

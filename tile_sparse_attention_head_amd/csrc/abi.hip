@@ -310,7 +310,7 @@ int veda_tile_score(const veda_layout* L, const float* desc, const float* w_q, c
                     const float* b_q, const float* b_k, int32_t d_e, float* phi, float* scores,
                     void* stream) {
   if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
-  if (desc == nullptr || w_q == nullptr || w_k == nullptr || phi == nullptr || scores == nullptr)
+  if (desc == nullptr || w_q == nullptr || w_k == nullptr || phi == nullptr)
     return VEDA_ERR_INVALID_ARG;
   if (d_e < 1) return VEDA_ERR_INVALID_ARG;
   if (d_e > 256) return VEDA_ERR_UNSUPPORTED;
@@ -318,6 +318,27 @@ int veda_tile_score(const veda_layout* L, const float* desc, const float* w_q, c
   const DevLayout dl = make_dev_layout(L);
   return finish(launch_project_score(dl, desc, w_q, w_k, b_q, b_k, d_e, phi, scores,
                                      (hipStream_t)stream),
+                stream);
+}
+
+int veda_score_select(const veda_layout* L, const float* phi, int32_t d_e,
+                      const int32_t* k_per_head, int32_t* row_ptr, int32_t* col_idx,
+                      void* stream) {
+  if (L == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  if (phi == nullptr || k_per_head == nullptr || row_ptr == nullptr || col_idx == nullptr)
+    return VEDA_ERR_INVALID_ARG;
+  if (d_e < 1) return VEDA_ERR_INVALID_ARG;
+  int64_t nnz = 0;
+  for (int h = 0; h < L->num_heads; ++h) {
+    if (k_per_head[h] < 1 || k_per_head[h] > L->n_tiles[h]) return VEDA_ERR_INVALID_ARG;
+    nnz += (int64_t)L->n_tiles[h] * k_per_head[h];
+  }
+  if (nnz > INT32_MAX) return VEDA_ERR_INVALID_ARG;
+  if ((d_e != 64 && d_e != 128) || !aligned16(phi)) return VEDA_ERR_UNSUPPORTED;
+  if (L->max_tiles > score_select_max_cols()) return VEDA_ERR_UNSUPPORTED;
+  const DevLayout dl = make_dev_layout(L);
+  return finish(launch_score_select(dl, phi, d_e, k_per_head, row_ptr, col_idx,
+                                    (hipStream_t)stream),
                 stream);
 }
 

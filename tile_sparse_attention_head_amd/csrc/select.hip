@@ -169,33 +169,13 @@ __device__ __forceinline__ uint32_t lane_prefix(uint64_t bal) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
+// The selection of one row by one wave, from the row's keys in registers
+// (lane l: columns l, l + 64, ..., key 0 past the row's end): writes the k
+// kept columns, ascending, to out.  cl: kCand words of LDS for this wave.
 template <int KPL>
-__global__ __launch_bounds__(64 * kWaves) void select_wave_kernel(DevLayout L, SelectArgs sa,
-                                                                  const float* __restrict__ scores,
-                                                                  int32_t* __restrict__ row_ptr,
-                                                                  int32_t* __restrict__ col_idx) {
-  __shared__ uint32_t cand_lds[kWaves][kCand];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t r = (int64_t)blockIdx.x * kWaves + wave;
-  if (r >= L.tile_off[L.heads]) return;
-  const int h = head_of_tile(L, r);
-  const int i = (int)(r - L.tile_off[h]);
-  const int n = (int)(L.tile_off[h + 1] - L.tile_off[h]);
-  const int k = sa.k[h];
-  const int64_t start = sa.nnz_off[h] + (int64_t)i * k;
-  if (lane == 0) {
-    row_ptr[r] = (int32_t)start;
-    if (r + 1 == L.tile_off[L.heads]) row_ptr[r + 1] = (int32_t)sa.nnz_off[L.heads];
-  }
-  const float* row = scores + L.score_off[h] + (int64_t)i * n;
-  uint32_t key[KPL];
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int c = 64 * j + lane;
-    key[j] = c < n ? order_key(row[c]) : 0u;
-  }
-  uint32_t* cl = cand_lds[wave];
+__device__ __forceinline__ void select_from_keys(const uint32_t (&key)[KPL], int n, int k,
+                                                 int lane, uint32_t* cl,
+                                                 int32_t* __restrict__ out) {
   uint32_t t = 0u;
   bool found = false;
   const int rr = (k + 63) / 64;
@@ -307,7 +287,6 @@ __global__ __launch_bounds__(64 * kWaves) void select_wave_kernel(DevLayout L, S
 #pragma unroll
   for (int j = 0; j < KPL; ++j) gt += __popcll(__ballot(64 * j + lane < n && key[j] > t));
   const int need = k - gt;
-  int32_t* out = col_idx + start;
   int pos = 0, eq_seen = 0;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
@@ -324,7 +303,190 @@ __global__ __launch_bounds__(64 * kWaves) void select_wave_kernel(DevLayout L, S
   }
 }
 
+template <int KPL>
+__global__ __launch_bounds__(64 * kWaves) void select_wave_kernel(DevLayout L, SelectArgs sa,
+                                                                  const float* __restrict__ scores,
+                                                                  int32_t* __restrict__ row_ptr,
+                                                                  int32_t* __restrict__ col_idx) {
+  __shared__ uint32_t cand_lds[kWaves][kCand];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r = (int64_t)blockIdx.x * kWaves + wave;
+  if (r >= L.tile_off[L.heads]) return;
+  const int h = head_of_tile(L, r);
+  const int i = (int)(r - L.tile_off[h]);
+  const int n = (int)(L.tile_off[h + 1] - L.tile_off[h]);
+  const int k = sa.k[h];
+  const int64_t start = sa.nnz_off[h] + (int64_t)i * k;
+  if (lane == 0) {
+    row_ptr[r] = (int32_t)start;
+    if (r + 1 == L.tile_off[L.heads]) row_ptr[r + 1] = (int32_t)sa.nnz_off[L.heads];
+  }
+  const float* row = scores + L.score_off[h] + (int64_t)i * n;
+  uint32_t key[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int c = 64 * j + lane;
+    key[j] = c < n ? order_key(row[c]) : 0u;
+  }
+  select_from_keys<KPL>(key, n, k, lane, cand_lds[wave], col_idx + start);
+}
+
+// ---- the score product fused with the selection ---------------------------
+// One workgroup of kSSRows waves per block of kSSRows query-tile rows of one
+// head; wave w owns row w.  Phase 1 computes the block's scores
+//   s[w][j] = <phi_Q[row w], phi_K[j]>,  j < n:
+// key tiles' phi_K rows are staged through LDS 64 at a time (lane c of every
+// wave takes column c of the stage), each wave's phi_Q row sits in LDS and is
+// read as a broadcast, and every score is the sequential FMA chain over the
+// d_e components that the standalone score product uses, so the values are
+// the same f32 numbers.  Lane l of wave w computes columns l, l + 64, ... of
+// row w, which is the register layout of the wave-per-row selection above, so
+// phase 2 runs that selection on the scores where they were computed.  The
+// n x n score matrix is never written to memory.
+constexpr int kSSRows = 8;          // query rows (and waves) per workgroup
+constexpr int kSSCols = 64;         // key rows per stage
+
+struct ScoreSelectArgs {
+  int32_t k[VEDA_MAX_HEADS];
+  int64_t nnz_off[VEDA_MAX_HEADS + 1];
+  int32_t blk_off[VEDA_MAX_HEADS + 1];   // first workgroup of each head
+};
+
+template <int KPL, int DE>
+__global__ __launch_bounds__(64 * kSSRows) void score_select_kernel(
+    DevLayout L, ScoreSelectArgs sa, const float* __restrict__ phi, int32_t* __restrict__ row_ptr,
+    int32_t* __restrict__ col_idx) {
+  constexpr int CPR = DE / 4;                       // 16-byte chunks per phi row
+  static_assert(CPR % 8 == 0, "phi rows of whole 32-float groups");
+  // stage of kSSCols phi_K rows, padded by 4 floats (the 16 lanes of a 128-bit
+  // read that take one chunk of 16 rows then hit 16 distinct bank groups);
+  // after phase 1 it holds the waves' selection candidates
+  constexpr int RS = DE + 4;
+  __shared__ __attribute__((aligned(16))) float stage[kSSCols * RS];
+  __shared__ __attribute__((aligned(16))) float qs[kSSRows][DE];
+  static_assert(kSSCols * RS >= kSSRows * kCand, "candidate buffers fit in the stage");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x;
+  int h = 0;
+  while (h + 1 < L.heads && sa.blk_off[h + 1] <= b) ++h;
+  const int n = (int)(L.tile_off[h + 1] - L.tile_off[h]);
+  const int i0 = (b - sa.blk_off[h]) * kSSRows;
+  const int i = i0 + wave;                          // this wave's row (may lie past n)
+  const float* pk = phi + (L.tile_off[L.heads] + L.tile_off[h]) * DE;
+  // this wave's phi_Q row (a valid row when i >= n; its scores are unused)
+  const float* pq = phi + (L.tile_off[h] + min(i, n - 1)) * DE;
+  if (lane < CPR)
+    *reinterpret_cast<float4*>(&qs[wave][4 * lane]) = *reinterpret_cast<const float4*>(pq + 4 * lane);
+
+  constexpr int PF = kSSCols * CPR / (64 * kSSRows);   // 16-byte chunks per thread per stage
+  static_assert(PF * 64 * kSSRows == kSSCols * CPR, "stage splits evenly");
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  v4f pf[PF];
+  auto fetch = [&](int j0) {
+    // the base goes through an empty asm statement here, after the stage's
+    // barrier: the loads cannot be hoisted into earlier stages (the
+    // unrolled stages would otherwise hold every stage's prefetch at once)
+    typedef __attribute__((address_space(1))) const v4f gv4f;
+    gv4f* base = (gv4f*)(pk + (int64_t)j0 * DE);
+    asm volatile("" : "+s"(base));
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int x = u * 64 * kSSRows + tid;         // chunk of the stage
+      const int r = x / CPR, c = x % CPR;
+      pf[u] = j0 + r < n ? base[r * CPR + c] : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // Stage jj holds key rows 64 jj .. 64 jj + 63, and lane l of every wave
+  // computes column 64 jj + l of its row: exactly the key the selection keeps
+  // in register key[jj] of lane l, so the scores go straight to registers.
+  uint32_t key[KPL];
+  fetch(0);
+#pragma unroll
+  for (int jj = 0; jj < KPL; ++jj) {
+    const int j0 = 64 * jj;
+    key[jj] = 0u;
+    if (j0 >= n) continue;                          // uniform: no barrier is skipped by some waves only
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int x = u * 64 * kSSRows + tid;
+      const int r = x / CPR, c = x % CPR;
+      *reinterpret_cast<v4f*>(&stage[r * RS + 4 * c]) = pf[u];
+    }
+    __syncthreads();
+    if (j0 + kSSCols < n) fetch(j0 + kSSCols);     // in flight during the products
+    float acc = 0.f;
+    const float* krow = &stage[lane * RS];
+    // the phi_Q row is read again in every stage: an LDS pointer hidden from
+    // the compiler keeps it from holding 4*CPR loop-invariant registers
+    typedef __attribute__((address_space(3))) const v4f lds_v4f;
+    lds_v4f* qrow = (lds_v4f*)(&qs[wave][0]);
+    asm volatile("" : "+v"(qrow));
+    // eight chunks at a time, so that few operand reads are in flight
+#pragma unroll
+    for (int cg = 0; cg < CPR; cg += 8) {
+#pragma unroll
+      for (int c = cg; c < cg + 8; ++c) {
+        const float4 kv = *reinterpret_cast<const float4*>(&krow[4 * c]);
+        const v4f qv = qrow[c];
+        acc = fmaf(qv.x, kv.x, acc);
+        acc = fmaf(qv.y, kv.y, acc);
+        acc = fmaf(qv.z, kv.z, acc);
+        acc = fmaf(qv.w, kv.w, acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the products are done here for every lane (the compiler may not sink
+    // them into the masked assignment below and hoist all their reads)
+    asm volatile("" : "+v"(acc));
+    key[jj] = j0 + lane < n ? order_key(acc + 0.f) : 0u;
+    __syncthreads();
+  }
+  if (i >= n) return;
+  const int k = sa.k[h];
+  const int64_t start = sa.nnz_off[h] + (int64_t)i * k;
+  const int64_t r = L.tile_off[h] + i;
+  if (lane == 0) {
+    row_ptr[r] = (int32_t)start;
+    if (r + 1 == L.tile_off[L.heads]) row_ptr[r + 1] = (int32_t)sa.nnz_off[L.heads];
+  }
+  select_from_keys<KPL>(key, n, k, lane, reinterpret_cast<uint32_t*>(stage) + wave * kCand,
+                        col_idx + start);
+}
+
 }  // namespace
+
+int launch_score_select(const DevLayout& L, const float* phi, int d_e, const int32_t* k_host,
+                        int32_t* row_ptr, int32_t* col_idx, hipStream_t s) {
+  ScoreSelectArgs sa;
+  sa.nnz_off[0] = 0;
+  sa.blk_off[0] = 0;
+  for (int h = 0; h < L.heads; ++h) {
+    const int64_t n = L.tile_off[h + 1] - L.tile_off[h];
+    sa.k[h] = k_host[h];
+    sa.nnz_off[h + 1] = sa.nnz_off[h] + n * (int64_t)k_host[h];
+    sa.blk_off[h + 1] = sa.blk_off[h] + (int32_t)((n + kSSRows - 1) / kSSRows);
+  }
+  const unsigned wgs = (unsigned)sa.blk_off[L.heads];
+  if (wgs == 0) return VEDA_OK;
+  const dim3 block(64 * kSSRows);
+#define VEDA_SS(KPL, DE) \
+  hipLaunchKernelGGL((score_select_kernel<KPL, DE>), dim3(wgs), block, 0, s, L, sa, phi, row_ptr, col_idx)
+  if (d_e == 128) {
+    if (L.max_tiles <= 512) VEDA_SS(8, 128);
+    else if (L.max_tiles <= 1024) VEDA_SS(16, 128);
+    else VEDA_SS(32, 128);
+  } else {
+    if (L.max_tiles <= 512) VEDA_SS(8, 64);
+    else if (L.max_tiles <= 1024) VEDA_SS(16, 64);
+    else VEDA_SS(32, 64);
+  }
+#undef VEDA_SS
+  return launch_status();
+}
+
+int score_select_max_cols() { return 64 * 32; }
 
 int launch_select(const DevLayout& L, const float* scores, const int32_t* k_host,
                   int32_t* row_ptr, int32_t* col_idx, hipStream_t s) {

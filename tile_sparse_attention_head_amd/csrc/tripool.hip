@@ -263,6 +263,7 @@ int launch_project_score(const DevLayout& L, const float* desc, const float* wq,
     hipLaunchKernelGGL(project_kernel<false>, pgrid, dim3(kGemmThreads), 0, s, L, d_e, desc, wq,
                        wk, bq, bk, phi);
   if (launch_status() != VEDA_OK) return VEDA_ERR_LAUNCH;
+  if (scores == nullptr) return VEDA_OK;   // projection only
   if (svec)
     hipLaunchKernelGGL(score_kernel<true>, dim3(mb, mb, L.heads), dim3(kGemmThreads), 0, s, L,
                        d_e, phi, scores);

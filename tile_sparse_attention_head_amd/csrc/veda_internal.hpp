@@ -93,6 +93,11 @@ int launch_project_score(const DevLayout& L, const float* desc, const float* wq,
                          float* phi, float* scores, hipStream_t s);
 int launch_select(const DevLayout& L, const float* scores, const int32_t* k_host,
                   int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
+// the score product fused with the selection: d_e in {64, 128}, max_tiles
+// <= score_select_max_cols()
+int launch_score_select(const DevLayout& L, const float* phi, int d_e, const int32_t* k_host,
+                        int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
+int score_select_max_cols();
 int launch_sparse_attn(const DevLayout& L, const void* q, const void* k, const void* vt,
                        const int32_t* row_ptr, const int32_t* col_idx, float sm_scale,
                        void* o, float* lse, bool tokens, hipStream_t s);

@@ -12,6 +12,9 @@ runs the fused sequence:
   3. veda_select_tiles       top-k key tiles per query tile -> CSR
   4. veda_sparse_attn_fwd_tokens   attention, O written in token order
 
+(with ``score_select=True`` steps 2-3 are the projection alone and
+veda_score_select, which never stores the score matrix: the same CSR).
+
 ``forward_unfused`` runs the same method one step per call (permute,
 veda_tripool_score, select, veda_sparse_attn_fwd, inverse permute); both give
 identical results.  ``maxpool_map`` runs veda_oracle_maxpool_map for a subset
@@ -94,6 +97,14 @@ class TileSparseAttention:
     def score_from_desc(self, w_q, w_k, b_q=None, b_k=None, stream=None):
         V.veda_tile_score(self.L, self.desc, w_q, w_k, self.phi, self.scores, b_q, b_k, stream)
 
+    def score_select_from_desc(self, w_q, w_k, b_q=None, b_k=None, stream=None):
+        """Projection, then the scores and their top-k in one call
+        (veda_score_select): the same CSR as score_from_desc + select, with
+        ``scores`` left unwritten."""
+        V.veda_tile_score(self.L, self.desc, w_q, w_k, self.phi, None, b_q, b_k, stream)
+        V.veda_score_select(self.L, self.phi, self.d_e, self.k_per_head, self.row_ptr,
+                            self.col_idx, stream)
+
     def attend_tokens(self, sm_scale: float, out, with_lse: bool = True, stream=None):
         V.veda_sparse_attn_fwd_tokens(self.L, self.q_perm, self.k_perm, self.vt_perm,
                                       self.row_ptr, self.col_idx, sm_scale, out,
@@ -101,13 +112,17 @@ class TileSparseAttention:
 
     # whole layer -----------------------------------------------------------
     def forward(self, q, k, v, w_q, w_k, sm_scale: float, out=None, b_q=None, b_k=None,
-                stream=None):
-        """q, k, v: bf16 [N][heads][d] (token order).  Returns O, same shape."""
+                stream=None, score_select: bool = False):
+        """q, k, v: bf16 [N][heads][d] (token order).  Returns O, same shape.
+        score_select: scores and selection in one call (scores not stored)."""
         if out is None:
             out = self.torch.empty_like(q)
         self.permute_pool_inputs(q, k, v, stream)
-        self.score_from_desc(w_q, w_k, b_q, b_k, stream)
-        self.select(stream)
+        if score_select:
+            self.score_select_from_desc(w_q, w_k, b_q, b_k, stream)
+        else:
+            self.score_from_desc(w_q, w_k, b_q, b_k, stream)
+            self.select(stream)
         self.attend_tokens(sm_scale, out, True, stream)
         return out
 
