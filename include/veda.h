@@ -16,6 +16,13 @@
  *   veda_oracle_maxpool_map   two-pass max-pooled attention
  *                             map (distillation target)      (Veda §2.1, §2.3)
  *
+ * with fused forms of the same steps (veda_tile_permute_pool: gather +
+ * TripPool; veda_tile_score: projection + scores from the descriptors;
+ * veda_score_select: scores + top-k without the score matrix;
+ * veda_sparse_attn_fwd_tokens: attention + inverse permutation), and the
+ * further calls of the method: the distillation step, the tiling search's
+ * error and choice, and the attention backward.
+ *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
  *    memory; the library never allocates, frees or retains a pointer.
