@@ -222,7 +222,7 @@ int veda_score_select(const veda_layout* L, const float* phi, int32_t d_e,
  *                  row_ptr non-decreasing, entries in [0, n_tiles[hd]))
  *  o_perm          bf16, tile order (output); padding query rows unspecified
  *  lse             f32 [tile_off[num_heads]*S] natural-log log-sum-exp per
- *                  query slot, or NULL (output)
+ *                  query slot (padding slots unspecified), or NULL (output)
  *  sm_scale        finite and > 0 (else VEDA_ERR_INVALID_ARG)
  * A query row whose CSR row is empty gets O = 0 and lse = -inf.  Entries of
  * col_idx outside [0, n_tiles[hd]) are skipped.  Supported: (head_dim,

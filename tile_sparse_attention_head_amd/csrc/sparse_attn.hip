@@ -104,9 +104,15 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hf = lane >> 5;
 
+  // A wave whose 32 query slots are all padding (a boundary tile's cut rows)
+  // computes nothing: it issues its share of every copy and joins every
+  // barrier, and leaves O = 0 and lse = -inf for its rows.
+  const TileExtent eq = tile_extent(L, h, (int)(g - head_base));
+  const bool pad_wave = !__any(eq.slot_real(wave * 32 + n));
+
   bf16x8 qr[KS];
   const int64_t qrow = g * S + wave * 32 + n;
-  load_q_regs<D>(qr, q + qrow * D, hf);
+  if (!pad_wave) load_q_regs<D>(qr, q + qrow * D, hf);
 
   cint32* rp = (cint32*)row_ptr;
   int beg = rp[g], end = rp[g + 1];
@@ -291,6 +297,27 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
+  // A padding wave's step: the same copies of step s (K(s+2), or K(s) again
+  // when there is no step s+2, and V(s)) into the same slots, and the same
+  // end-of-step wait and barrier, with no product.
+  auto copy_step = [&](int s) {
+    if ((s + 2) / SPT - wbase >= 64) load_window((s + 2) / SPT - 2);
+    const int es = entry(s);
+    const int t2 = s + 2 < N ? s + 2 : s;
+    const int e2 = entry(t2);
+    const uint32_t kgs = k_off(e2, t2);
+    const uint32_t vgs = v_off(es, s);
+    unsigned char* kdst = (s & 1) ? k1 : k0;
+    unsigned char* vdst = (s & 1) ? v1 : v0;
+    static_for<0, KB::PER_WAVE>([&](auto mc) {
+      KB::round(decltype(mc)::value, krs, kgs, kdst, koff, wave);
+    });
+    static_for<0, VB::PER_WAVE>([&](auto mc) {
+      VB::round(decltype(mc)::value, vrs, vgs, vdst, voff, wave);
+    });
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
   using T = std::true_type;
   using F = std::false_type;
   using Z = std::integral_constant<int, 0>;
@@ -302,6 +329,10 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     build_bias_table<SPT, 9>(btab, L, h, tid, 2 * S);
     wait_all();
     __syncthreads();
+    if (pad_wave) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      for (int s = 0; s < N; ++s) copy_step(s);
+    } else {
     // logits of step 0 (its mask rows are added by the step)
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -335,6 +366,7 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     };
     if ((N - 1) & 1) pv_last(pB, v1);
     else pv_last(pA, v0);
+    }
   }
 
   const float l_tot = swap32_sum(l_run);
@@ -343,7 +375,7 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   // head h, none for a padding slot
   int64_t orow_i = qrow;
   if constexpr (TOK) {
-    const TileExtent e = tile_extent(L, h, (int)(g - head_base));
+    const TileExtent& e = eq;
     const int u = wave * 32 + n;   // slot = (dt*ph + dh)*pw + dw
     const int dw = u % e.pw, r = u / e.pw, dh = r % e.ph, dt = r / e.ph;
     const int64_t tok =
