@@ -84,9 +84,16 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
   const int j0 = (int)((int64_t)c * n_h / chunks), j1 = (int)((int64_t)(c + 1) * n_h / chunks);
   const int N = (j1 - j0) * SPT;   // steps
 
+  // A wave whose 32 query slots are all padding (the cut rows of a boundary
+  // subset tile) computes nothing: it issues its share of every copy, joins
+  // every barrier, and writes -inf row maxima and an empty partial for its
+  // rows, which the reduce pass treats as padding.
+  const bool pad_wave =
+      !__any(tile_extent(L, h, (int)(g - L.tile_off[h])).slot_real(wave * 32 + n));
+
   bf16x8 qr[KS];
   const int qslot = wave * 32 + n;
-  load_q_regs<D>(qr, q + (g * S + qslot) * D, hf);
+  if (!pad_wave) load_q_regs<D>(qr, q + (g * S + qslot) * D, hf);
 
   const auto krs = make_rsrc(reinterpret_cast<const unsigned char*>(k) + head_base * TILE,
                              (int64_t)n_h * TILE);
@@ -236,6 +243,18 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
   using F = std::false_type;
   using Z = std::integral_constant<int, 0>;
   using O1 = std::integral_constant<int, 1>;
+  // a padding wave's step: the same copy of K(s+2) (K(s) again when there is
+  // no step s+2) into the same slot, the row maxima as -inf, and the same
+  // end-of-step wait and barrier
+  auto copy_step = [&](int s) {
+    const uint32_t kgs = s + 2 < N ? k_off(s + 2) : k_off(s);
+    unsigned char* kdst = (s & 1) ? k1 : k0;
+    static_for<0, KB::PER_WAVE>([&](auto mc) {
+      KB::round(decltype(mc)::value, krs, kgs, kdst, koff, wave);
+    });
+    if (s % SPT == SPT - 1 && hf == 0) rm_row[(int64_t)(s / SPT) * S] = -INFINITY;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
   // a step with products, in the variant its next tile's cut asks for
   auto qk_step = [&](auto par, int s) __attribute__((always_inline)) {
     if (cut_at(s + 1) == 0) step(T{}, par, T{}, s);
@@ -247,6 +266,10 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
     build_bias_table<SPT>(btab, L, h, tid, 2 * S);
     wait_all();
     __syncthreads();
+    if (pad_wave) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      for (int s = 0; s < N; ++s) copy_step(s);
+    } else {
     cut_at(0);
     load_bias(sA, bias_of(0));
 #pragma unroll
@@ -266,6 +289,7 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
     }
     if (s & 1) step(F{}, O1{}, F{}, s);
     else step(F{}, Z{}, F{}, s);
+    }
   }
   const float l_tot = swap32_sum(l_run);
   if (hf == 0) ml[((int64_t)sub * chunks + c) * S + qslot] = make_float2(m_run, l_tot);
