@@ -220,9 +220,9 @@ def test_select_bit_exact_large_rows(n_shape, pct, ties):
     key tiles per row (8192 is the largest the selection call accepts), k at
     5 % and 10 %; with ties the values come from a six-value set with +-0, and
     NaN is planted on a lattice; "flat" rows are mostly one value with a few
-    Gaussian entries, so that most keys tie at the k-th place (more than 512
-    keys reach the wave kernel's pre-filter threshold, which sends the row to
-    its search over all keys).  Every row against oracle.select_topk."""
+    Gaussian entries, so that most keys tie at the k-th place (the wave
+    kernel's open range never shrinks to 64 keys and its final pass takes the
+    lowest-index ties).  Every row against oracle.select_topk."""
     grid, shape = n_shape
     _say(f"select large rows {grid} {shape} {pct}% ties={ties}")
     torch = need_gpu()
@@ -248,3 +248,63 @@ def test_select_bit_exact_large_rows(n_shape, pct, ties):
     assert np.array_equal(host(rp), ref_rp)
     assert np.array_equal(host(ci), ref_ci)
     _say(f"  n = {n}, k = {k} bit-exact")
+
+
+def _row_kind(kind, n, rng):
+    """One score row of a given kind (the shapes a threshold search can trip
+    on: narrow ranges, infinities, NaN halves, all-equal rows, integer ties,
+    heavy tails, a diagonal trend)."""
+    if kind == 0:
+        r = rng.normal(size=n)
+    elif kind == 1:
+        r = rng.integers(-3, 3, size=n).astype(np.float64)
+    elif kind == 2:
+        r = np.full(n, 1.5)
+    elif kind == 3:
+        r = rng.normal(size=n)
+        r[rng.random(n) < 0.2] = np.nan
+        r[rng.random(n) < 0.1] = -0.0
+        r[rng.random(n) < 0.1] = 0.0
+    elif kind == 4:
+        r = 5.0 + 1e-3 * rng.normal(size=n)
+    elif kind == 5:
+        r = np.where(rng.random(n) < 0.5, np.inf, -np.inf)
+    elif kind == 6:
+        r = rng.normal(size=n)
+        r[: n // 2] = np.nan
+    elif kind == 7:
+        r = rng.exponential(size=n)
+    else:
+        r = -np.abs(np.arange(n) - rng.integers(0, n)) * 0.002 + rng.normal(size=n)
+    return r.astype(np.float32)
+
+
+@pytest.mark.parametrize("grid,shape", [((21, 30, 52), (4, 4, 8)),      # 336 key tiles
+                                        ((31, 45, 80), (4, 4, 8)),      # 960
+                                        ((61, 45, 80), (4, 4, 8))])     # 1920
+def test_select_row_kinds(grid, shape):
+    """The wave-per-row selection (8, 16 and 32 keys per lane) on rows of nine
+    kinds, one kind per row in turn, at k = 1, 2, 64, 65, 129, 256, 257, n and
+    the 95 % / 90 % keep counts: the k that start the search from the largest,
+    the second, the third-or-fourth largest key per lane or from zero, and the
+    rows whose open range never narrows to 64 keys (ties).  Every row against
+    oracle.select_topk (largest first, ties to the lowest index)."""
+    _say(f"select row kinds {grid} {shape}")
+    torch = need_gpu()
+    import tile_sparse_attention_head_amd as V
+    L = V.veda_layout_init(*grid, 128, 128, [shape])
+    n = L.n(0)
+    rng = np.random.default_rng(500 + n)
+    s = np.stack([_row_kind(i % 9, n, rng) for i in range(n)])
+    dev = to_dev_f32(s.ravel())
+    ks = sorted({1, 2, 64, 65, 129, 256, 257, n, V.veda_keep_count(n, 95),
+                 V.veda_keep_count(n, 90)} & set(range(1, n + 1)))
+    for k in ks:
+        rp = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+        ci = torch.empty(n * k, dtype=torch.int32, device="cuda")
+        V.veda_select_tiles(L, dev, [k], rp, ci)
+        torch.cuda.synchronize()
+        ref_rp, ref_ci = oracle.select_topk(s, k)
+        assert np.array_equal(host(rp), ref_rp), k
+        assert np.array_equal(host(ci), ref_ci), k
+    _say(f"  n = {n}, k in {ks} bit-exact")

@@ -137,30 +137,31 @@ __global__ __launch_bounds__(kThreads) void select_kernel(DevLayout L, SelectArg
 
 // One wave per row, for rows of at most 64*KPL columns: lane l holds the keys
 // of columns l, l + 64, ..., l + 64*(KPL-1) in registers (key 0 past the row's
-// end).  The k-th largest key K* is found bit by bit from the top: t is the
-// largest value with at least k keys >= t, and each candidate t | bit is
-// counted over the wave with one compare and a ballot population count, no
-// barrier.
+// end).  The k-th largest key K* is the largest t with at least k keys >= t;
+// a threshold is counted over the wave with one compare and a ballot
+// population count per register, no barrier.
 //
-// Pre-filter (k <= 256, rows up to 1024 columns; with 32 keys per lane the
-// extra registers cost more occupancy than the filter saves): with
-// r = ceil(k / 64), every lane's r-th largest
-// key is >= tau0, their minimum over the wave, so at least 64 r >= k keys are
-// >= tau0 and K* >= tau0; K* <= the row's largest key, so K* shares their
-// common upper bits.  Only the real keys >= tau0 (a few per lane, compacted
-// into the wave's LDS) are counted, from the first bit where tau0 and the
-// largest key differ: below tau0 both the full and the candidate counts reach
-// k, above it they are equal, so the search ends at the same K*.  Rows where
-// more than kCand keys pass the filter (heavy ties) take the plain search
-// over all keys, which after the upper 16 bits counts only the keys sharing
-// them when at most 64 do.
+// The search keeps t <= K* with c_lo = count(keys >= t) >= k, and c_hi, the
+// count above the range of keys still open (those sharing t's decided upper
+// bits), < k:
+//   * start: with r = ceil(k / 64) <= 4, every lane's r-th largest key is >=
+//     tau0, their minimum over the wave, so at least 64 r >= k keys are >= tau0
+//     and K* >= tau0 (tau0 = 0 for larger k); K* <= the row's largest key, so
+//     K* has the upper bits tau0 and the largest key share, and t starts there;
+//   * while more than 64 keys lie in the open range, the next bit is decided
+//     by counting all keys against t | bit;
+//   * then those keys (at most 64) are compacted into the wave's LDS, one per
+//     lane; the bits they all share are taken at once, and the remaining bits
+//     count only them (plus c_hi for the keys above the range).
+// On score rows the range holds at most 64 keys after about five full counts.
 //
-// The final pass walks the columns in index order, keeps every key > K* and
-// the lowest-index keys == K*, and writes each kept column at the position the
-// ballot prefix gives it: ascending, deterministic, and the same result as the
-// workgroup kernel.
+// The final pass walks the columns in index order and writes each kept column
+// at the position the ballot prefix gives it: ascending, deterministic, and the
+// same result as the workgroup kernel.  When exactly k keys are >= K* (no tie
+// at K* beyond the ones needed) it keeps every key >= K*; otherwise every key
+// > K* and the lowest-index keys == K*.
 constexpr int kWaves = 4;
-constexpr int kCand = 512;   // pre-filter candidates kept in LDS per wave
+constexpr int kCand = 64;   // compacted keys per wave (one per lane)
 
 __device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
   return max(min(a, b), min(max(a, b), c));
@@ -168,19 +169,50 @@ __device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t bal) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
+// bits of x above bit `top` kept, the rest cleared (top < 0: all kept; top =
+// 31: none)
+__device__ __forceinline__ uint32_t upper_bits(uint32_t x, int top) {
+  return top < 0 ? x : top >= 31 ? 0u : (x & ~((2u << top) - 1u));
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
 
 // The selection of one row by one wave, from the row's keys in registers
-// (lane l: columns l, l + 64, ..., key 0 past the row's end): writes the k
-// kept columns, ascending, to out.  cl: kCand words of LDS for this wave.
+// (lane l: columns l, l + 64, ..., key 0 past the row's end), 1 <= k <= n:
+// writes the k kept columns, ascending, to out.  cl: kCand words of LDS for
+// this wave.
 template <int KPL>
 __device__ __forceinline__ void select_from_keys(const uint32_t (&key)[KPL], int n, int k,
                                                  int lane, uint32_t* cl,
                                                  int32_t* __restrict__ out) {
-  uint32_t t = 0u;
-  bool found = false;
-  const int rr = (k + 63) / 64;
-  if (KPL <= 16 && rr <= 4) {
-    // this lane's largest and r-th largest key
+  // real keys >= v over the wave, for v > 0 (padding keys are 0 and never count)
+  auto count_ge = [&](uint32_t v) {
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(key[j] >= v));
+    return cnt;
+  };
+  // the lower bound tau0 and the row's largest key
+  const int r = (k + 63) / 64;
+  uint32_t tau, top_key;
+  if (r <= 2) {
+    uint32_t m1 = 0u, m2 = 0u;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      m2 = med3u(m1, m2, key[j]);
+      m1 = max(m1, key[j]);
+    }
+    tau = r == 1 ? m1 : m2;
+    top_key = m1;
+  } else if (r <= 4) {
     uint32_t m1 = 0u, m2 = 0u, m3 = 0u, m4 = 0u;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
@@ -190,104 +222,84 @@ __device__ __forceinline__ void select_from_keys(const uint32_t (&key)[KPL], int
       m2 = med3u(m1, m2, x);
       m1 = max(m1, x);
     }
-    uint32_t tau = rr == 1 ? m1 : rr == 2 ? m2 : rr == 3 ? m3 : m4, top_key = m1;
+    tau = r == 3 ? m3 : m4;
+    top_key = m1;
+  } else {
+    top_key = 0u;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      tau = min(tau, (uint32_t)__shfl_xor((int)tau, o, 64));
-      top_key = max(top_key, (uint32_t)__shfl_xor((int)top_key, o, 64));
-    }
-    int m = 0;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) m += __popcll(__ballot(64 * j + lane < n && key[j] >= tau));
-    if (m <= kCand) {
-      int base = 0;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        const bool is_c = 64 * j + lane < n && key[j] >= tau;
-        const uint64_t bal = __ballot(is_c);
-        if (is_c) cl[base + lane_prefix(bal)] = key[j];
-        base += __popcll(bal);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      constexpr int CM = kCand / 64;
-      uint32_t cv[CM];
-#pragma unroll
-      for (int j = 0; j < CM; ++j) cv[j] = 64 * j + lane < m ? cl[64 * j + lane] : 0u;
-      const int cw = (m + 63) / 64;   // candidate slots in use per lane
-      const uint32_t diff = tau ^ top_key;
-      const int top = diff ? 31 - __builtin_clz(diff) : -1;
-      t = top < 0 ? tau : (top == 31 ? 0u : tau & ~((2u << top) - 1u));
+    for (int j = 0; j < KPL; ++j) top_key = max(top_key, key[j]);
+    tau = 0u;
+  }
+  tau = wave_min(tau);
+  top_key = wave_max(top_key);
+
+  int b = tau == top_key ? -1 : 31 - __builtin_clz(tau ^ top_key);
+  uint32_t t = upper_bits(tau, b);
+  int c_lo = t == 0u ? n : count_ge(t);
+  int c_hi = 0;
 #pragma unroll 1
-      for (int b = top; b >= 0; --b) {
-        const uint32_t cand = t | (1u << b);
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < CM; ++j)
-          if (j < cw) cnt += __popcll(__ballot(cv[j] >= cand));
-        if (cnt >= k) t = cand;
-      }
-      found = true;
+  for (; b >= 0 && c_lo - c_hi > kCand; --b) {
+    const uint32_t cand = t | (1u << b);
+    const int cnt = count_ge(cand);
+    if (cnt >= k) {
+      t = cand;
+      c_lo = cnt;
+    } else {
+      c_hi = cnt;
     }
   }
-  if (!found) {
-    // count of keys >= v over the wave (padding keys are 0: they count only
-    // for v = 0, where every real key counts too and n >= k already)
-    auto count_ge = [&](uint32_t v) {
-      int cnt = 0;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(key[j] >= v));
-      return cnt;
-    };
-#pragma unroll 1
-    for (int b = 31; b >= 16; --b) {
-      const uint32_t cand = t | (1u << b);
-      if (count_ge(cand) >= k) t = cand;
-    }
-    // keys above the 16-bit prefix always count; keys sharing it are the
-    // candidates for the low bits
-    const uint32_t hi = t >> 16;
-    int above = 0, m = 0;
+  if (b >= 0) {
+    // the c_lo - c_hi <= 64 real keys in [t, t + 2^(b+1)): one per lane
+    const uint32_t span = b >= 31 ? 0xffffffffu : (2u << b) - 1u;
+    int base = 0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      above += __popcll(__ballot((key[j] >> 16) > hi));
-      m += __popcll(__ballot((key[j] >> 16) == hi));
+      const bool is_c = 64 * j + lane < n && key[j] >= t && key[j] - t <= span;
+      const uint64_t bal = __ballot(is_c);
+      if (is_c) cl[base + lane_prefix(bal)] = key[j];
+      base += __popcll(bal);
     }
-    if (m <= 64) {
-      int base = 0;
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        const bool is_c = (key[j] >> 16) == hi;
-        const uint64_t bal = __ballot(is_c);
-        if (is_c) cl[base + lane_prefix(bal)] = key[j];
-        base += __popcll(bal);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const uint32_t mine = lane < m ? cl[lane] : 0u;
-      const bool live = lane < m;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const bool live = lane < base;
+    const uint32_t mine = live ? cl[lane] : 0u;
+    // K* is one of them: its bits above where their minimum and maximum differ
+    // are decided
+    const uint32_t cmin = wave_min(live ? mine : 0xffffffffu);
+    const uint32_t cmax = wave_max(live ? mine : 0u);
+    const int top2 = cmin == cmax ? -1 : 31 - __builtin_clz(cmin ^ cmax);
+    t = upper_bits(cmin, top2);
+    c_lo = c_hi + base;
+    const int above = c_hi;
 #pragma unroll 1
-      for (int b = 15; b >= 0; --b) {
-        const uint32_t cand = t | (1u << b);
-        if (above + __popcll(__ballot(live && mine >= cand)) >= k) t = cand;
-      }
-    } else {
-#pragma unroll 1
-      for (int b = 15; b >= 0; --b) {
-        const uint32_t cand = t | (1u << b);
-        if (count_ge(cand) >= k) t = cand;
+    for (b = top2; b >= 0; --b) {
+      const uint32_t cand = t | (1u << b);
+      const int cnt = above + __popcll(__ballot(live && mine >= cand));
+      if (cnt >= k) {
+        t = cand;
+        c_lo = cnt;
       }
     }
   }
-  // t = K*, the k-th largest key; keep every key > K* and the first `need`
-  // keys == K* in index order
+  // t = K*, c_lo = count(keys >= K*)
+  int pos = 0;
+  if (c_lo == k) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int c = 64 * j + lane;
+      const bool take = c < n && key[j] >= t;
+      const uint64_t bt = __ballot(take);
+      if (take) out[pos + lane_prefix(bt)] = c;
+      pos += __popcll(bt);
+    }
+    return;
+  }
   int gt = 0;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) gt += __popcll(__ballot(64 * j + lane < n && key[j] > t));
   const int need = k - gt;
-  int pos = 0, eq_seen = 0;
+  int eq_seen = 0;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int c = 64 * j + lane;
@@ -323,12 +335,19 @@ __global__ __launch_bounds__(64 * kWaves) void select_wave_kernel(DevLayout L, S
     if (r + 1 == L.tile_off[L.heads]) row_ptr[r + 1] = (int32_t)sa.nnz_off[L.heads];
   }
   const float* row = scores + L.score_off[h] + (int64_t)i * n;
+  // range-checked buffer loads over the row (columns past it read 0): every
+  // load is unconditional, so all of them are in flight at once, and the
+  // padding keys are masked to 0 after
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), (short)0, n * 4, 0x00020000);
+  float v[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j)
+    v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (64 * j + lane) * 4, 0, 0));
   uint32_t key[KPL];
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int c = 64 * j + lane;
-    key[j] = c < n ? order_key(row[c]) : 0u;
-  }
+  for (int j = 0; j < KPL; ++j)
+    key[j] = order_key(v[j]) & (0u - (uint32_t)(64 * j + lane < n));
   select_from_keys<KPL>(key, n, k, lane, cand_lds[wave], col_idx + start);
 }
 
