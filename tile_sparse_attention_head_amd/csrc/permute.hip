@@ -6,8 +6,12 @@
 // is computed once into LDS.  Every row is d contiguous elements in both
 // layouts, moved as 16-byte chunks: consecutive lanes take consecutive
 // chunks, so each row is one fully coalesced 16*CPR-byte burst, and a lane
-// issues several loads before its stores.  The kernels are pure data
-// movement, bound by HBM bandwidth.
+// issues several loads before its stores.  Those loads and stores are
+// unconditional (a padding slot reads slot 0's row, always a real token, and
+// stores zeros; a chunk index past the tile is clamped to its last chunk,
+// which is then written twice with the same value): a load or store under a
+// branch gets a wait of its own, and then each store waits for the one
+// before it.  The kernels are pure data movement, bound by HBM bandwidth.
 #include "veda_internal.hpp"
 
 namespace veda {
@@ -54,21 +58,17 @@ __global__ __launch_bounds__(kThreads) void permute_fwd_kernel(DevLayout L, int 
   Chunk* dst = y + g * (int64_t)total;
   for (int c0 = 0; c0 < total; c0 += kThreads * kBatch) {
     Chunk v[kBatch];
+    int cc[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int c = c0 + i * kThreads + threadIdx.x;
-      v[i] = Chunk{0u, 0u, 0u, 0u};
-      if (c < total) {
-        const int u = c / cpr, k = c - u * cpr;
-        const int64_t r = rows[u];
-        if (r >= 0) v[i] = x[r * cpr + k];
-      }
+      cc[i] = min(c0 + i * kThreads + (int)threadIdx.x, total - 1);
+      const int u = cc[i] / cpr, k = cc[i] - u * cpr;
+      const int64_t r = rows[u];
+      const Chunk a = x[(r >= 0 ? r : rows[0]) * cpr + k];
+      v[i] = r >= 0 ? a : Chunk{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int c = c0 + i * kThreads + threadIdx.x;
-      if (c < total) dst[c] = v[i];
-    }
+    for (int i = 0; i < kBatch; ++i) dst[cc[i]] = v[i];
   }
 }
 
@@ -101,24 +101,18 @@ __global__ __launch_bounds__(kThreads) void permute_fwd_pool_kernel(DevLayout L,
   for (int c0 = 0; c0 < total; c0 += kThreads * kBatch) {
     Chunk v[kBatch];
     bool real[kBatch];
+    int cc[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int c = c0 + i * kThreads + threadIdx.x;
-      v[i] = Chunk{0u, 0u, 0u, 0u};
-      real[i] = false;
-      if (c < total) {
-        const int64_t r = rows[c / CPR];
-        if (r >= 0) {
-          v[i] = x[r * CPR + ch];
-          real[i] = true;
-        }
-      }
+      cc[i] = min(c, total - 1);
+      const int64_t r = rows[cc[i] / CPR];
+      real[i] = c < total && r >= 0;
+      const Chunk a = x[(r >= 0 ? r : rows[0]) * CPR + cc[i] % CPR];
+      v[i] = r >= 0 ? a : Chunk{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int c = c0 + i * kThreads + threadIdx.x;
-      if (c < total) dst[c] = v[i];
-    }
+    for (int i = 0; i < kBatch; ++i) dst[cc[i]] = v[i];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       if (!real[i]) continue;
