@@ -323,6 +323,12 @@ class Bench:
         for _ in range(warmup):
             self.step(with_map=with_map)
         ev = self._events(steps)
+        # torch creates a HIP event at its first record(): do that for every
+        # event here, outside the timed region (creating 20 x 9 of them inside it
+        # stalled one step's launches for about 20 ms)
+        for e in ev:
+            for x in e:
+                x.record()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
