@@ -147,6 +147,51 @@ def test_tile_score_from_desc_vs_oracle():
         assert np.abs(r.scores_head(h) - sref).max() <= 1e-4 * max(1.0, np.abs(sref).max()), h
 
 
+def test_tile_score_odd_width_and_unaligned_operands():
+    """veda_tile_score with d_e = 50 (the score product's K is not a multiple
+    of 4, nor of the 32-wide K step) on descriptors, weights, biases and phi
+    shifted by 4 bytes from 16-byte alignment: the kernels' element-wise,
+    zero-padded loads, against the oracle."""
+    _say("tile_score d_e = 50, unaligned")
+    torch = need_gpu()
+    r = Run("ragged-small")
+    V, L, d = r.V, r.L, r.d
+    de = 50
+    rng = np.random.default_rng(13)
+    wq = rng.normal(0, 0.02, size=(r.heads, de, 3 * d)).astype(np.float32)
+    wk = rng.normal(0, 0.02, size=(r.heads, de, 3 * d)).astype(np.float32)
+    bq = rng.normal(0, 0.1, size=(r.heads, de)).astype(np.float32)
+    bk = rng.normal(0, 0.1, size=(r.heads, de)).astype(np.float32)
+    r.layer.permute_pool_inputs(r.q, r.k, r.v)
+    tot = L.total_tiles
+
+    def shifted(a):
+        t = a if isinstance(a, torch.Tensor) else to_dev_f32(np.ascontiguousarray(a).ravel())
+        buf = torch.empty(t.numel() + 1, dtype=torch.float32, device="cuda")
+        buf[1:].copy_(t.reshape(-1))
+        return buf[1:].view(a.shape)
+    phi_u = shifted(torch.zeros(2 * tot * de, dtype=torch.float32, device="cuda"))
+    scores = torch.empty(L.total_scores, dtype=torch.float32, device="cuda")
+    V.veda_tile_score(L, shifted(r.layer.desc), shifted(wq), shifted(wk), phi_u, scores,
+                      shifted(bq), shifted(bk))
+    torch.cuda.synchronize()
+    desc = host(r.layer.desc).reshape(2, tot, 3 * d).astype(np.float64)
+    phi = host(phi_u).reshape(2, tot, de)
+    sc = host(scores)
+    for h in range(r.heads):
+        a, b = int(L.tile_off[h]), int(L.tile_off[h + 1])
+        pq = oracle.project(desc[0, a:b], wq[h].astype(np.float64), bq[h].astype(np.float64))
+        pk = oracle.project(desc[1, a:b], wk[h].astype(np.float64), bk[h].astype(np.float64))
+        tol = 1e-4 * max(1.0, np.abs(pq).max(), np.abs(pk).max())
+        assert np.abs(phi[0, a:b] - pq).max() <= tol, h
+        assert np.abs(phi[1, a:b] - pk).max() <= tol, h
+        n = b - a
+        off = int(L.score_off[h])
+        sref = oracle.tile_scores(phi[0, a:b].astype(np.float64), phi[1, a:b].astype(np.float64))
+        sg = sc[off:off + n * n].reshape(n, n)
+        assert np.abs(sg - sref).max() <= 1e-4 * max(1.0, np.abs(sref).max()), h
+
+
 def _check_tokens(r, out, q_tiles_per_head=None):
     """Token-order O of the fused layer against the oracle's sparse attention
     on the GPU's own CSR, scattered to token order."""

@@ -103,6 +103,48 @@ def _sample(r, seed, per_head=2):
                               r.L.n(h) - 1)) for h in range(r.heads)]
 
 
+def _check_estimator_sampled(r, sample):
+    """The projection (128-row tiles at these sizes) and the score product of
+    the full-size layer on the sampled query tiles of every head: phi against
+    the oracle's projection of the GPU's descriptors, and those tiles' score
+    rows against the oracle's score of the GPU's phi.  Then the same call on
+    copies of the descriptors, weights and phi shifted by 4 bytes (so the
+    kernels take their generic, element-wise loads) must give the same bits."""
+    torch = need_gpu()
+    V, L, d, ly = r.V, r.L, r.d, r.layer
+    tot, de = L.total_tiles, ly.d_e
+    desc = host(ly.desc).reshape(2, tot, 3 * d).astype(np.float64)
+    phi = host(ly.phi).reshape(2, tot, de)
+    worst = 0.0
+    for h in range(r.heads):
+        a, b = int(L.tile_off[h]), int(L.tile_off[h + 1])
+        w = r.wl.w[h].astype(np.float64)
+        rows = a + sample[h]
+        for side in (0, 1):
+            ref = oracle.project(desc[side, rows], w)
+            err = np.abs(phi[side, rows] - ref).max()
+            assert err <= 1e-4 * max(1.0, np.abs(ref).max()), (h, side, err)
+        sref = oracle.tile_scores(phi[0, rows].astype(np.float64), phi[1, a:b].astype(np.float64))
+        sg = r.scores_head(h)[sample[h]]
+        err = np.abs(sg - sref).max()
+        worst = max(worst, err / max(1.0, np.abs(sref).max()))
+        assert err <= 1e-4 * max(1.0, np.abs(sref).max()), (h, err)
+    # unaligned operands: the element-wise path of both products, same bits
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        buf[1:].copy_(t.reshape(-1))
+        return buf[1:].view(t.shape)
+    desc_u, w_u = shifted(ly.desc), shifted(r.w)
+    phi_u = shifted(torch.zeros_like(ly.phi))
+    sc_u = torch.empty_like(ly.scores)
+    V.veda_tile_score(L, desc_u, w_u, w_u, phi_u, sc_u)
+    torch.cuda.synchronize()
+    assert torch.equal(phi_u, ly.phi)
+    assert torch.equal(sc_u, ly.scores)
+    _say(f"  projection and scores on sampled tiles: worst {worst:.2e} of max|S|; "
+         f"unaligned operands bit-identical")
+
+
 @pytest.mark.timeout(420)
 @pytest.mark.parametrize("name,sparsity,T", [("waver12b-720p-121f", 90, None),
                                              ("waver12b-720p-121f", 95, None),
@@ -113,7 +155,8 @@ def test_attention_full_size_layer_sampled(name, sparsity, T):
     on two seeded query tiles per head plus the head's last tile.  At the
     720P 241-frame layer the selection is also checked bit-exact on the GPU's
     own scores for every row of one head of each tile shape (1830-1920 key
-    tiles per row)."""
+    tiles per row).  The projection and score product are checked on the
+    sampled tiles too, with aligned and unaligned operands."""
     _say(f"full-size {name} {sparsity}%")
     torch = need_gpu()
     r = Run(name, sparsity=sparsity, T=T, cache=True)
@@ -124,6 +167,7 @@ def test_attention_full_size_layer_sampled(name, sparsity, T):
     _say(f"  max-abs {worst:.3e} mean-abs {mean:.3e}, longest kept row {longest}")
     if sparsity == 90 or name.startswith("long"):
         assert longest > 64
+    _check_estimator_sampled(r, sample)
     if name.startswith("long"):
         first = {}
         for h in range(r.heads):
