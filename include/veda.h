@@ -323,7 +323,10 @@ int veda_sparse_attn_bwd_workspace(const veda_layout* L, int64_t nnz, int64_t* b
  *  lse             f32 [n_sub*S] (output); padding query rows unspecified
  *  map             f32 [n_sub][max_tiles] (output)
  * Pass 1 also records, per query row and key tile, the largest logit, so
- * pass 2 reads n_sub*max_tiles*S floats instead of recomputing Q K^T.
+ * pass 2 reads n_sub*max_tiles*S floats instead of recomputing Q K^T.  Pass 1
+ * hands out its work items (subset tile, chunk of key tiles) through eight
+ * counters in the workspace, reset by a small kernel on `stream` first (no
+ * memset); which workgroup computes an item does not change the results.
  * Supported: (head_dim, tile_size) in {(64,64), (128,128)}, max_tiles <=
  * VEDA_MAX_TILES_PER_HEAD. */
 int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void* k_perm,
@@ -333,7 +336,9 @@ int veda_oracle_maxpool_map(const veda_layout* L, const void* q_perm, const void
 
 /* Workspace bytes veda_oracle_maxpool_map needs for n_sub subset entries of
  * layout L (0 for n_sub = 0): n_sub*max_tiles*S*4 for the row maxima plus
- * n_sub*chunks*S*8 for per-chunk partial sums.  Host-only, no device work.
+ * n_sub*16*S*8 for per-chunk partial sums (up to 16 chunks), each rounded up
+ * to 256 bytes, plus 256 for pass 1's work counters.  Host-only, no device
+ * work.
  * n_sub above VEDA_MAX_SUBSET or max_tiles above VEDA_MAX_TILES_PER_HEAD:
  * VEDA_ERR_UNSUPPORTED.
  *  bytes  (host) output */

@@ -227,8 +227,9 @@ def test_distill_rejections_and_workspace(lib):
 
 
 def test_map_workspace_size(lib):
-    # row maxima (n_sub x max_tiles x S f32, rounded up to 256 bytes) followed by
-    # the per-chunk (m, l) pairs (n_sub x chunks x S x 2 f32)
+    # row maxima (n_sub x max_tiles x S f32), the per-chunk (m, l) pairs for up
+    # to 16 chunks (n_sub x 16 x S x 2 f32), each rounded up to 256 bytes, then
+    # 256 bytes for pass 1's eight work-claim counters
     L = _layout()
     out = ctypes.c_int64(-5)
     assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(L), 0, ctypes.byref(out)) == 0
@@ -236,10 +237,8 @@ def test_map_workspace_size(lib):
     for n_sub in (1, 3, 400):
         assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(L), n_sub, ctypes.byref(out)) == 0
         rm = -(-n_sub * L.max_tiles * L.tile_size * 4 // 256) * 256
-        rest = out.value - rm
-        assert rest > 0 and rest % (n_sub * L.tile_size * 8) == 0
-        chunks = rest // (n_sub * L.tile_size * 8)
-        assert 1 <= chunks <= min(16, L.max_tiles)
+        ml = -(-n_sub * 16 * L.tile_size * 8 // 256) * 256
+        assert out.value == rm + ml + 256
     assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(L), -1, ctypes.byref(out)) == -1
     assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(L), 3, None) == -1
 

@@ -56,11 +56,32 @@ struct MapPipe {
 //   ml[sub][c][q]     = (m, l) with sum over the chunk's real keys of
 //                       exp2(sm_scale*log2(e) q.k) = l * 2^m  (l = 0 for a
 //                       chunk with no real key)
+// Item of pass 1 for a workgroup on XCD x, out of G items in 8 contiguous
+// ranges (range y: per + (y < rem) items from y*per + min(y, rem)): the next
+// unclaimed item of range x, else of range x+1, x+2, ... (mod 8); -1 when all
+// are claimed.  Every item goes to exactly one workgroup: the counters only
+// grow, and a range is only given up once its counter has passed its length.
+__device__ __forceinline__ int claim_item(int* claim, int x, int G) {
+  const int per = G / 8, rem = G % 8;
+  for (int o = 0; o < 8; ++o) {
+    const int y = (x + o) & 7;
+    const int len = per + (y < rem ? 1 : 0);
+    if (__hip_atomic_load(&claim[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
+    const int i = atomicAdd(&claim[y], 1);
+    if (i < len) return y * per + min(y, rem) + i;
+  }
+  return -1;
+}
+
+__global__ void map_claim_reset_kernel(int* claim) {
+  if (threadIdx.x < 8) claim[threadIdx.x] = 0;
+}
+
 template <int D, int S>
 __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
-    const int32_t* __restrict__ q_tiles, int chunks, float* __restrict__ rowmax,
-    float2* __restrict__ ml) {
+    const int32_t* __restrict__ q_tiles, int n_sub, int chunks, float* __restrict__ rowmax,
+    float2* __restrict__ ml, int* __restrict__ claim) {
   using P = MapPipe<D, S>;
   using KB = typename P::KBuf;
   constexpr int SPT = P::SPT, KS = P::KS, TILE = P::TILE;
@@ -68,11 +89,20 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char k1[KB::BYTES];
   __shared__ BiasTable<SPT> btab;
 
-  // chunk-major: the workgroups running together on one XCD take the same
-  // key-tile range for consecutive subset tiles, which share it in L2
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t n_sub = gridDim.x / chunks;
-  const int sub = (int)(b % n_sub), c = (int)(b / n_sub);
+  // The work items (subset tile, chunk) are numbered chunk-major and cut
+  // into 8 contiguous ranges, range x for XCD x: the workgroups running
+  // together on one XCD take the same key-tile range for consecutive subset
+  // tiles, which share it in L2.  A workgroup claims the next item of its
+  // XCD's range (the hardware places workgroup b on XCD b % 8), or, once that
+  // range is used up, of the next range that is not: XCDs that run faster
+  // take over the end of the slower ones' work.  The grid holds spare
+  // workgroups for that; one that finds every range used up exits.
+  __shared__ int item_s;
+  if (threadIdx.x == 0) item_s = claim_item(claim, (int)(blockIdx.x & 7), n_sub * chunks);
+  __syncthreads();
+  const int b = item_s;
+  if (b < 0) return;
+  const int sub = b % n_sub, c = b / n_sub;
   const int64_t g = ((cint32*)q_tiles)[sub];
   if (g < 0 || g >= L.tile_off[L.heads]) return;   // the reduce pass writes a zero row
   const int h = head_of_tile(L, g);
@@ -404,22 +434,25 @@ __global__ __launch_bounds__(256) void map_reduce_kernel(
 
 }  // namespace
 
-// Pass-1 chunks per subset tile.  Pass 1 runs n_sub * c equal workgroups,
-// `slots` of them at a time; its time is about rounds(c) * (work of one
-// workgroup) with rounds(c) = ceil(n_sub c / slots) and one workgroup's work
-// ceil(max_tiles / c) * SPT steps plus a fixed cost of about kChunkFixed
-// steps (loading its queries, the first copies, the final partials).  c is
-// the smallest minimiser over 1 .. kMaxChunks: a last round that would run
-// nearly empty is avoided by cutting the key tiles finer.
+// Pass-1 chunks per subset tile.  Pass 1 runs n_sub * c items of w(c) =
+// ceil(max_tiles / c) * SPT steps plus a fixed cost of about kChunkFixed steps
+// (loading its queries, the first copies, the final partials), `slots`
+// workgroups at a time.  The work claiming keeps every slot busy until the
+// items run out, so the time is about the work per slot, n_sub c (w(c) +
+// kChunkFixed) / slots, plus the drain at the end, which lasts about one
+// item: t(c) = n_sub c (w(c) + fixed) / slots + w(c).  Finer chunks shorten
+// the drain and add fixed costs; c is the smallest minimiser over
+// 1 .. kMaxChunks.
 constexpr int64_t kChunkFixed = 6;
 int64_t map_chunks(int64_t n_sub, int64_t max_tiles, int64_t spt, int64_t slots) {
   if (n_sub <= 0) return 1;
   if (slots < 1) slots = 1;
-  int64_t best = 1, best_t = -1;
+  int64_t best = 1;
+  double best_t = -1.0;
   for (int64_t c = 1; c <= kMaxChunks && c <= max_tiles; ++c) {
-    const int64_t rounds = (n_sub * c + slots - 1) / slots;
-    const int64_t t = rounds * ((max_tiles + c - 1) / c * spt + kChunkFixed);
-    if (best_t < 0 || t < best_t) {
+    const int64_t w = (max_tiles + c - 1) / c * spt;
+    const double t = (double)(n_sub * c) * (double)(w + kChunkFixed) / (double)slots + (double)w;
+    if (best_t < 0.0 || t < best_t) {
       best_t = t;
       best = c;
     }
@@ -445,8 +478,8 @@ int64_t map_workspace_bytes(const DevLayout& L, int64_t n_sub) {
   if (n_sub <= 0) return 0;
   const int64_t S = L.S;
   const int64_t rm = ((n_sub * L.max_tiles * S * 4) + 255) / 256 * 256;
-  const int64_t mlb = n_sub * kMaxChunks * S * 8;
-  return rm + mlb;
+  const int64_t mlb = (n_sub * kMaxChunks * S * 8 + 255) / 256 * 256;
+  return rm + mlb + 256;   // + the 8 claim counters of pass 1
 }
 
 int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm_scale,
@@ -458,20 +491,27 @@ int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm
   const int chunks = (int)map_chunks(n_sub, L.max_tiles, L.S / 64, slots);
   float* rowmax = static_cast<float*>(workspace);
   const int64_t rm = ((n_sub * (int64_t)L.max_tiles * L.S * 4) + 255) / 256 * 256;
+  const int64_t mlb = ((int64_t)n_sub * kMaxChunks * L.S * 8 + 255) / 256 * 256;
   float2* ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(workspace) + rm);
-  const unsigned grid1 = (unsigned)(n_sub * chunks);
+  int* claim = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + rm + mlb);
+  // items plus a quarter of each XCD's share in spare workgroups
+  const int64_t items = (int64_t)n_sub * chunks;
+  const unsigned grid1 = (unsigned)(items + 8 * (((items + 7) / 8 + 3) / 4));
+  hipLaunchKernelGGL(map_claim_reset_kernel, dim3(1), dim3(64), 0, s, claim);
   // pass 2: blocks of 32..256 key tiles, about 4096 workgroups in all
   int64_t tb = ((int64_t)L.max_tiles * n_sub / 4096 + 31) / 32 * 32;
   tb = tb < 32 ? 32 : (tb > 256 ? 256 : tb);
   const dim3 grid2((unsigned)((L.max_tiles + tb - 1) / tb), (unsigned)n_sub);
   if (L.d == 128) {
     hipLaunchKernelGGL((map_stats_kernel<128, 128>), dim3(grid1), dim3(256), 0, s, L,
-                       (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, chunks, rowmax, ml);
+                       (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, n_sub, chunks,
+                       rowmax, ml, claim);
     hipLaunchKernelGGL((map_reduce_kernel<128>), grid2, dim3(256), 0, s, L, q_tiles, chunks,
                        (int)tb, rowmax, ml, lse, map);
   } else {
     hipLaunchKernelGGL((map_stats_kernel<64, 64>), dim3(grid1), dim3(128), 0, s, L,
-                       (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, chunks, rowmax, ml);
+                       (const __bf16*)q, (const __bf16*)k, scale_log2, q_tiles, n_sub, chunks,
+                       rowmax, ml, claim);
     hipLaunchKernelGGL((map_reduce_kernel<64>), grid2, dim3(256), 0, s, L, q_tiles, chunks,
                        (int)tb, rowmax, ml, lse, map);
   }
