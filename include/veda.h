@@ -224,6 +224,18 @@ int veda_score_select(const veda_layout* L, const float* phi, int32_t d_e,
  *  lse             f32 [tile_off[num_heads]*S] natural-log log-sum-exp per
  *                  query slot (padding slots unspecified), or NULL (output)
  *  sm_scale        finite and > 0 (else VEDA_ERR_INVALID_ARG)
+ *  workspace       device scratch of at least workspace_bytes >=
+ *                  veda_sparse_attn_fwd_workspace(L) bytes, 16-byte aligned,
+ *                  owned by the caller, contents on entry and exit
+ *                  unspecified; or NULL (workspace_bytes ignored).  With it,
+ *                  on layers whose heads all have at least 512 tiles, the
+ *                  query tiles at the end of each XCD's share are handed out
+ *                  through counters in it (reset by a small kernel on
+ *                  `stream` first), so that XCDs that run faster take them
+ *                  over; without it every tile keeps its fixed XCD.  The
+ *                  results are the same bits either way.  Calls sharing a
+ *                  workspace must be ordered on one stream.  Too small or
+ *                  misaligned: VEDA_ERR_INVALID_ARG.
  * A query row whose CSR row is empty gets O = 0 and lse = -inf.  Entries of
  * col_idx outside [0, n_tiles[hd]) are skipped.  Supported: (head_dim,
  * tile_size) in {(64,64), (128,128)}, 16-byte aligned tensors, max_tiles <=
@@ -231,7 +243,12 @@ int veda_score_select(const veda_layout* L, const float* phi, int32_t d_e,
 int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k_perm,
                          const void* vt_perm, const int32_t* row_ptr,
                          const int32_t* col_idx, float sm_scale, void* o_perm,
-                         float* lse, void* stream);
+                         float* lse, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes veda_sparse_attn_fwd and veda_sparse_attn_fwd_tokens use
+ * (the same for any layout: eight counters).  Host-only, no device work.
+ *  bytes  (host) output */
+int veda_sparse_attn_fwd_workspace(const veda_layout* L, int64_t* bytes);
 
 /* veda_sparse_attn_fwd with the inverse permutation folded into its
  * epilogue (Veda §2.3 tile-skipping kernel, §2.2 tiles): the same O values,
@@ -244,7 +261,8 @@ int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k
 int veda_sparse_attn_fwd_tokens(const veda_layout* L, const void* q_perm, const void* k_perm,
                                 const void* vt_perm, const int32_t* row_ptr,
                                 const int32_t* col_idx, float sm_scale, void* o,
-                                float* lse, void* stream);
+                                float* lse, void* workspace, int64_t workspace_bytes,
+                                void* stream);
 
 /* Backward of the tile-skipping attention (Veda §2.3 kernel; the pages
  * fine-tune with the sparse path in place but give no backward kernel): the

@@ -38,7 +38,8 @@ int launch_select(const DevLayout&, const float*, const int32_t*, int32_t*, int3
   return ++g_launches, VEDA_OK;
 }
 int launch_sparse_attn(const DevLayout&, const void*, const void*, const void*, const int32_t*,
-                       const int32_t*, float, void*, float*, bool, hipStream_t) {
+                       const int32_t*, float, void*, float*, bool, int* claim, hipStream_t) {
+  g_last_workspace = claim;
   return ++g_launches, VEDA_OK;
 }
 int launch_oracle_map(const DevLayout&, const void*, const void*, float, const int32_t*, int, void* ws,
@@ -196,14 +197,35 @@ int main() {
     EXPECT_CALL(veda_select_tiles(&Lw, F(1), kw, I(2), I(3), nullptr), VEDA_OK, 1);
   }
 
-  EXPECT_CALL(veda_sparse_attn_fwd(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(6), F(7), nullptr), VEDA_OK, 1);
-  EXPECT_CALL(veda_sparse_attn_fwd_tokens(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(6), nullptr, nullptr),
+  EXPECT_CALL(veda_sparse_attn_fwd(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(6), F(7), nullptr, 0,
+                                   nullptr), VEDA_OK, 1);
+  EXPECT_CALL(veda_sparse_attn_fwd_tokens(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(6), nullptr,
+                                          nullptr, 0, nullptr),
               VEDA_OK, 1);
-  EXPECT_CALL(veda_sparse_attn_fwd(&L, P(1), P(2), P(3), I(4), I(5), -1.f, P(6), F(7), nullptr),
+  {
+    // the optional workspace reaches the launch; too small or misaligned is rejected
+    int64_t aw = -1;
+    CHECK(veda_sparse_attn_fwd_workspace(&L, &aw) == VEDA_OK && aw == 256);
+    CHECK(veda_sparse_attn_fwd_workspace(&L, nullptr) == VEDA_ERR_INVALID_ARG);
+    EXPECT_CALL(veda_sparse_attn_fwd_tokens(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(6), nullptr,
+                                            P(8), aw, nullptr),
+                VEDA_OK, 1);
+    CHECK(veda::g_last_workspace == P(8));
+    EXPECT_CALL(veda_sparse_attn_fwd(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(6), F(7), P(8),
+                                     aw - 1, nullptr),
+                VEDA_ERR_INVALID_ARG, 0);
+    EXPECT_CALL(veda_sparse_attn_fwd(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(6), F(7),
+                                     static_cast<char*>(P(8)) + 4, aw, nullptr),
+                VEDA_ERR_INVALID_ARG, 0);
+  }
+  EXPECT_CALL(veda_sparse_attn_fwd(&L, P(1), P(2), P(3), I(4), I(5), -1.f, P(6), F(7), nullptr, 0,
+                                   nullptr),
               VEDA_ERR_INVALID_ARG, 0);
-  EXPECT_CALL(veda_sparse_attn_fwd(&L, P(1), P(2), nullptr, I(4), I(5), 0.088f, P(6), F(7), nullptr),
+  EXPECT_CALL(veda_sparse_attn_fwd(&L, P(1), P(2), nullptr, I(4), I(5), 0.088f, P(6), F(7), nullptr,
+                                   0, nullptr),
               VEDA_ERR_INVALID_ARG, 0);
-  EXPECT_CALL(veda_sparse_attn_fwd_tokens(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(1), nullptr, nullptr),
+  EXPECT_CALL(veda_sparse_attn_fwd_tokens(&L, P(1), P(2), P(3), I(4), I(5), 0.088f, P(1), nullptr,
+                                          nullptr, 0, nullptr),
               VEDA_ERR_INVALID_ARG, 0);
 
   int64_t ws = -1;
@@ -298,7 +320,7 @@ int main() {
     for (int h = 0; h < VEDA_MAX_HEADS; ++h) kk[h] = 1;
     veda_tile_permute(&R, VEDA_BF16, VEDA_FWD, P(1), P(2), nullptr);
     veda_select_tiles(&R, F(1), kk, I(2), I(3), nullptr);
-    veda_sparse_attn_fwd(&R, P(1), P(2), P(3), I(4), I(5), 0.1f, P(6), nullptr, nullptr);
+    veda_sparse_attn_fwd(&R, P(1), P(2), P(3), I(4), I(5), 0.1f, P(6), nullptr, nullptr, 0, nullptr);
     veda_oracle_maxpool_map_workspace(&R, 10, &ws);
     veda_sparse_attn_bwd_workspace(&R, 10, &ws);
   }

@@ -139,20 +139,36 @@ def test_device_calls_reject_before_launch(lib):
     # attention: nulls, NaN / zero / negative scale (the kernels scale the row
     # maximum of the raw logits, which is the maximum of the scaled logits only
     # for a positive scale), unsupported shape
-    assert lib.veda_sparse_attn_fwd(Lp, fake, fake, None, fake, fake, 0.1, fake, None, None) == -1
+    assert lib.veda_sparse_attn_fwd(Lp, fake, fake, None, fake, fake, 0.1, fake, None, None, 0, None) == -1
     for bad in (float("nan"), 0.0, -0.1, float("inf")):
-        assert lib.veda_sparse_attn_fwd(Lp, fake, fake, fake, fake, fake, bad, fake, None, None) == -1
+        assert lib.veda_sparse_attn_fwd(Lp, fake, fake, fake, fake, fake, bad, fake, None, None, 0,
+                                        None) == -1
     L3 = V.veda_layout_init(5, 9, 20, 96, 128, [(8, 4, 4)])
-    assert lib.veda_sparse_attn_fwd(ctypes.byref(L3), fake, fake, fake, fake, fake, 0.1, fake, None, None) == -2
+    assert lib.veda_sparse_attn_fwd(ctypes.byref(L3), fake, fake, fake, fake, fake, 0.1, fake, None, None,
+                                    0, None) == -2
+    # the optional workspace: its size query, too small, misaligned
+    ws = ctypes.c_int64(-1)
+    assert lib.veda_sparse_attn_fwd_workspace(Lp, ctypes.byref(ws)) == 0 and ws.value == 256
+    assert lib.veda_sparse_attn_fwd_workspace(Lp, None) == -1
+    assert lib.veda_sparse_attn_fwd_workspace(None, ctypes.byref(ws)) == -1
+    assert lib.veda_sparse_attn_fwd(Lp, fake, fake * 16, fake * 32, fake, fake, 0.1, fake * 64,
+                                    None, fake * 128, 255, None) == -1
+    assert lib.veda_sparse_attn_fwd(Lp, fake, fake * 16, fake * 32, fake, fake, 0.1, fake * 64,
+                                    None, fake * 128 + 4, 256, None) == -1
+    assert lib.veda_sparse_attn_fwd_tokens(Lp, fake, fake * 16, fake * 32, fake, fake, 0.1,
+                                           fake * 64, None, fake * 128, 8, None) == -1
     # token-order attention: same checks, plus an output overlapping an input
     A = lib.veda_sparse_attn_fwd_tokens
-    assert A(Lp, fake, fake, None, fake, fake, 0.1, fake * 64, None, None) == -1
+    assert A(Lp, fake, fake, None, fake, fake, 0.1, fake * 64, None, None, 0, None) == -1
     for bad in (float("nan"), 0.0, -0.1, float("inf")):
-        assert A(Lp, fake, fake * 16, fake * 32, fake, fake, bad, fake * 64, None, None) == -1
+        assert A(Lp, fake, fake * 16, fake * 32, fake, fake, bad, fake * 64, None, None, 0,
+                 None) == -1
     assert A(ctypes.byref(L3), fake, fake * 16, fake * 32, fake, fake, 0.1, fake * 64, None,
+             None, 0, None) == -2
+    assert A(Lp, fake, fake * 16, fake * 32, fake, fake, 0.1, fake * 64 + 8, None, None, 0,
              None) == -2
-    assert A(Lp, fake, fake * 16, fake * 32, fake, fake, 0.1, fake * 64 + 8, None, None) == -2
-    assert A(Lp, fake, fake * 16, fake * 32, fake, fake, 0.1, fake + 4096, None, None) == -1
+    assert A(Lp, fake, fake * 16, fake * 32, fake, fake, 0.1, fake + 4096, None, None, 0,
+             None) == -1
     # fused gather + TripPool: nulls, bad dtype, head_dim outside {64, 128},
     # misalignment, overlaps
     P = lib.veda_tile_permute_pool
@@ -392,7 +408,7 @@ def test_tiles_per_head_limit(lib):
     bad.max_tiles = 70000
     fake = 1 << 20
     assert lib.veda_sparse_attn_fwd(ctypes.byref(bad), fake, fake, fake, fake, fake, 0.1, fake,
-                                    None, None) == -1
+                                    None, None, 0, None) == -1
     assert lib.veda_oracle_maxpool_map_workspace(ctypes.byref(bad), 4, ctypes.byref(ws)) == -1
 
 

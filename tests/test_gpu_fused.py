@@ -147,6 +147,49 @@ def test_tile_score_from_desc_vs_oracle():
         assert np.abs(r.scores_head(h) - sref).max() <= 1e-4 * max(1.0, np.abs(sref).max()), h
 
 
+def test_attention_claimed_tiles_bit_identical():
+    """Heads of 512 tiles take the lockstep XCD order; with a workspace the
+    last tenth of each XCD's share of query tiles is handed out through its
+    counters.  O (token order, starting as NaN so that every element must be
+    written) and lse must be bit-identical to the call without a workspace,
+    on two calls in a row (the counters are reset by each call)."""
+    _say("attention with claimed tiles")
+    torch = need_gpu()
+    import tile_sparse_attention_head_amd as V
+    L = V.veda_layout_init(32, 32, 64, 128, 128, [(4, 4, 8), (2, 8, 8)])
+    assert min(L.n(h) for h in range(L.num_heads)) >= 512
+    g = torch.Generator(device="cuda").manual_seed(7)
+    n_tok, H, d = 32 * 32 * 64, L.num_heads, L.head_dim
+    q, k, v = (torch.randn(n_tok, H, d, generator=g, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    nt = V.tiles_numel(L)
+    qp, kp, vtp = (torch.empty(nt, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    V.veda_tile_permute(L, q, qp, V.VEDA_FWD)
+    V.veda_tile_permute(L, k, kp, V.VEDA_FWD)
+    V.veda_tile_permute(L, v, vtp, V.VEDA_FWD_T)
+    rng = np.random.default_rng(3)
+    kk = 26
+    cols = [np.sort(rng.choice(L.n(h), size=kk, replace=False)) for h in range(H)
+            for _ in range(L.n(h))]
+    ci = torch.from_numpy(np.concatenate(cols).astype(np.int32)).cuda()
+    rp = torch.from_numpy(np.arange(0, L.total_tiles * kk + 1, kk, dtype=np.int32)).cuda()
+    ws = torch.empty(V.veda_sparse_attn_fwd_workspace(L), dtype=torch.uint8, device="cuda")
+    sm = 1.0 / np.sqrt(d)
+
+    def run(workspace):
+        o = torch.full((n_tok, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((L.total_tiles * L.tile_size,), float("nan"), device="cuda")
+        V.veda_sparse_attn_fwd_tokens(L, qp, kp, vtp, rp, ci, sm, o, lse, workspace=workspace)
+        torch.cuda.synchronize()
+        return o.view(torch.int16), lse
+    o0, l0 = run(None)
+    assert not torch.isnan(o0.view(torch.bfloat16)).any()
+    for _ in range(2):
+        o1, l1 = run(ws)
+        assert torch.equal(o1, o0)
+        assert torch.equal(l1.view(torch.int32), l0.view(torch.int32))
+
+
 def test_tile_score_odd_width_and_unaligned_operands():
     """veda_tile_score with d_e = 50 (the score product's K is not a multiple
     of 4, nor of the 32-wide K step) on descriptors, weights, biases and phi

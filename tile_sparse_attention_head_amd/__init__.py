@@ -13,7 +13,8 @@ from ._lib import (  # noqa: F401
     veda_head_sq_error, veda_head_sq_error_workspace, veda_sparse_attn_bwd, veda_sparse_attn_bwd_tiles,
     veda_sparse_attn_bwd_workspace, status_string, tiles_numel, tokens_numel, veda_keep_count, veda_layout, veda_layout_init,
     veda_oracle_maxpool_map, veda_oracle_maxpool_map_workspace, veda_score_select, veda_select_tiles,
-    veda_sparse_attn_fwd, veda_sparse_attn_fwd_tokens, veda_tile_permute, veda_tile_permute_pool,
+    veda_sparse_attn_fwd, veda_sparse_attn_fwd_tokens, veda_sparse_attn_fwd_workspace,
+    veda_tile_permute, veda_tile_permute_pool,
     veda_tile_score, veda_tripool_score)
 from .layer import TileSparseAttention  # noqa: F401
 from .tiling_search import search_tile_shapes  # noqa: F401

@@ -90,9 +90,10 @@ def lib() -> ctypes.CDLL:
         "veda_select_tiles": (c_i32, [P, c_vp, ctypes.POINTER(c_i32), c_vp, c_vp, c_vp]),
         "veda_score_select": (c_i32, [P, c_vp, c_i32, ctypes.POINTER(c_i32), c_vp, c_vp, c_vp]),
         "veda_sparse_attn_fwd": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_vp, c_vp,
-                                         c_vp]),
+                                         c_vp, c_i64, c_vp]),
         "veda_sparse_attn_fwd_tokens": (c_i32, [P, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_vp,
-                                                c_vp, c_vp]),
+                                                c_vp, c_vp, c_i64, c_vp]),
+        "veda_sparse_attn_fwd_workspace": (c_i32, [P, ctypes.POINTER(c_i64)]),
         "veda_oracle_maxpool_map": (c_i32, [P, c_vp, c_vp, c_f32, c_vp, c_i32, c_vp, c_i64,
                                             c_vp, c_vp, c_vp]),
         "veda_oracle_maxpool_map_workspace": (c_i32, [P, c_i32, ctypes.POINTER(c_i64)]),
@@ -298,8 +299,31 @@ def veda_score_select(L: veda_layout, phi, d_e: int, k_per_head: Sequence[int], 
            "veda_score_select")
 
 
+def veda_sparse_attn_fwd_workspace(L: veda_layout) -> int:
+    """Bytes of device workspace the attention forward calls use."""
+    out = c_i64(0)
+    _check(lib().veda_sparse_attn_fwd_workspace(ctypes.byref(L), ctypes.byref(out)),
+           "veda_sparse_attn_fwd_workspace")
+    return int(out.value)
+
+
+def _attn_workspace(L: veda_layout, workspace):
+    """(pointer, bytes) of an optional attention workspace tensor."""
+    if workspace is None:
+        return None, 0
+    need = veda_sparse_attn_fwd_workspace(L)
+    pw = _dev(workspace, "workspace", None, 0)
+    have = workspace.numel() * workspace.element_size()
+    if have < need:
+        raise ValueError(f"workspace holds {have} bytes, needs {need}")
+    return pw, have
+
+
 def veda_sparse_attn_fwd(L: veda_layout, q_perm, k_perm, vt_perm, row_ptr, col_idx,
-                         sm_scale: float, o_perm, lse=None, stream=None) -> None:
+                         sm_scale: float, o_perm, lse=None, workspace=None, stream=None) -> None:
+    """workspace: None, or a contiguous GPU tensor of at least
+    veda_sparse_attn_fwd_workspace(L) bytes (the end of each XCD's share of
+    query tiles is then balanced across XCDs; the results are the same)."""
     torch = _torch()
     bf = torch.bfloat16
     n = tiles_numel(L)
@@ -309,13 +333,15 @@ def veda_sparse_attn_fwd(L: veda_layout, q_perm, k_perm, vt_perm, row_ptr, col_i
             _dev(col_idx, "col_idx", torch.int32, 0)]
     po = _dev(o_perm, "o_perm", bf, n)
     pl = _dev(lse, "lse", torch.float32, L.total_tiles * L.tile_size, True)
-    _check(lib().veda_sparse_attn_fwd(ctypes.byref(L), *args, float(sm_scale), po, pl,
+    pw, have = _attn_workspace(L, workspace)
+    _check(lib().veda_sparse_attn_fwd(ctypes.byref(L), *args, float(sm_scale), po, pl, pw, have,
                                       _stream(stream)),
            "veda_sparse_attn_fwd")
 
 
 def veda_sparse_attn_fwd_tokens(L: veda_layout, q_perm, k_perm, vt_perm, row_ptr, col_idx,
-                                sm_scale: float, o, lse=None, stream=None) -> None:
+                                sm_scale: float, o, lse=None, workspace=None,
+                                stream=None) -> None:
     """As veda_sparse_attn_fwd, with O written in token order [N][heads][d]."""
     torch = _torch()
     bf = torch.bfloat16
@@ -326,8 +352,9 @@ def veda_sparse_attn_fwd_tokens(L: veda_layout, q_perm, k_perm, vt_perm, row_ptr
             _dev(col_idx, "col_idx", torch.int32, 0)]
     po = _dev(o, "o", bf, tokens_numel(L))
     pl = _dev(lse, "lse", torch.float32, L.total_tiles * L.tile_size, True)
-    _check(lib().veda_sparse_attn_fwd_tokens(ctypes.byref(L), *args, float(sm_scale), po, pl,
-                                             _stream(stream)),
+    pw, have = _attn_workspace(L, workspace)
+    _check(lib().veda_sparse_attn_fwd_tokens(ctypes.byref(L), *args, float(sm_scale), po, pl, pw,
+                                             have, _stream(stream)),
            "veda_sparse_attn_fwd_tokens")
 
 

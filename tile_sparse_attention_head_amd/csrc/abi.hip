@@ -359,21 +359,32 @@ int veda_select_tiles(const veda_layout* L, const float* scores, const int32_t* 
                 stream);
 }
 
+int veda_sparse_attn_fwd_workspace(const veda_layout* L, int64_t* bytes) {
+  if (L == nullptr || bytes == nullptr || !layout_ok(L)) return VEDA_ERR_INVALID_ARG;
+  *bytes = kAttnWorkspaceBytes;
+  return VEDA_OK;
+}
+
 int veda_sparse_attn_fwd(const veda_layout* L, const void* q_perm, const void* k_perm,
                          const void* vt_perm, const int32_t* row_ptr, const int32_t* col_idx,
-                         float sm_scale, void* o_perm, float* lse, void* stream) {
+                         float sm_scale, void* o_perm, float* lse, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  if (workspace != nullptr && (workspace_bytes < kAttnWorkspaceBytes || !aligned16(workspace)))
+    return VEDA_ERR_INVALID_ARG;
   const int st = attn_args(L, q_perm, k_perm, vt_perm, row_ptr, col_idx, sm_scale, o_perm, stream);
   if (st != VEDA_OK) return st;
   const DevLayout dl = make_dev_layout(L);
   return finish(launch_sparse_attn(dl, q_perm, k_perm, vt_perm, row_ptr, col_idx, sm_scale, o_perm,
-                                   lse, false, (hipStream_t)stream),
+                                   lse, false, static_cast<int*>(workspace), (hipStream_t)stream),
                 stream);
 }
 
 int veda_sparse_attn_fwd_tokens(const veda_layout* L, const void* q_perm, const void* k_perm,
                                 const void* vt_perm, const int32_t* row_ptr,
                                 const int32_t* col_idx, float sm_scale, void* o, float* lse,
-                                void* stream) {
+                                void* workspace, int64_t workspace_bytes, void* stream) {
+  if (workspace != nullptr && (workspace_bytes < kAttnWorkspaceBytes || !aligned16(workspace)))
+    return VEDA_ERR_INVALID_ARG;
   const int st = attn_args(L, q_perm, k_perm, vt_perm, row_ptr, col_idx, sm_scale, o, stream);
   if (st != VEDA_OK) return st;
   const size_t tok = (size_t)L->T * L->H * L->W * L->num_heads * L->head_dim * 2;
@@ -383,7 +394,7 @@ int veda_sparse_attn_fwd_tokens(const veda_layout* L, const void* q_perm, const 
     return VEDA_ERR_INVALID_ARG;
   const DevLayout dl = make_dev_layout(L);
   return finish(launch_sparse_attn(dl, q_perm, k_perm, vt_perm, row_ptr, col_idx, sm_scale, o, lse,
-                                   true, (hipStream_t)stream),
+                                   true, static_cast<int*>(workspace), (hipStream_t)stream),
                 stream);
 }
 

@@ -76,12 +76,44 @@ struct Pipe {
 
 // TOK: O is written in token order ([N][heads][D], real slots only) instead
 // of tile order, which folds the inverse permutation into the epilogue.
+// Work claiming at the end of the lockstep order.  XCD x's run has len[x]
+// tiles; workgroup b = 8 i + x with i < fixed[x] takes run position i as
+// before, and the last len[x] - fixed[x] positions (about a tenth) are handed
+// out through counter x of the caller's workspace: a workgroup past fixed[x]
+// takes the next unclaimed position of its own XCD's tail, else of the next
+// XCD's tail that has one left (x+1, x+2, ... mod 8), else nothing (-1).  The
+// counters only grow and a tail is only passed over once its counter has
+// reached its length, so every position goes to exactly one workgroup.  The
+// XCDs do not all run at the same speed (on one box the odd ones took 2.5 %
+// longer per tile); with fixed shares the last of them finished 1.5 ms after
+// the first.
+struct ClaimPlan {
+  int len[8];
+  int fixed[8];
+};
+
+__device__ __forceinline__ int64_t claim_tail_tile(const DevLayout& L, int* claim,
+                                                   const ClaimPlan& plan, int x) {
+  for (int o = 0; o < 8; ++o) {
+    const int y = (x + o) & 7;
+    const int tail = plan.len[y] - plan.fixed[y];
+    if (__hip_atomic_load(&claim[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= tail) continue;
+    const int c = atomicAdd(&claim[y], 1);
+    if (c < tail) return lockstep_tile(L, (int64_t)(plan.fixed[y] + c) * 8 + y);
+  }
+  return -1;
+}
+
+__global__ void attn_claim_reset_kernel(int* claim) {
+  if (threadIdx.x < 8) claim[threadIdx.x] = 0;
+}
+
 template <int D, int S, bool TOK>
 __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     DevLayout L, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ vt, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, float scale_log2, __bf16* __restrict__ o,
-    float* __restrict__ lse, int lockstep) {
+    float* __restrict__ lse, int lockstep, int* __restrict__ claim, ClaimPlan plan) {
   using P = Pipe<D, S>;
   using KB = typename P::KBuf;
   using VB = typename P::VBuf;
@@ -95,8 +127,22 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char v1[VB::BYTES];
   __shared__ BiasTable<SPT, 9> btab;
 
-  const int64_t g = lockstep ? lockstep_tile(L, blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
-  if (g < 0) return;   // past the end of this XCD's run
+  int64_t g;
+  if (!lockstep) {
+    g = xcd_remap(blockIdx.x, gridDim.x);
+  } else {
+    const int x = (int)(blockIdx.x & 7);
+    const int i = (int)(blockIdx.x >> 3);
+    if (claim == nullptr || i < plan.fixed[x]) {
+      g = lockstep_tile(L, blockIdx.x);
+    } else {
+      __shared__ int64_t g_s;
+      if (threadIdx.x == 0) g_s = claim_tail_tile(L, claim, plan, x);
+      __syncthreads();
+      g = g_s;
+    }
+  }
+  if (g < 0) return;   // past the end of this XCD's run, or nothing left to claim
   const int h = head_of_tile(L, g);
   const int n_h = (int)(L.tile_off[h + 1] - L.tile_off[h]);
   const int64_t head_base = L.tile_off[h];
@@ -404,33 +450,52 @@ namespace {
 template <bool TOK>
 void launch_attn(const DevLayout& L, const void* q, const void* k, const void* vt,
                  const int32_t* row_ptr, const int32_t* col_idx, float scale_log2, void* o,
-                 float* lse, hipStream_t s) {
+                 float* lse, int* claim, hipStream_t s) {
   int min_tiles = INT32_MAX;
   for (int h = 0; h < L.heads; ++h)
     min_tiles = std::min<int>(min_tiles, (int)(L.tile_off[h + 1] - L.tile_off[h]));
   const int lockstep = min_tiles >= kLockstepTiles;
-  const unsigned G = (unsigned)(lockstep ? lockstep_grid(L) : L.tile_off[L.heads]);
+  unsigned G = (unsigned)(lockstep ? lockstep_grid(L) : L.tile_off[L.heads]);
+  ClaimPlan plan{};
+  if (!lockstep) claim = nullptr;
+  if (claim != nullptr) {
+    // the last tenth of every XCD's run is claimed; each XCD gets spare
+    // workgroups for twice its own tail, to take over other XCDs' tails
+    int most = 0;
+    for (int x = 0; x < 8; ++x) {
+      int64_t len = 0;
+      for (int h = 0; h < L.heads; ++h) {
+        const int64_t n = L.tile_off[h + 1] - L.tile_off[h];
+        len += n * (x + 1) / 8 - n * x / 8;
+      }
+      plan.len[x] = (int)len;
+      plan.fixed[x] = (int)(len - (len + 9) / 10);
+      most = std::max(most, plan.fixed[x] + 2 * (plan.len[x] - plan.fixed[x]));
+    }
+    G = 8u * (unsigned)most;
+    hipLaunchKernelGGL(attn_claim_reset_kernel, dim3(1), dim3(64), 0, s, claim);
+  }
   if (L.d == 128) {
     hipLaunchKernelGGL((sparse_attn_fwd_kernel<128, 128, TOK>), dim3(G), dim3(256), 0, s,
                        L, (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, row_ptr, col_idx,
-                       scale_log2, (__bf16*)o, lse, lockstep);
+                       scale_log2, (__bf16*)o, lse, lockstep, claim, plan);
   } else {
     hipLaunchKernelGGL((sparse_attn_fwd_kernel<64, 64, TOK>), dim3(G), dim3(128), 0, s, L,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, row_ptr, col_idx,
-                       scale_log2, (__bf16*)o, lse, lockstep);
+                       scale_log2, (__bf16*)o, lse, lockstep, claim, plan);
   }
 }
 }  // namespace
 
 int launch_sparse_attn(const DevLayout& L, const void* q, const void* k, const void* vt,
                        const int32_t* row_ptr, const int32_t* col_idx, float sm_scale, void* o,
-                       float* lse, bool tokens, hipStream_t s) {
+                       float* lse, bool tokens, int* claim, hipStream_t s) {
   if (L.tile_off[L.heads] == 0) return VEDA_OK;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   if (tokens)
-    launch_attn<true>(L, q, k, vt, row_ptr, col_idx, scale_log2, o, lse, s);
+    launch_attn<true>(L, q, k, vt, row_ptr, col_idx, scale_log2, o, lse, claim, s);
   else
-    launch_attn<false>(L, q, k, vt, row_ptr, col_idx, scale_log2, o, lse, s);
+    launch_attn<false>(L, q, k, vt, row_ptr, col_idx, scale_log2, o, lse, claim, s);
   return launch_status();
 }
 

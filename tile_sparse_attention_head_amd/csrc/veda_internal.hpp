@@ -98,9 +98,12 @@ int launch_select(const DevLayout& L, const float* scores, const int32_t* k_host
 int launch_score_select(const DevLayout& L, const float* phi, int d_e, const int32_t* k_host,
                         int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
 int score_select_max_cols();
+// claim: 8 work counters in the caller's workspace, or nullptr (fixed
+// XCD shares)
+constexpr int64_t kAttnWorkspaceBytes = 256;
 int launch_sparse_attn(const DevLayout& L, const void* q, const void* k, const void* vt,
                        const int32_t* row_ptr, const int32_t* col_idx, float sm_scale,
-                       void* o, float* lse, bool tokens, hipStream_t s);
+                       void* o, float* lse, bool tokens, int* claim, hipStream_t s);
 int launch_oracle_map(const DevLayout& L, const void* q, const void* k, float sm_scale,
                       const int32_t* q_tiles, int n_sub, void* workspace, float* lse,
                       float* map, hipStream_t s);

@@ -57,6 +57,10 @@ class TileSparseAttention:
         self._map_ws = None   # veda_oracle_maxpool_map workspace, sized on first use
         self._distill_ws = None   # veda_distill_grad workspace, sized on first use
         self._bwd_ws = None       # veda_sparse_attn_bwd workspace, sized on first use
+        # the attention forward's work counters (calls on one layer are ordered
+        # on one stream)
+        self._attn_ws = torch.empty(V.veda_sparse_attn_fwd_workspace(L), dtype=torch.uint8,
+                                    device=dev)
         self.desc = torch.empty(2 * L.total_tiles * 3 * head_dim, dtype=f32, device=dev)
         self.phi = torch.empty(2 * L.total_tiles * self.d_e, dtype=f32, device=dev)
         self.scores = torch.empty(L.total_scores, dtype=f32, device=dev)
@@ -80,7 +84,8 @@ class TileSparseAttention:
     def attend(self, sm_scale: float, with_lse: bool = True, stream=None):
         V.veda_sparse_attn_fwd(self.L, self.q_perm, self.k_perm, self.vt_perm, self.row_ptr,
                                self.col_idx, sm_scale, self.o_perm,
-                               self.lse if with_lse else None, stream)
+                               self.lse if with_lse else None, workspace=self._attn_ws,
+                               stream=stream)
 
     def unpermute(self, out, stream=None):
         V.veda_tile_permute(self.L, self.o_perm, out, V.VEDA_INV, stream)
@@ -108,7 +113,8 @@ class TileSparseAttention:
     def attend_tokens(self, sm_scale: float, out, with_lse: bool = True, stream=None):
         V.veda_sparse_attn_fwd_tokens(self.L, self.q_perm, self.k_perm, self.vt_perm,
                                       self.row_ptr, self.col_idx, sm_scale, out,
-                                      self.lse if with_lse else None, stream)
+                                      self.lse if with_lse else None, workspace=self._attn_ws,
+                                      stream=stream)
 
     # whole layer -----------------------------------------------------------
     def forward(self, q, k, v, w_q, w_k, sm_scale: float, out=None, b_q=None, b_k=None,
