@@ -41,7 +41,9 @@
 // are a contiguous run of that head (neighbours whose kept key tiles overlap
 // in its L2).  With smaller heads, one eighth of a head is shorter than the
 // workgroups an XCD runs at once, and each XCD takes a contiguous eighth of
-// the layer instead.
+// the layer instead.  Either way XCD x has a run of tiles; with a workspace
+// the last tenth of every run is handed out through counters to whichever
+// XCD gets there first (see claim_tail_tile).
 #include <algorithm>
 #include <climits>
 
@@ -92,14 +94,22 @@ struct ClaimPlan {
   int fixed[8];
 };
 
-__device__ __forceinline__ int64_t claim_tail_tile(const DevLayout& L, int* claim,
+// Tile at position i of XCD x's run: the lockstep order, or the x-th
+// contiguous eighth of the layer's tiles.
+__device__ __forceinline__ int64_t run_tile(const DevLayout& L, int lockstep, int x, int i) {
+  if (lockstep) return lockstep_tile(L, (int64_t)i * 8 + x);
+  const int64_t G = L.tile_off[L.heads];
+  return xcd_remap((int64_t)i * 8 + x, G);
+}
+
+__device__ __forceinline__ int64_t claim_tail_tile(const DevLayout& L, int lockstep, int* claim,
                                                    const ClaimPlan& plan, int x) {
   for (int o = 0; o < 8; ++o) {
     const int y = (x + o) & 7;
     const int tail = plan.len[y] - plan.fixed[y];
     if (__hip_atomic_load(&claim[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= tail) continue;
     const int c = atomicAdd(&claim[y], 1);
-    if (c < tail) return lockstep_tile(L, (int64_t)(plan.fixed[y] + c) * 8 + y);
+    if (c < tail) return run_tile(L, lockstep, y, plan.fixed[y] + c);
   }
   return -1;
 }
@@ -128,19 +138,17 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   __shared__ BiasTable<SPT, 9> btab;
 
   int64_t g;
-  if (!lockstep) {
-    g = xcd_remap(blockIdx.x, gridDim.x);
+  const int x = (int)(blockIdx.x & 7);
+  const int i = (int)(blockIdx.x >> 3);
+  if (claim == nullptr) {
+    g = lockstep ? lockstep_tile(L, blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+  } else if (i < plan.fixed[x]) {
+    g = run_tile(L, lockstep, x, i);
   } else {
-    const int x = (int)(blockIdx.x & 7);
-    const int i = (int)(blockIdx.x >> 3);
-    if (claim == nullptr || i < plan.fixed[x]) {
-      g = lockstep_tile(L, blockIdx.x);
-    } else {
-      __shared__ int64_t g_s;
-      if (threadIdx.x == 0) g_s = claim_tail_tile(L, claim, plan, x);
-      __syncthreads();
-      g = g_s;
-    }
+    __shared__ int64_t g_s;
+    if (threadIdx.x == 0) g_s = claim_tail_tile(L, lockstep, claim, plan, x);
+    __syncthreads();
+    g = g_s;
   }
   if (g < 0) return;   // past the end of this XCD's run, or nothing left to claim
   const int h = head_of_tile(L, g);
@@ -457,16 +465,19 @@ void launch_attn(const DevLayout& L, const void* q, const void* k, const void* v
   const int lockstep = min_tiles >= kLockstepTiles;
   unsigned G = (unsigned)(lockstep ? lockstep_grid(L) : L.tile_off[L.heads]);
   ClaimPlan plan{};
-  if (!lockstep) claim = nullptr;
   if (claim != nullptr) {
     // the last tenth of every XCD's run is claimed; each XCD gets spare
     // workgroups for twice its own tail, to take over other XCDs' tails
     int most = 0;
+    const int64_t G_all = L.tile_off[L.heads];
     for (int x = 0; x < 8; ++x) {
-      int64_t len = 0;
-      for (int h = 0; h < L.heads; ++h) {
-        const int64_t n = L.tile_off[h + 1] - L.tile_off[h];
-        len += n * (x + 1) / 8 - n * x / 8;
+      int64_t len = G_all / 8 + (x < G_all % 8 ? 1 : 0);
+      if (lockstep) {
+        len = 0;
+        for (int h = 0; h < L.heads; ++h) {
+          const int64_t n = L.tile_off[h + 1] - L.tile_off[h];
+          len += n * (x + 1) / 8 - n * x / 8;
+        }
       }
       plan.len[x] = (int)len;
       plan.fixed[x] = (int)(len - (len + 9) / 10);
