@@ -528,8 +528,9 @@ def stage_record(b, per):
     return med, pct
 
 
-def layer_summary(b, med, wall_ms):
-    """The metric's figures for one timed run of a Bench."""
+def layer_summary(b, med, wall_ms, with_map=True):
+    """The metric's figures for one timed run of a Bench (the map's only when
+    the run included it)."""
     attn = med["sparse_attn"]
     layer_ms = sum(med[n] for n in b.stages if n != "map")
     out = {"step_ms_wall": wall_ms, "ms_per_layer": layer_ms,
@@ -537,7 +538,7 @@ def layer_summary(b, med, wall_ms):
            "attn_frac_peak": b.flops_c / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
            "layer_tflops_effective": b.flops_c / (layer_ms * 1e-3) / 1e12,
            "kept_pairs": b.pairs, "kept_tiles_per_row": sorted(set(b.layer.k_per_head))}
-    if "map" in med and b.flops_d > 0 and med["map"] > 0:
+    if with_map and "map" in med and b.flops_d > 0 and med["map"] > 0:
         out.update({"map_ms": med["map"], "map_tflops": b.flops_d / (med["map"] * 1e-3) / 1e12,
                     "map_frac_peak": b.flops_d / (med["map"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                     "map_subset_tiles": int(sum(b.n_sub)),
@@ -640,7 +641,7 @@ def main():
         c = Bench(args.workload, 0, wl=b.wl)
         c_ms, _, cper = c.run(3, 1, with_map=False, flush=flush)
         cmed, _ = stage_record(c, cper)
-        context["sparsity_0"] = layer_summary(c, cmed, c_ms)
+        context["sparsity_0"] = layer_summary(c, cmed, c_ms, with_map=False)
         context["attn_speedup_vs_dense"] = cmed["sparse_attn"] / st["sparse_attn"]
         context["density"] = b.pairs / c.pairs
         del c
