@@ -228,9 +228,8 @@ int veda_score_select(const veda_layout* L, const float* phi, int32_t d_e,
  *                  veda_sparse_attn_fwd_workspace(L) bytes, 16-byte aligned,
  *                  owned by the caller, contents on entry and exit
  *                  unspecified; or NULL (workspace_bytes ignored).  With it,
- *                  on layers whose heads all have at least 512 tiles, the
- *                  query tiles at the end of each XCD's share are handed out
- *                  through counters in it (reset by a small kernel on
+ *                  the query tiles at the end of each XCD's share are handed
+ *                  out through counters in it (reset by a small kernel on
  *                  `stream` first), so that XCDs that run faster take them
  *                  over; without it every tile keeps its fixed XCD.  The
  *                  results are the same bits either way.  Calls sharing a
