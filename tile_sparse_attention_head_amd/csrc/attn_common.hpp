@@ -201,11 +201,13 @@ __device__ __forceinline__ void build_bias_table(BiasTable<SPT, NCUT>& bt, const
   const int ew = L.W - (L.grid[h][2] - 1) * pw;
   float* flat = reinterpret_cast<float*>(&bt);
   constexpr int ENTRIES = NCUT * SPT * 2 * 2 * 16;
+  const float rpw = small_rcp(pw), rph = small_rcp(ph);
   for (int x = tid; x < ENTRIES; x += nthreads) {
     const int i = x & 15, hf = (x >> 4) & 1, b = (x >> 5) & 1, half = (x >> 6) % SPT;
     const int cut = (x >> 6) / SPT;
     const int u = half * 64 + 32 * b + 16 * (i >> 3) + 8 * hf + (i & 7);   // slot in tile
-    const int dw = u % pw, r = u / pw, dh = r % ph, dt = r / ph;
+    const int r = small_div(u, rpw), dw = u - r * pw;
+    const int dt = small_div(r, rph), dh = r - dt * ph;
     const bool ok = cut < 8 && (!(cut & 4) || dt < et) && (!(cut & 2) || dh < eh) &&
                     (!(cut & 1) || dw < ew);
     flat[x] = ok ? 0.f : -INFINITY;

@@ -137,7 +137,8 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
   const int nH = L.grid[h][1], nW = L.grid[h][2], nT = L.grid[h][0];
   const bool part_t = L.T % L.shape[h][0] != 0, part_h = L.H % L.shape[h][1] != 0,
              part_w = L.W % L.shape[h][2] != 0;
-  int kw = j0 % nW, kh = (j0 / nW) % nH, kt = j0 / (nW * nH);
+  const TileExtent e0 = tile_extent(L, h, j0);
+  int kw = e0.iw, kh = e0.ih, kt = e0.it;
   int qcut = 0;
   // cut of the tile of step t (called once per step, in order)
   auto cut_at = [&](int t) -> int {
@@ -191,8 +192,8 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
         opnd[i % (LA + 1)] = operand(i);
       });
     }
-    float pm[4], e[32];
-    float mxs = 0.f, m_new = 0.f, neg_m = 0.f, psum0 = 0.f, psum1 = 0.f;
+    float e[32];
+    float mx = 0.f, mxs = 0.f, m_new = 0.f, psum0 = 0.f, psum1 = 0.f;
     bool raise = false;
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, NSLOT>([&](auto ic) {
@@ -208,26 +209,28 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
         else
           snext[i & 1] = mfma32(opnd[i % (LA + 1)], qr[i >> 1], snext[i & 1]);
       }
-      // statistics of step s: row maximum in slots 0..4, then the elements
+      // statistics of step s: row maximum in slots 0..4 (one chain of
+      // three-operand maxima over the lane's 32 logits), then the elements
       if constexpr (i < 4) {
         constexpr int bb = i >> 1, o8 = (i & 1) * 8;
-        float x = fmaxf(fmaxf(scur[bb][o8], scur[bb][o8 + 1]), scur[bb][o8 + 2]);
-        x = fmaxf(fmaxf(x, scur[bb][o8 + 3]), scur[bb][o8 + 4]);
-        x = fmaxf(fmaxf(x, scur[bb][o8 + 5]), scur[bb][o8 + 6]);
-        pm[i] = fmaxf(x, scur[bb][o8 + 7]);
-        asm volatile("" : "+v"(pm[i]));
+        float x = i == 0 ? fmaxf(scur[bb][o8], scur[bb][o8 + 1])
+                         : fmaxf(fmaxf(mx, scur[bb][o8]), scur[bb][o8 + 1]);
+        x = fmaxf(fmaxf(x, scur[bb][o8 + 2]), scur[bb][o8 + 3]);
+        x = fmaxf(fmaxf(x, scur[bb][o8 + 4]), scur[bb][o8 + 5]);
+        mx = fmaxf(fmaxf(x, scur[bb][o8 + 6]), scur[bb][o8 + 7]);
+        asm volatile("" : "+v"(mx));
       }
       if constexpr (i == 3) {
-        mxs = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
-        mxs = swap32_max(mxs) * scale_log2;
+        mxs = swap32_max(mx) * scale_log2;
         asm volatile("" : "+v"(mxs));
       }
+      // the reference is held as m_new; its negation is a source modifier of
+      // the FMAs below, not an instruction of its own
       if constexpr (i == 4) {
         const float m_cand = fmaxf(m_run, mxs);
         raise = m_cand > m_thr;
         m_new = raise ? m_cand : m_run;
-        neg_m = -m_new;
-        asm volatile("" : "+v"(neg_m));
+        asm volatile("" : "+v"(m_new));
       }
       // element pairs: FMA in slot fs(k), exp in fs(k)+1, sum in fs(k)+2
       static_for<0, 16>([&](auto kc_) {
@@ -235,8 +238,8 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
         constexpr int f = 5 + (kp * (NSLOT - 7)) / 16;
         constexpr int el0 = 2 * kp, bb = el0 >> 4, ii = el0 & 15;
         if constexpr (f == i) {
-          e[el0] = fmaf(scur[bb][ii], scale_log2, neg_m);
-          e[el0 + 1] = fmaf(scur[bb][ii + 1], scale_log2, neg_m);
+          e[el0] = fmaf(scur[bb][ii], scale_log2, -m_new);
+          e[el0 + 1] = fmaf(scur[bb][ii + 1], scale_log2, -m_new);
           asm volatile("" : "+v"(e[el0]), "+v"(e[el0 + 1]));
         }
         if constexpr (f + 1 == i) {
@@ -245,8 +248,9 @@ __global__ __launch_bounds__(2 * S, 3) void map_stats_kernel(
           asm volatile("" : "+v"(e[el0]), "+v"(e[el0 + 1]));
         }
         if constexpr (f + 2 == i) {
-          psum0 += e[el0];
-          psum1 += e[el0 + 1];
+          // the first pair starts the two sums (0 + e is e: no add)
+          psum0 = kp == 0 ? e[el0] : psum0 + e[el0];
+          psum1 = kp == 0 ? e[el0 + 1] : psum1 + e[el0 + 1];
           asm volatile("" : "+v"(psum0), "+v"(psum1));
         }
       });

@@ -23,10 +23,8 @@ constexpr int kBatch = 8;   // chunks a lane loads before it stores any
 struct Chunk { uint32_t x, y, z, w; };
 
 __device__ __forceinline__ int64_t token_of_slot(const DevLayout& L, const TileExtent& e, int u) {
-  const int dw = u % e.pw;
-  const int r = u / e.pw;
-  const int dh = r % e.ph;
-  const int dt = r / e.ph;
+  int dt, dh, dw;
+  e.slot_coords(u, dt, dh, dw);
   if (dt >= e.lt || dh >= e.lh || dw >= e.lw) return -1;
   const int64_t t = (int64_t)e.it * e.pt + dt;
   const int64_t h = (int64_t)e.ih * e.ph + dh;

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
     const int p = beg + base + lane;
     const int c = p < end ? col_idx[p] : -1;
     const bool ok = c >= 0 && c < n_h;
-    const int cut = ok ? cut_of(tile_extent(L, h, c)) : 8;
+    const int cut = ok ? cut_of(tile_extent(L, h, ok ? c : 0)) : 8;
     win = (ok ? c : 0) | (cut << 16);
     wbase = base;
   };
@@ -264,8 +264,8 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
       if constexpr (has_mfma(i)) opnd[i % (LA + 1)] = operand(i);
     });
 
-    float pm[4], e[32];
-    float mxs = 0.f, m_new = 0.f, neg_m = 0.f, psum0 = 0.f, psum1 = 0.f;
+    float e[32];
+    float mx = 0.f, mxs = 0.f, m_new = 0.f, psum0 = 0.f, psum1 = 0.f;
     bool raise = false;
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, NSLOT>([&](auto ic) {
@@ -284,26 +284,28 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
         if constexpr (i & 1) oacc[j % DB] = mfma32(opnd[i % (LA + 1)], pprev[j / DB], oacc[j % DB]);
         else snext[j & 1] = mfma32(opnd[i % (LA + 1)], qr[j >> 1], j < 2 ? f32x16{} : snext[j & 1]);
       }
-      // softmax(s): row maximum in slots 0..4, then the elements
+      // softmax(s): row maximum in slots 0..4 (one chain of three-operand
+      // maxima over the lane's 32 logits), then the elements
       if constexpr (i < 4) {
         constexpr int b = i >> 1, o8 = (i & 1) * 8;
-        float x = fmaxf(fmaxf(scur[b][o8], scur[b][o8 + 1]), scur[b][o8 + 2]);
-        x = fmaxf(fmaxf(x, scur[b][o8 + 3]), scur[b][o8 + 4]);
-        x = fmaxf(fmaxf(x, scur[b][o8 + 5]), scur[b][o8 + 6]);
-        pm[i] = fmaxf(x, scur[b][o8 + 7]);
-        asm volatile("" : "+v"(pm[i]));
+        float x = i == 0 ? fmaxf(scur[b][o8], scur[b][o8 + 1])
+                         : fmaxf(fmaxf(mx, scur[b][o8]), scur[b][o8 + 1]);
+        x = fmaxf(fmaxf(x, scur[b][o8 + 2]), scur[b][o8 + 3]);
+        x = fmaxf(fmaxf(x, scur[b][o8 + 4]), scur[b][o8 + 5]);
+        mx = fmaxf(fmaxf(x, scur[b][o8 + 6]), scur[b][o8 + 7]);
+        asm volatile("" : "+v"(mx));
       }
       if constexpr (i == 3) {
-        mxs = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
-        mxs = swap32_max(mxs);
+        mxs = swap32_max(mx);
         asm volatile("" : "+v"(mxs));
       }
+      // the reference is held as m_new; its negation is a source modifier of
+      // the FMAs below, not an instruction of its own
       if constexpr (i == 4) {
         const float m_cand = fmaxf(m_run, mxs * scale_log2);
         raise = m_cand > m_thr;
         m_new = raise ? m_cand : m_run;
-        neg_m = -m_new;
-        asm volatile("" : "+v"(neg_m));
+        asm volatile("" : "+v"(m_new));
       }
       // element pairs get their FMAs in slot fs(k), exps in fs(k)+1, sums and
       // bf16 conversion in fs(k)+2; an empty asm statement pins each value to
@@ -313,8 +315,8 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
         constexpr int f = 5 + (kp * (NSLOT - 7)) / 16;
         constexpr int el0 = 2 * kp, b = el0 >> 4, ii = el0 & 15;
         if constexpr (f == i) {
-          e[el0] = fmaf(scur[b][ii], scale_log2, neg_m);
-          e[el0 + 1] = fmaf(scur[b][ii + 1], scale_log2, neg_m);
+          e[el0] = fmaf(scur[b][ii], scale_log2, -m_new);
+          e[el0 + 1] = fmaf(scur[b][ii + 1], scale_log2, -m_new);
           asm volatile("" : "+v"(e[el0]), "+v"(e[el0 + 1]));
         }
         if constexpr (f + 1 == i) {
@@ -323,8 +325,9 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
           asm volatile("" : "+v"(e[el0]), "+v"(e[el0 + 1]));
         }
         if constexpr (f + 2 == i) {
-          psum0 += e[el0];
-          psum1 += e[el0 + 1];
+          // the first pair starts the two sums (0 + e is e: no add)
+          psum0 = kp == 0 ? e[el0] : psum0 + e[el0];
+          psum1 = kp == 0 ? e[el0 + 1] : psum1 + e[el0 + 1];
           pcur[2 * b + (ii >> 3)][ii & 7] = (__bf16)e[el0];
           pcur[2 * b + (ii >> 3)][(ii & 7) + 1] = (__bf16)e[el0 + 1];
           // the bf16 conversion stays in this slot: left to itself the
@@ -430,8 +433,8 @@ __global__ __launch_bounds__(2 * S, 2) void sparse_attn_fwd_kernel(
   int64_t orow_i = qrow;
   if constexpr (TOK) {
     const TileExtent& e = eq;
-    const int u = wave * 32 + n;   // slot = (dt*ph + dh)*pw + dw
-    const int dw = u % e.pw, r = u / e.pw, dh = r % e.ph, dt = r / e.ph;
+    int dt, dh, dw;
+    e.slot_coords(wave * 32 + n, dt, dh, dw);
     const int64_t tok =
         ((int64_t)(e.it * e.pt + dt) * L.H + (e.ih * e.ph + dh)) * L.W + (e.iw * e.pw + dw);
     orow_i = dt < e.lt && dh < e.lh && dw < e.lw ? tok * L.heads + h : -1;

@@ -46,7 +46,8 @@ constexpr int kWaitVmLgkm0 = 0x0070;
 // padding slot.
 __device__ __forceinline__ int64_t slot_row(const DevLayout& L, const TileExtent& e, int h,
                                             int u) {
-  const int dw = u % e.pw, r = u / e.pw, dh = r % e.ph, dt = r / e.ph;
+  int dt, dh, dw;
+  e.slot_coords(u, dt, dh, dw);
   if (dt >= e.lt || dh >= e.lh || dw >= e.lw) return -1;
   const int64_t tok =
       ((int64_t)(e.it * e.pt + dt) * L.H + (e.ih * e.ph + dh)) * L.W + (e.iw * e.pw + dw);
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(2 * S, 2) void attn_bwd_dq_kernel(
   auto tile_of = [&](int s, int& cut) {
     const int c = cp[beg + s / SPT];
     const bool ok = c >= 0 && c < n_h;
-    cut = ok ? cut_of(tile_extent(L, h, c)) : 8;
+    cut = ok ? cut_of(tile_extent(L, h, ok ? c : 0)) : 8;
     return ok ? c : 0;
   };
   // copies of step s; returns its mask cut
